@@ -1,0 +1,128 @@
+/*
+ * lat_moe.h -- C ABI of the quantized latent-MoE expert stage for MI355X (gfx950).
+ *
+ * The operation (page "Run Edge0-145B Q3_K on AMD HIP (Linux, gfx1100) #1",
+ * section "Contents" and the lat_q3k_w11.cu commit message): for every token t
+ * and each of its k routed experts e = router_idx[t][j],
+ *     G, U = gate and up rows of expert e (Q3_K)  x  x[t] (q8_1),
+ *            integer dots per 32-value activation block, scales folded in fp32;
+ *     H    = silu(G) * U, re-rounded to q8_1 (32-value blocks);
+ *     O    = down rows of expert e (IQ4_NL)  x  H, same block structure;
+ *     y[t] = sum over j of router_w[t][j] * O      (j = 0 .. k-1, in order).
+ * Tokens are grouped by expert on the device and each expert's weights are read
+ * in place.  Block layouts are ggml's GGUF formats:
+ *     Q3_K   110 B per 256 weights: hmask[32] | qs[64] | scales[12] | d (fp16)
+ *     IQ4_NL  18 B per  32 weights: d (fp16) | qs[16] (4-bit table indices)
+ *     q8_1    36 B per  32 values : d (fp16) | s (fp16) | qs[32] (int8)
+ * q8_1 rounding rule (inputs and H): amax = max|v|, d = amax/127, id = 1/d (0 if
+ * d == 0), q = round-half-away(v * id), stored d = fp16(d), s = fp16(d * sum q);
+ * all in IEEE fp32.
+ *
+ * Memory and ownership: every array argument is device memory owned by the
+ * caller (for instance a torch tensor's data pointer), 16-byte aligned.  Shape
+ * structs and the debug struct are host memory, read during the call only.
+ * The library allocates nothing inside a call and keeps no state between calls
+ * except a per-device "is this a gfx950" cache.
+ *
+ * Execution: work is enqueued on `stream` (a hipStream_t; NULL = the default
+ * stream) and the call returns without synchronising; results are valid once
+ * the stream reaches that point.  Calls that share a workspace must not
+ * overlap in time.
+ *
+ * Errors: the return value is 0 or a LAT_MOE_E* code; nothing is enqueued when
+ * an argument or workspace error is returned (these checks make no HIP call).
+ * Expert ids outside [0, E) are dropped on the device: the pair contributes
+ * nothing (as a zero router weight would) and is counted in the debug struct.
+ */
+#ifndef LAT_MOE_H
+#define LAT_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LAT_MOE_OK 0
+#define LAT_MOE_EINVAL 1     /* null pointer, unsupported shape, misaligned pointer */
+#define LAT_MOE_EWORKSPACE 2 /* workspace_bytes smaller than lat_moe_workspace_size() */
+#define LAT_MOE_EDEVICE 3    /* current device is not a gfx950 (MI355X/MI350X) */
+#define LAT_MOE_ELAUNCH 4    /* a kernel launch failed (hipGetLastError after enqueue) */
+
+#define LAT_MOE_MAX_E 1024
+
+/* Shapes of one call.  Supported: T >= 0, T * k < 2^31, L % 256 == 0
+ * (256 <= L <= 65536), F % 32 == 0 (32 <= F <= 65536), 1 <= E <= 1024,
+ * 1 <= k <= E. */
+typedef struct lat_moe_shapes {
+  int64_t T; /* tokens */
+  int32_t L; /* latent dimension */
+  int32_t F; /* expert FFN width */
+  int32_t E; /* experts */
+  int32_t k; /* experts per token */
+} lat_moe_shapes;
+
+/* Bytes of device workspace lat_moe_expert_forward needs for these shapes
+ * (0 if the shapes are unsupported).  Grows with T*k*(F + 4L). */
+size_t lat_moe_workspace_size(const lat_moe_shapes* shapes);
+
+/* The expert stage.
+ *   x_q8_1      [T][L/32] q8_1 blocks         latent activations, already in q8_1
+ *   router_idx  [T][k] int32                  routed expert ids
+ *   router_w    [T][k] fp32                   combine weights, used as given
+ *   gateup_q3k  [E][2F][L/256] Q3_K blocks    rows 0..F-1 gate, F..2F-1 up
+ *   down_iq4nl  [E][L][F/32] IQ4_NL blocks
+ *   y           [T][L] fp32                   output, overwritten
+ *   workspace   workspace_bytes of device memory, contents need no initialisation
+ *   stream      hipStream_t
+ * Results are deterministic: the same inputs give bitwise identical y. */
+int lat_moe_expert_forward(const void* x_q8_1, const int32_t* router_idx, const float* router_w,
+                           const void* gateup_q3k, const void* down_iq4nl, const lat_moe_shapes* shapes,
+                           float* y, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Optional device outputs of the debug entry point.  Any pointer may be NULL. */
+typedef struct lat_moe_debug {
+  void* h_q8_1;         /* [T*k][F/32] q8_1: H of every pair p = t*k + j, ggml layout;
+                           pairs with an invalid expert id get all-zero blocks */
+  int32_t* perm;        /* [T*k]: pair ids grouped by expert, ascending within an expert;
+                           only the first offsets[E] entries are defined */
+  int32_t* offsets;     /* [E+1]: start of each expert's group in perm */
+  int32_t* dropped;     /* [1]: number of pairs whose expert id is outside [0, E) */
+  /* Integer block dots as the kernels form them, for a range of weight rows:
+   * gateup_i32 [T*k][gu_rows][L/32] for gate/up rows gu_row0 .. gu_row0+gu_rows-1
+   * (of 2F), each the dot of the scale-folded Q3_K row with the token's q8_1
+   * codes over one 32-value block: sum sigma(i/16) * (c(i) - 4) * q(i).
+   * down_i32 [T*k][dn_rows][F/32] for down rows dn_row0 .. dn_row0+dn_rows-1
+   * (of L): sum over a block of table(idx(i)) * qH(i).  Entries of invalid
+   * pairs are left untouched. */
+  int32_t* gateup_i32;
+  int32_t gu_row0, gu_rows;
+  int32_t* down_i32;
+  int32_t dn_row0, dn_rows;
+} lat_moe_debug;
+
+/* Same computation as lat_moe_expert_forward (same kernels, same y), plus the
+ * requested debug outputs.  Row ranges must lie inside [0, 2F) and [0, L). */
+int lat_moe_expert_forward_debug(const void* x_q8_1, const int32_t* router_idx, const float* router_w,
+                                 const void* gateup_q3k, const void* down_iq4nl, const lat_moe_shapes* shapes,
+                                 float* y, void* workspace, size_t workspace_bytes, void* stream,
+                                 const lat_moe_debug* dbg);
+
+/* Round fp32 rows to q8_1 with the rule above: x [rows][cols] -> out
+ * [rows][cols/32] q8_1 blocks (cols % 32 == 0, rows >= 0).  This is the rounding
+ * the stage's producer applies to the latent rows (the D projection's q8_1
+ * store) and the same rule the stage applies to H. */
+int lat_moe_quantize_q8_1(const float* x, int64_t rows, int32_t cols, void* out_q8_1, void* stream);
+
+/* Static description of an error code. */
+const char* lat_moe_strerror(int code);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int lat_moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LAT_MOE_H */

@@ -1,0 +1,142 @@
+"""Quantized latent-MoE expert stage on MI355X (gfx950): Python binding.
+
+Thin ctypes marshalling over ``liblatmoe.so`` (the C ABI in
+``include/lat_moe.h``).  Every step of the stage runs in the library's HIP
+kernels; torch tensors only provide device memory and the current stream.
+There is no fallback: if the library is not built, calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liblatmoe.so")
+
+LAT_MOE_MAX_E = 1024
+
+# Symbols the C header declares (checked by the CPU test suite).
+EXPORTED = (
+    "lat_moe_workspace_size",
+    "lat_moe_expert_forward",
+    "lat_moe_expert_forward_debug",
+    "lat_moe_quantize_q8_1",
+    "lat_moe_strerror",
+    "lat_moe_version",
+)
+
+
+class Shapes(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("L", ctypes.c_int32), ("F", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("k", ctypes.c_int32)]
+
+
+class Debug(ctypes.Structure):
+    _fields_ = [
+        ("h_q8_1", ctypes.c_void_p),
+        ("perm", ctypes.c_void_p),
+        ("offsets", ctypes.c_void_p),
+        ("dropped", ctypes.c_void_p),
+        ("gateup_i32", ctypes.c_void_p),
+        ("gu_row0", ctypes.c_int32),
+        ("gu_rows", ctypes.c_int32),
+        ("down_i32", ctypes.c_void_p),
+        ("dn_row0", ctypes.c_int32),
+        ("dn_rows", ctypes.c_int32),
+    ]
+
+
+class LatMoeError(RuntimeError):
+    pass
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load liblatmoe.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise LatMoeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                              "(or python quantized_latent_moe_amd/build.py)")
+        c = ctypes.CDLL(LIB_PATH)
+        P = ctypes.c_void_p
+        c.lat_moe_workspace_size.argtypes = [ctypes.POINTER(Shapes)]
+        c.lat_moe_workspace_size.restype = ctypes.c_size_t
+        c.lat_moe_expert_forward.argtypes = [P, P, P, P, P, ctypes.POINTER(Shapes), P, P, ctypes.c_size_t, P]
+        c.lat_moe_expert_forward.restype = ctypes.c_int
+        c.lat_moe_expert_forward_debug.argtypes = [P, P, P, P, P, ctypes.POINTER(Shapes), P, P, ctypes.c_size_t, P,
+                                                   ctypes.POINTER(Debug)]
+        c.lat_moe_expert_forward_debug.restype = ctypes.c_int
+        c.lat_moe_quantize_q8_1.argtypes = [P, ctypes.c_int64, ctypes.c_int32, P, P]
+        c.lat_moe_quantize_q8_1.restype = ctypes.c_int
+        c.lat_moe_strerror.argtypes = [ctypes.c_int]
+        c.lat_moe_strerror.restype = ctypes.c_char_p
+        c.lat_moe_version.restype = ctypes.c_int
+        _lib = c
+    return _lib
+
+
+def strerror(code: int) -> str:
+    return lib().lat_moe_strerror(int(code)).decode()
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        raise LatMoeError(f"lat_moe error {rc}: {strerror(rc)}")
+
+
+def shapes(T: int, L: int, F: int, E: int, k: int) -> Shapes:
+    return Shapes(int(T), int(L), int(F), int(E), int(k))
+
+
+def workspace_size(s: Shapes) -> int:
+    return int(lib().lat_moe_workspace_size(ctypes.byref(s)))
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is not None:
+        return int(stream)
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def expert_forward(x_q8_1, router_idx, router_w, gateup_q3k, down_iq4nl, s: Shapes, y, workspace,
+                   stream=None) -> None:
+    """Enqueue the expert stage; all tensors on the current GPU (uint8 blocks,
+    int32 ids, fp32 weights, fp32 y [T, L], uint8 workspace)."""
+    rc = lib().lat_moe_expert_forward(_ptr(x_q8_1), _ptr(router_idx), _ptr(router_w), _ptr(gateup_q3k),
+                                      _ptr(down_iq4nl), ctypes.byref(s), _ptr(y), _ptr(workspace),
+                                      workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(rc)
+
+
+def expert_forward_debug(x_q8_1, router_idx, router_w, gateup_q3k, down_iq4nl, s: Shapes, y, workspace, *,
+                         h_q8_1=None, perm=None, offsets=None, dropped=None, gateup_i32=None, gu_row0=0,
+                         down_i32=None, dn_row0=0, stream=None) -> None:
+    """As expert_forward, plus the optional debug outputs of lat_moe_debug.
+    gateup_i32 is [T*k, rows, L/32] int32 and down_i32 [T*k, rows, F/32]."""
+    d = Debug(_ptr(h_q8_1), _ptr(perm), _ptr(offsets), _ptr(dropped), _ptr(gateup_i32), int(gu_row0),
+              0 if gateup_i32 is None else int(gateup_i32.shape[1]), _ptr(down_i32), int(dn_row0),
+              0 if down_i32 is None else int(down_i32.shape[1]))
+    rc = lib().lat_moe_expert_forward_debug(_ptr(x_q8_1), _ptr(router_idx), _ptr(router_w), _ptr(gateup_q3k),
+                                            _ptr(down_iq4nl), ctypes.byref(s), _ptr(y), _ptr(workspace),
+                                            workspace.numel() * workspace.element_size(), _stream(stream),
+                                            ctypes.byref(d))
+    _check(rc)
+
+
+def quantize_q8_1(x, out, stream=None) -> None:
+    """fp32 [rows, cols] -> q8_1 blocks (uint8 [rows, cols/32, 36])."""
+    rows, cols = x.shape
+    _check(lib().lat_moe_quantize_q8_1(_ptr(x), int(rows), int(cols), _ptr(out), _stream(stream)))
+
+
+def version() -> int:
+    return int(lib().lat_moe_version())

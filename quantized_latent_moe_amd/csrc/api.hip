@@ -1,0 +1,177 @@
+// C ABI of the expert stage: argument checks, workspace layout, launches.
+#include <mutex>
+#include <string.h>
+
+#include "../../include/lat_moe.h"
+#include "lat_moe_internal.h"
+
+using namespace latmoe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool shapes_ok(const lat_moe_shapes* s) {
+  if (!s) return false;
+  if (s->T < 0 || s->L < 256 || s->L > 65536 || s->L % 256) return false;
+  if (s->F < 32 || s->F > 65536 || s->F % 32) return false;
+  if (s->E < 1 || s->E > LAT_MOE_MAX_E || s->k < 1 || s->k > s->E) return false;
+  if (s->T * (int64_t)s->k >= (int64_t)1 << 31) return false;
+  return true;
+}
+
+struct Layout {
+  size_t chunk_hist, chunk_bad, offsets, misc, tiles, perm, h_codes, h_ds, slots, total;
+  int nchunk, max_tiles;
+};
+
+Layout layout(const lat_moe_shapes* s) {
+  Layout L{};
+  const int64_t P = s->T * s->k;
+  L.nchunk = (int)((P + kRouteChunk - 1) / kRouteChunk);
+  L.max_tiles = (int)((P + kTileN - 1) / kTileN + s->E);
+  size_t o = 0;
+  L.chunk_hist = o; o = align_up(o + sizeof(int32_t) * (size_t)L.nchunk * s->E);
+  L.chunk_bad = o;  o = align_up(o + sizeof(int32_t) * (size_t)L.nchunk);
+  L.offsets = o;    o = align_up(o + sizeof(int32_t) * (size_t)(s->E + 1));
+  L.misc = o;       o = align_up(o + sizeof(int32_t) * kMiscWords);
+  L.tiles = o;      o = align_up(o + sizeof(int32_t) * 2 * (size_t)L.max_tiles);
+  L.perm = o;       o = align_up(o + sizeof(int32_t) * (size_t)P);
+  L.h_codes = o;    o = align_up(o + (size_t)P * s->F);
+  L.h_ds = o;       o = align_up(o + sizeof(uint32_t) * (size_t)P * (s->F / 32));
+  L.slots = o;      o = align_up(o + sizeof(float) * (size_t)P * s->L);
+  L.total = o;
+  return L;
+}
+
+Work carve(const Layout& L, void* ws) {
+  char* b = static_cast<char*>(ws);
+  Work w;
+  w.chunk_hist = reinterpret_cast<int32_t*>(b + L.chunk_hist);
+  w.chunk_bad = reinterpret_cast<int32_t*>(b + L.chunk_bad);
+  w.offsets = reinterpret_cast<int32_t*>(b + L.offsets);
+  w.misc = reinterpret_cast<int32_t*>(b + L.misc);
+  w.tiles = reinterpret_cast<int32_t*>(b + L.tiles);
+  w.perm = reinterpret_cast<int32_t*>(b + L.perm);
+  w.h_codes = reinterpret_cast<int8_t*>(b + L.h_codes);
+  w.h_ds = reinterpret_cast<uint32_t*>(b + L.h_ds);
+  w.slots = reinterpret_cast<float*>(b + L.slots);
+  w.nchunk = L.nchunk;
+  w.max_tiles = L.max_tiles;
+  return w;
+}
+
+// Once per device: is it a gfx950 with 64-wide wavefronts?
+int check_device() {
+  static std::mutex mu;
+  static signed char state[64];  // 0 unknown, 1 ok, -1 unsupported
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return LAT_MOE_EDEVICE;
+  std::lock_guard<std::mutex> g(mu);
+  if (state[dev] == 0) {
+    hipDeviceProp_t p;
+    if (hipGetDeviceProperties(&p, dev) != hipSuccess) return LAT_MOE_EDEVICE;
+    state[dev] = (strncmp(p.gcnArchName, "gfx950", 6) == 0 && p.warpSize == 64) ? 1 : -1;
+  }
+  return state[dev] == 1 ? LAT_MOE_OK : LAT_MOE_EDEVICE;
+}
+
+int forward_impl(const void* x, const int32_t* idx, const float* w, const void* gu, const void* dn,
+                 const lat_moe_shapes* s, float* y, void* ws, size_t ws_bytes, void* stream,
+                 const lat_moe_debug* dbg) {
+  if (!shapes_ok(s)) return LAT_MOE_EINVAL;
+  if (s->T > 0) {
+    const void* ptrs[] = {x, idx, w, gu, dn, y, ws};
+    for (const void* p : ptrs)
+      if (!p || !aligned16(p)) return LAT_MOE_EINVAL;
+  }
+  if (dbg) {
+    if (dbg->gateup_i32 && (dbg->gu_rows < 1 || dbg->gu_row0 < 0 || dbg->gu_row0 + (int64_t)dbg->gu_rows > 2 * (int64_t)s->F))
+      return LAT_MOE_EINVAL;
+    if (dbg->down_i32 && (dbg->dn_rows < 1 || dbg->dn_row0 < 0 || dbg->dn_row0 + (int64_t)dbg->dn_rows > s->L))
+      return LAT_MOE_EINVAL;
+  }
+  const Layout L = layout(s);
+  if (s->T == 0) return LAT_MOE_OK;
+  if (ws_bytes < L.total) return LAT_MOE_EWORKSPACE;
+  int rc = check_device();
+  if (rc != LAT_MOE_OK) return rc;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const Shapes sh{s->T, s->L, s->F, s->E, s->k};
+  const Work wk = carve(L, ws);
+  const uint8_t* xb = static_cast<const uint8_t*>(x);
+  if (launch_route(idx, sh, wk, st) != hipSuccess) return LAT_MOE_ELAUNCH;
+  ProbeRows pg{nullptr, 0, 0}, pd{nullptr, 0, 0};
+  if (dbg && dbg->gateup_i32) pg = ProbeRows{dbg->gateup_i32, dbg->gu_row0, dbg->gu_rows};
+  if (dbg && dbg->down_i32) pd = ProbeRows{dbg->down_i32, dbg->dn_row0, dbg->dn_rows};
+  if (launch_gateup(xb, static_cast<const uint8_t*>(gu), sh, wk, pg.out ? &pg : nullptr, st) != hipSuccess)
+    return LAT_MOE_ELAUNCH;
+  if (launch_down(static_cast<const uint8_t*>(dn), w, sh, wk, pd.out ? &pd : nullptr, st) != hipSuccess)
+    return LAT_MOE_ELAUNCH;
+  if (launch_combine(idx, sh, wk, y, st) != hipSuccess) return LAT_MOE_ELAUNCH;
+  if (dbg) {
+    if (dbg->h_q8_1 && launch_export_h(sh, wk, static_cast<uint8_t*>(dbg->h_q8_1), st) != hipSuccess)
+      return LAT_MOE_ELAUNCH;
+    if (dbg->perm && launch_copy_i32(wk.perm, dbg->perm, sh.pairs(), st) != hipSuccess) return LAT_MOE_ELAUNCH;
+    if (dbg->offsets && launch_copy_i32(wk.offsets, dbg->offsets, s->E + 1, st) != hipSuccess) return LAT_MOE_ELAUNCH;
+    if (dbg->dropped && launch_copy_i32(wk.misc + kMiscDropped, dbg->dropped, 1, st) != hipSuccess)
+      return LAT_MOE_ELAUNCH;
+  }
+  return LAT_MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t lat_moe_workspace_size(const lat_moe_shapes* shapes) {
+  if (!shapes_ok(shapes)) return 0;
+  return layout(shapes).total;
+}
+
+int lat_moe_expert_forward(const void* x_q8_1, const int32_t* router_idx, const float* router_w,
+                           const void* gateup_q3k, const void* down_iq4nl, const lat_moe_shapes* shapes, float* y,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  return forward_impl(x_q8_1, router_idx, router_w, gateup_q3k, down_iq4nl, shapes, y, workspace, workspace_bytes,
+                      stream, nullptr);
+}
+
+int lat_moe_expert_forward_debug(const void* x_q8_1, const int32_t* router_idx, const float* router_w,
+                                 const void* gateup_q3k, const void* down_iq4nl, const lat_moe_shapes* shapes,
+                                 float* y, void* workspace, size_t workspace_bytes, void* stream,
+                                 const lat_moe_debug* dbg) {
+  if (!dbg) return LAT_MOE_EINVAL;
+  return forward_impl(x_q8_1, router_idx, router_w, gateup_q3k, down_iq4nl, shapes, y, workspace, workspace_bytes,
+                      stream, dbg);
+}
+
+int lat_moe_quantize_q8_1(const float* x, int64_t rows, int32_t cols, void* out_q8_1, void* stream) {
+  if (rows < 0 || cols < 32 || cols % 32) return LAT_MOE_EINVAL;
+  if (rows == 0) return LAT_MOE_OK;
+  if (!x || !out_q8_1 || !aligned16(x) || !aligned16(out_q8_1)) return LAT_MOE_EINVAL;
+  int rc = check_device();
+  if (rc != LAT_MOE_OK) return rc;
+  if (launch_quantize_q8_1(x, rows, cols, static_cast<uint8_t*>(out_q8_1), static_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return LAT_MOE_ELAUNCH;
+  return LAT_MOE_OK;
+}
+
+const char* lat_moe_strerror(int code) {
+  switch (code) {
+    case LAT_MOE_OK: return "ok";
+    case LAT_MOE_EINVAL: return "invalid argument (null or misaligned pointer, or unsupported shape)";
+    case LAT_MOE_EWORKSPACE: return "workspace smaller than lat_moe_workspace_size()";
+    case LAT_MOE_EDEVICE: return "current device is not a gfx950 with 64-wide wavefronts";
+    case LAT_MOE_ELAUNCH: return "kernel launch failed";
+    default: return "unknown error";
+  }
+}
+
+int lat_moe_version(void) { return 100; }
+
+}  // extern "C"

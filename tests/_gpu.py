@@ -1,0 +1,117 @@
+"""Helpers of the GPU parity tests: upload seeded inputs, run the HIP library
+through its C ABI, and compare with the oracle by the stage's criteria:
+
+  C1  integer block dots (gate/up I32, down J32) bit-exact;
+  C2  H q8_1 codes >= 99.99 % equal, every other code within +-1, fp16 d_H
+      within one ulp;
+  C3  max |y_gpu - y_ref(H_gpu)| <= 2e-3 * rms(y_ref), where y_ref(H_gpu) is
+      the oracle's down projection and combine fed the GPU's own H (the GPU's
+      fp32 folds and the oracle's fp64 folds may round a few H codes
+      differently, and each such +-1 legitimately moves a whole output row).
+      The end-to-end difference against the oracle's own y is reported.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+import quantized_latent_moe_amd as lm
+
+Y_TOL = 2e-3        # C3, relative to rms(y_ref)
+H_EQUAL = 0.9999    # C2
+
+
+def say(*a):
+    print("[gpu-test]", *a, flush=True)
+    sys.stdout.flush()
+
+
+class Gpu:
+    """Device copies of one case's inputs plus the workspace."""
+
+    def __init__(self, I, xq):
+        wl = I.wl
+        self.wl, self.I = wl, I
+        dev = torch.device("cuda", 0)
+        self.x = torch.from_numpy(np.ascontiguousarray(xq)).to(dev)
+        self.idx = torch.from_numpy(np.ascontiguousarray(I.router_idx, np.int32)).to(dev)
+        self.w = torch.from_numpy(np.ascontiguousarray(I.router_w, np.float32)).to(dev)
+        self.gu = torch.from_numpy(I.gateup_q3k).to(dev)
+        self.dn = torch.from_numpy(I.down_iq4nl).to(dev)
+        self.s = lm.shapes(wl.T, wl.L, wl.F, wl.E, wl.k)
+        self.ws = torch.empty(max(lm.workspace_size(self.s), 256), dtype=torch.uint8, device=dev)
+        self.y = torch.empty((max(wl.T, 1), wl.L), dtype=torch.float32, device=dev)
+
+    def set_routing(self, idx, w):
+        self.idx = torch.from_numpy(np.ascontiguousarray(idx, np.int32)).cuda()
+        self.w = torch.from_numpy(np.ascontiguousarray(w, np.float32)).cuda()
+
+    def forward(self):
+        lm.expert_forward(self.x, self.idx, self.w, self.gu, self.dn, self.s, self.y, self.ws)
+        torch.cuda.synchronize()
+        return self.y[: self.wl.T].cpu().numpy()
+
+    def forward_debug(self, gu_rows=None, dn_rows=None):
+        wl = self.wl
+        P = wl.T * wl.k
+        dev = self.x.device
+        h = torch.empty((P, wl.F // 32, 36), dtype=torch.uint8, device=dev)
+        perm = torch.full((P,), -7, dtype=torch.int32, device=dev)
+        offs = torch.empty((wl.E + 1,), dtype=torch.int32, device=dev)
+        dropped = torch.empty((1,), dtype=torch.int32, device=dev)
+        gi = di = None
+        if gu_rows is not None:
+            gi = torch.zeros((P, gu_rows[1], wl.L // 32), dtype=torch.int32, device=dev)
+        if dn_rows is not None:
+            di = torch.zeros((P, dn_rows[1], wl.F // 32), dtype=torch.int32, device=dev)
+        lm.expert_forward_debug(self.x, self.idx, self.w, self.gu, self.dn, self.s, self.y, self.ws, h_q8_1=h,
+                                perm=perm, offsets=offs, dropped=dropped, gateup_i32=gi,
+                                gu_row0=0 if gu_rows is None else gu_rows[0], down_i32=di,
+                                dn_row0=0 if dn_rows is None else dn_rows[0])
+        torch.cuda.synchronize()
+        out = dict(y=self.y[: wl.T].cpu().numpy(), h=h.cpu().numpy(), perm=perm.cpu().numpy(),
+                   offsets=offs.cpu().numpy(), dropped=int(dropped.item()))
+        if gi is not None:
+            out["gu_i32"] = gi.cpu().numpy()
+        if di is not None:
+            out["dn_i32"] = di.cpu().numpy()
+        return out
+
+
+def h_fields(h):
+    d = h[..., 0:2].copy().view(np.uint16)[..., 0]
+    q = h[..., 4:36].view(np.int8)
+    return d, q
+
+
+def check_h(h_gpu, h_ref, pairs=None, label=""):
+    """C2 on the given pairs (rows of the [P, F/32, 36] arrays)."""
+    if pairs is not None:
+        h_gpu, h_ref = h_gpu[pairs], h_ref
+    dg, qg = h_fields(h_gpu)
+    dr, qr = h_fields(h_ref)
+    diff = np.abs(qg.astype(np.int32) - qr.astype(np.int32))
+    frac = float((diff == 0).mean()) if diff.size else 1.0
+    dd = np.abs(dg.astype(np.int32) - dr.astype(np.int32))
+    say(f"{label} H codes equal {frac * 100:.5f}% ({int((diff != 0).sum())} of {diff.size}), max|dq|="
+        f"{int(diff.max()) if diff.size else 0}, d_H ulp max {int(dd.max()) if dd.size else 0}")
+    assert frac >= H_EQUAL, frac
+    assert diff.size == 0 or diff.max() <= 1
+    assert dd.size == 0 or dd.max() <= 1
+    return frac
+
+
+def check_y(y_gpu, y_ref, label=""):
+    rms = float(np.sqrt(np.mean(y_ref ** 2))) if y_ref.size else 0.0
+    err = float(np.abs(y_gpu - y_ref).max()) if y_ref.size else 0.0
+    say(f"{label} y max|err| / rms = {err / max(rms, 1e-30):.3e}")
+    assert err <= Y_TOL * rms + 1e-30, (err, rms)
+    return err / max(rms, 1e-30)
+
+
+def stagewise_y(out, I, tokens=None):
+    wl = I.wl
+    return oracle.down_combine(out["h"], I.router_idx, I.router_w, I.down_iq4nl, wl.L, wl.F, wl.E, tokens=tokens)

@@ -1,0 +1,74 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, sizes its workspace, and rejects bad arguments before making
+any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_latent_moe_amd as lm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "lat_moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(lat_moe_\w+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    names = _declared()
+    assert names == sorted(lm.EXPORTED)
+    lib = lm.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lm.version() >= 100
+
+
+def test_workspace_size():
+    ok = lm.shapes(5268, 1024, 2048, 128, 8)
+    ws = lm.workspace_size(ok)
+    P = 5268 * 8
+    # H codes + H scales + weighted slots dominate
+    assert ws >= P * 2048 + P * 64 * 4 + P * 1024 * 4
+    assert ws < P * 2048 + P * 64 * 4 + P * 1024 * 4 + (1 << 22)
+    for bad in [(1, 100, 512, 8, 2), (1, 256, 40, 8, 2), (1, 256, 512, 0, 1), (1, 256, 512, 8, 9), (-1, 256, 512, 8, 2),
+                (1, 256, 512, 2000, 2), (1 << 29, 256, 512, 8, 8)]:
+        assert lm.workspace_size(lm.shapes(*bad)) == 0, bad
+
+
+def _fwd(ptrs, s, ws_bytes):
+    x, idx, w, gu, dn, y, ws = ptrs
+    return lm.lib().lat_moe_expert_forward(x, idx, w, gu, dn, ctypes.byref(s), y, ws, ws_bytes, None)
+
+
+def test_argument_errors_before_any_hip_call():
+    s = lm.shapes(4, 256, 512, 8, 2)
+    need = lm.workspace_size(s)
+    good = [0x10000 * (i + 1) for i in range(7)]  # aligned, never dereferenced on these paths
+    for i in range(7):
+        p = list(good)
+        p[i] = None
+        assert _fwd(p, s, need) == 1
+        p[i] = good[i] + 4
+        assert _fwd(p, s, need) == 1
+    assert _fwd(good, s, need - 1) == 2
+    assert _fwd(good, lm.shapes(4, 200, 512, 8, 2), need) == 1
+    # T = 0 is a no-op that touches nothing
+    assert _fwd([None] * 7, lm.shapes(0, 256, 512, 8, 2), 0) == 0
+    # debug row ranges are validated too
+    d = lm.Debug(None, None, None, None, 0x1000, 1000, 40, None, 0, 0)
+    rc = lm.lib().lat_moe_expert_forward_debug(*good[:5], ctypes.byref(s), good[5], good[6], need, None,
+                                               ctypes.byref(d))
+    assert rc == 1
+    assert lm.lib().lat_moe_quantize_q8_1(0x1000, 4, 40, 0x2000, None) == 1
+    assert lm.lib().lat_moe_quantize_q8_1(0x1004, 4, 64, 0x2000, None) == 1
+    assert lm.lib().lat_moe_quantize_q8_1(None, 0, 64, None, None) == 0
+
+
+def test_strerror():
+    for c in range(5):
+        assert lm.strerror(c)
+    assert "unknown" in lm.strerror(99)
