@@ -1,0 +1,228 @@
+#!/usr/bin/env python3
+"""Benchmark of the quantized latent-MoE expert stage on one MI355X.
+
+A step is one whole expert-stage call (device routing sort, gate/up GEMM with
+the SwiGLU + q8_1 epilogue, IQ4_NL down GEMM, weighted combine) over one
+batch of synthetic inputs already resident in HBM.  Default workload: the
+5268-token prefill (L=1024, F=2048, E=128, top-8, Zipf-skewed routing).
+
+Prints one JSON line: whole-job tokens/s over exactly --steps timed calls, the
+dominant kernel's roofline (algorithmic int8 ops per launch over its measured
+launch duration, from events recorded on the kernels' own stream), a
+decode-shaped bandwidth line, and the CPU oracle timed on a bounded token
+sample of the same workload as a reference baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA, 5.0 POP/s
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, 8 TB/s
+METRIC = "expert-stage prefill tokens/s at T=5268; % int8 MFMA peak; HBM GB/s"
+
+
+def algorithmic(wl, idx):
+    """Valid pairs, int8 ops per stage and algorithmic HBM bytes of one call."""
+    import numpy as np
+    ids = idx.reshape(-1)
+    valid = (ids >= 0) & (ids < wl.E)
+    pv = int(valid.sum())
+    active = int(np.unique(ids[valid]).size)
+    gu_bytes = 2 * wl.F * (wl.L // 256) * 110
+    dn_bytes = wl.L * (wl.F // 32) * 18
+    ops_gateup = 2 * pv * 2 * wl.F * wl.L
+    ops_down = 2 * pv * wl.L * wl.F
+    nbytes = (active * (gu_bytes + dn_bytes) + wl.T * (wl.L // 32) * 36 + wl.T * wl.k * 8 + wl.T * wl.L * 4)
+    return dict(pairs=pv, active=active, ops_gateup=ops_gateup, ops_down=ops_down, bytes=nbytes,
+                gu_bytes_active=active * gu_bytes, dn_bytes_active=active * dn_bytes)
+
+
+class Stage:
+    """One workload resident on the GPU."""
+
+    def __init__(self, wl):
+        import numpy as np
+        import torch
+        import quantized_latent_moe_amd as lm
+        from quantized_latent_moe_amd.inputs import make_inputs
+        self.lm, self.torch, self.wl = lm, torch, wl
+        I = make_inputs(wl)
+        self.inputs = I
+        dev = torch.device("cuda", 0)
+        t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+        x32 = t(I.x)
+        self.x = torch.empty((wl.T, wl.L // 32, 36), dtype=torch.uint8, device=dev)
+        lm.quantize_q8_1(x32, self.x)     # the producer's q8_1 rounding; not part of the stage
+        del x32
+        self.idx, self.w = t(I.router_idx), t(I.router_w)
+        self.gu, self.dn = t(I.gateup_q3k), t(I.down_iq4nl)
+        self.s = lm.shapes(wl.T, wl.L, wl.F, wl.E, wl.k)
+        self.ws = torch.empty(lm.workspace_size(self.s), dtype=torch.uint8, device=dev)
+        self.y = torch.empty((wl.T, wl.L), dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
+
+    def step(self):
+        self.lm.expert_forward(self.x, self.idx, self.w, self.gu, self.dn, self.s, self.y, self.ws)
+
+    def step_timed(self, events):
+        self.lm.expert_forward_debug(self.x, self.idx, self.w, self.gu, self.dn, self.s, self.y, self.ws,
+                                     stage_events=events)
+
+    def time_steps(self, steps, warmup):
+        torch = self.torch
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        for _ in range(steps):
+            self.step()
+        e1.record()
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e3 / steps
+        return e0.elapsed_time(e1) / steps, wall
+
+    def stage_times(self, steps):
+        """Mean ms of route / gate-up / down / combine over `steps` calls."""
+        torch = self.torch
+        evs = []
+        for _ in range(steps):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+            for e in ev:
+                e.record()          # creates the underlying hipEvent_t
+            evs.append(ev)
+        torch.cuda.synchronize()
+        for ev in evs:
+            self.step_timed(ev)
+        torch.cuda.synchronize()
+        acc = [0.0] * 4
+        for ev in evs:
+            for i in range(4):
+                acc[i] += ev[i].elapsed_time(ev[i + 1])
+        return [a / steps for a in acc]
+
+
+def cpu_baseline(wl, target_s):
+    """The oracle, as it stands, on the first n tokens of the same workload."""
+    import numpy as np
+    import oracle
+    from quantized_latent_moe_amd.inputs import make_inputs
+    I = make_inputs(wl)
+    xq = oracle.quantize_q8_1(I.x)
+    run = lambda n: oracle.forward(xq, I.router_idx, I.router_w, I.gateup_q3k, I.down_iq4nl, wl.L, wl.F, wl.E,
+                                   tokens=np.arange(n), want_h=False)
+    cores = oracle.num_threads()
+    n0 = min(wl.T, max(cores, 8))
+    t0 = time.perf_counter()
+    run(n0)
+    per_tok = (time.perf_counter() - t0) / n0
+    n = int(min(wl.T, max(n0, target_s / max(per_tok, 1e-9))))
+    t0 = time.perf_counter()
+    run(n)
+    dt = time.perf_counter() - t0
+    return {"value": round(n / dt, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {n} of {wl.T} tokens of {wl.name} ({n * wl.k} routed pairs), {dt:.1f} s"}
+
+
+def read_traffic(kernel, workload):
+    """HBM bytes per launch from the committed counter summary, if one exists
+    for this kernel and workload (profiles/<kernel>_<workload>_traffic.txt)."""
+    p = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.txt")
+    if not os.path.exists(p):
+        return None
+    for line in open(p):
+        if line.startswith("hbm_bytes_per_launch"):
+            return int(float(line.split()[1]))
+    return None
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="prefill_5k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the expert stage here is built and timed on a single MI355X "
+              f"(--gpus {args.gpus} is not supported; token-parallel sharding is described in DESIGN.md).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from quantized_latent_moe_amd.inputs import WORKLOADS
+    torch.cuda.set_device(0)
+    wl = WORKLOADS[args.workload]
+    print(f"[bench] workload {wl}", file=sys.stderr, flush=True)
+    st = Stage(wl)
+    alg = algorithmic(wl, st.inputs.router_idx)
+    ms, wall_ms = st.time_steps(args.steps, args.warmup)
+    print(f"[bench] {ms:.4f} ms/step (events), {wall_ms:.4f} ms/step (host clock)", file=sys.stderr, flush=True)
+    stages = st.stage_times(args.steps)
+    names = ["route", "gateup", "down", "combine"]
+    print("[bench] stage ms: " + ", ".join(f"{n}={v:.4f}" for n, v in zip(names, stages)), file=sys.stderr,
+          flush=True)
+    ops = {"gateup": alg["ops_gateup"], "down": alg["ops_down"]}
+    dom = max(("gateup", "down"), key=lambda n: stages[names.index(n)])
+    dom_ms = stages[names.index(dom)]
+    achieved = ops[dom] / (dom_ms * 1e-3) / 1e12
+    kernel = {"gateup": "k_gateup", "down": "k_down"}[dom]
+    roofline = {"bound": "mfma", "kernel": kernel, "achieved": round(achieved, 2), "peak": PEAK_INT8_TOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 4),
+                "traffic": read_traffic(kernel, wl.name)}
+    total_ops = alg["ops_gateup"] + alg["ops_down"]
+    out = {
+        "metric": METRIC,
+        "value": round(wl.T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "T": wl.T, "L": wl.L, "F": wl.F, "E": wl.E, "k": wl.k,
+                   "zipf_s": wl.zipf_s, "n_masked": wl.n_masked, "seed": wl.seed, "pairs": alg["pairs"],
+                   "active_experts": alg["active"]},
+        "roofline": roofline,
+        "stage_ms": {n: round(v, 5) for n, v in zip(names, stages)},
+        "stage_int8_frac": round(total_ops / (ms * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4),
+        "stage_hbm_gbs": round(alg["bytes"] / (ms * 1e-3) / 1e9, 1),
+    }
+    del st
+    torch.cuda.empty_cache()
+    if not args.no_decode:
+        dwl = WORKLOADS["decode"]
+        ds = Stage(dwl)
+        dalg = algorithmic(dwl, ds.inputs.router_idx)
+        dms, _ = ds.time_steps(max(args.steps, 50), args.warmup)
+        dstage = ds.stage_times(max(args.steps, 50))
+        gbs = dalg["bytes"] / (dms * 1e-3) / 1e9
+        out["decode"] = {"workload": dwl.name, "us_per_step": round(dms * 1e3, 2),
+                         "alg_bytes": dalg["bytes"], "hbm_gbs": round(gbs, 1),
+                         "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "stage_us": {n: round(v * 1e3, 2) for n, v in zip(names, dstage)}}
+        print(f"[bench] decode {dms * 1e3:.2f} us/step, {gbs:.0f} GB/s", file=sys.stderr, flush=True)
+        del ds
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a token sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -100,6 +100,11 @@ typedef struct lat_moe_debug {
   int32_t gu_row0, gu_rows;
   int32_t* down_i32;
   int32_t dn_row0, dn_rows;
+  /* Five caller-created hipEvent_t handles (timing enabled), recorded on
+   * `stream` before the route kernels, after them, after gate/up, after down
+   * and after the combine, so elapsed times between consecutive events are the
+   * stage durations.  NULL to skip.  Recording adds no kernel. */
+  void* const* stage_events;
 } lat_moe_debug;
 
 /* Same computation as lat_moe_expert_forward (same kernels, same y), plus the

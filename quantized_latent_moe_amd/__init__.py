@@ -44,6 +44,7 @@ class Debug(ctypes.Structure):
         ("down_i32", ctypes.c_void_p),
         ("dn_row0", ctypes.c_int32),
         ("dn_rows", ctypes.c_int32),
+        ("stage_events", ctypes.POINTER(ctypes.c_void_p)),
     ]
 
 
@@ -119,12 +120,19 @@ def expert_forward(x_q8_1, router_idx, router_w, gateup_q3k, down_iq4nl, s: Shap
 
 def expert_forward_debug(x_q8_1, router_idx, router_w, gateup_q3k, down_iq4nl, s: Shapes, y, workspace, *,
                          h_q8_1=None, perm=None, offsets=None, dropped=None, gateup_i32=None, gu_row0=0,
-                         down_i32=None, dn_row0=0, stream=None) -> None:
+                         down_i32=None, dn_row0=0, stage_events=None, stream=None) -> None:
     """As expert_forward, plus the optional debug outputs of lat_moe_debug.
-    gateup_i32 is [T*k, rows, L/32] int32 and down_i32 [T*k, rows, F/32]."""
+    gateup_i32 is [T*k, rows, L/32] int32 and down_i32 [T*k, rows, F/32];
+    stage_events is a list of five recorded torch.cuda.Event(enable_timing=True)."""
+    ev = None
+    if stage_events is not None:
+        if len(stage_events) != 5:
+            raise ValueError("stage_events needs 5 events")
+        ev = (ctypes.c_void_p * 5)(*[int(e.cuda_event) for e in stage_events])
     d = Debug(_ptr(h_q8_1), _ptr(perm), _ptr(offsets), _ptr(dropped), _ptr(gateup_i32), int(gu_row0),
               0 if gateup_i32 is None else int(gateup_i32.shape[1]), _ptr(down_i32), int(dn_row0),
-              0 if down_i32 is None else int(down_i32.shape[1]))
+              0 if down_i32 is None else int(down_i32.shape[1]),
+              ctypes.cast(ev, ctypes.POINTER(ctypes.c_void_p)) if ev is not None else None)
     rc = lib().lat_moe_expert_forward_debug(_ptr(x_q8_1), _ptr(router_idx), _ptr(router_w), _ptr(gateup_q3k),
                                             _ptr(down_iq4nl), ctypes.byref(s), _ptr(y), _ptr(workspace),
                                             workspace.numel() * workspace.element_size(), _stream(stream),

@@ -24,7 +24,7 @@ bool shapes_ok(const lat_moe_shapes* s) {
 }
 
 struct Layout {
-  size_t chunk_hist, chunk_bad, offsets, misc, tiles, perm, h_codes, h_ds, slots, total;
+  size_t chunk_hist, chunk_bad, offsets, misc, tiles, perm, h_codes, h_ds, slots, xc, xd, total;
   int nchunk, max_tiles;
 };
 
@@ -43,6 +43,8 @@ Layout layout(const lat_moe_shapes* s) {
   L.h_codes = o;    o = align_up(o + (size_t)P * s->F);
   L.h_ds = o;       o = align_up(o + sizeof(uint32_t) * (size_t)P * (s->F / 32));
   L.slots = o;      o = align_up(o + sizeof(float) * (size_t)P * s->L);
+  L.xc = o;         o = align_up(o + (size_t)s->T * s->L);
+  L.xd = o;         o = align_up(o + sizeof(float) * (size_t)s->T * (s->L / 32));
   L.total = o;
   return L;
 }
@@ -59,6 +61,8 @@ Work carve(const Layout& L, void* ws) {
   w.h_codes = reinterpret_cast<int8_t*>(b + L.h_codes);
   w.h_ds = reinterpret_cast<uint32_t*>(b + L.h_ds);
   w.slots = reinterpret_cast<float*>(b + L.slots);
+  w.xc = reinterpret_cast<int8_t*>(b + L.xc);
+  w.xd = reinterpret_cast<float*>(b + L.xd);
   w.nchunk = L.nchunk;
   w.max_tiles = L.max_tiles;
   return w;
@@ -89,6 +93,9 @@ int forward_impl(const void* x, const int32_t* idx, const float* w, const void* 
       if (!p || !aligned16(p)) return LAT_MOE_EINVAL;
   }
   if (dbg) {
+    if (dbg->stage_events)
+      for (int i = 0; i < 5; ++i)
+        if (!dbg->stage_events[i]) return LAT_MOE_EINVAL;
     if (dbg->gateup_i32 && (dbg->gu_rows < 1 || dbg->gu_row0 < 0 || dbg->gu_row0 + (int64_t)dbg->gu_rows > 2 * (int64_t)s->F))
       return LAT_MOE_EINVAL;
     if (dbg->down_i32 && (dbg->dn_rows < 1 || dbg->dn_row0 < 0 || dbg->dn_row0 + (int64_t)dbg->dn_rows > s->L))
@@ -104,15 +111,23 @@ int forward_impl(const void* x, const int32_t* idx, const float* w, const void* 
   const Shapes sh{s->T, s->L, s->F, s->E, s->k};
   const Work wk = carve(L, ws);
   const uint8_t* xb = static_cast<const uint8_t*>(x);
+  hipEvent_t const* ev = (dbg && dbg->stage_events) ? reinterpret_cast<hipEvent_t const*>(dbg->stage_events) : nullptr;
+  auto mark = [&](int i) { return ev ? hipEventRecord(ev[i], st) : hipSuccess; };
+  if (mark(0) != hipSuccess) return LAT_MOE_ELAUNCH;
   if (launch_route(idx, sh, wk, st) != hipSuccess) return LAT_MOE_ELAUNCH;
+  if (launch_x_split(xb, sh, wk, st) != hipSuccess) return LAT_MOE_ELAUNCH;
+  if (mark(1) != hipSuccess) return LAT_MOE_ELAUNCH;
   ProbeRows pg{nullptr, 0, 0}, pd{nullptr, 0, 0};
   if (dbg && dbg->gateup_i32) pg = ProbeRows{dbg->gateup_i32, dbg->gu_row0, dbg->gu_rows};
   if (dbg && dbg->down_i32) pd = ProbeRows{dbg->down_i32, dbg->dn_row0, dbg->dn_rows};
-  if (launch_gateup(xb, static_cast<const uint8_t*>(gu), sh, wk, pg.out ? &pg : nullptr, st) != hipSuccess)
+  if (launch_gateup(sh, wk, static_cast<const uint8_t*>(gu), pg.out ? &pg : nullptr, st) != hipSuccess)
     return LAT_MOE_ELAUNCH;
+  if (mark(2) != hipSuccess) return LAT_MOE_ELAUNCH;
   if (launch_down(static_cast<const uint8_t*>(dn), w, sh, wk, pd.out ? &pd : nullptr, st) != hipSuccess)
     return LAT_MOE_ELAUNCH;
+  if (mark(3) != hipSuccess) return LAT_MOE_ELAUNCH;
   if (launch_combine(idx, sh, wk, y, st) != hipSuccess) return LAT_MOE_ELAUNCH;
+  if (mark(4) != hipSuccess) return LAT_MOE_ELAUNCH;
   if (dbg) {
     if (dbg->h_q8_1 && launch_export_h(sh, wk, static_cast<uint8_t*>(dbg->h_q8_1), st) != hipSuccess)
       return LAT_MOE_ELAUNCH;

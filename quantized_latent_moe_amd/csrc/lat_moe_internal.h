@@ -17,7 +17,7 @@ constexpr int kQ81Bytes = 36;    // 32 values
 // Pair ids are grouped per route chunk of this many pairs (one workgroup each).
 constexpr int kRouteChunk = 4096;
 // Token (sorted pair) tile of the grouped GEMMs.
-constexpr int kTileN = 64;
+constexpr int kTileN = 128;
 
 // Slots of the small device status array written by the route scan.
 constexpr int kMiscTiles = 0;    // number of (expert, token tile) work items
@@ -42,6 +42,8 @@ struct Work {
   int8_t* h_codes;      // [T*k][F] H codes in sorted order
   uint32_t* h_ds;       // [T*k][F/32] fp16 d | fp16 s << 16
   float* slots;         // [T*k][L] weighted expert outputs in pair order
+  int8_t* xc;           // [T][L] activation codes (q8_1 blocks split into codes ...)
+  float* xd;            // [T][L/32] ... and fp32 block scales)
   int nchunk, max_tiles;
 };
 
@@ -68,8 +70,8 @@ __device__ __forceinline__ float fp32_barrier(float v) {
 
 // Kernel launchers (each returns hipGetLastError() after the enqueue).
 hipError_t launch_route(const int32_t* idx, const Shapes& s, const Work& w, hipStream_t st);
-hipError_t launch_gateup(const uint8_t* x, const uint8_t* gu, const Shapes& s, const Work& w, const ProbeRows* probe,
-                         hipStream_t st);
+hipError_t launch_x_split(const uint8_t* x, const Shapes& s, const Work& w, hipStream_t st);
+hipError_t launch_gateup(const Shapes& s, const Work& w, const uint8_t* gu, const ProbeRows* probe, hipStream_t st);
 hipError_t launch_down(const uint8_t* dn, const float* router_w, const Shapes& s, const Work& w,
                        const ProbeRows* probe, hipStream_t st);
 hipError_t launch_combine(const int32_t* idx, const Shapes& s, const Work& w, float* y, hipStream_t st);
