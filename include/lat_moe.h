@@ -54,7 +54,8 @@ extern "C" {
 
 /* Shapes of one call.  Supported: T >= 0, T * k < 2^31, L % 256 == 0
  * (256 <= L <= 65536), F % 32 == 0 (32 <= F <= 65536), 1 <= E <= 1024,
- * 1 <= k <= E. */
+ * 1 <= k <= E, T * L < 2^31, and one expert's gate/up weights below 2 GiB
+ * (2F * L/256 * 110 < 2^31 bytes). */
 typedef struct lat_moe_shapes {
   int64_t T; /* tokens */
   int32_t L; /* latent dimension */

@@ -20,6 +20,10 @@ bool shapes_ok(const lat_moe_shapes* s) {
   if (s->F < 32 || s->F > 65536 || s->F % 32) return false;
   if (s->E < 1 || s->E > LAT_MOE_MAX_E || s->k < 1 || s->k > s->E) return false;
   if (s->T * (int64_t)s->k >= (int64_t)1 << 31) return false;
+  // one expert's gate/up rows stay below 2 GiB (kernels address within an expert with 32-bit offsets)
+  if ((int64_t)2 * s->F * (s->L / 256) * 110 >= (int64_t)1 << 31) return false;
+  // the activation codes too ([T][L] int8, 32-bit offsets)
+  if (s->T * (int64_t)s->L >= (int64_t)1 << 31) return false;
   return true;
 }
 
@@ -65,13 +69,15 @@ Work carve(const Layout& L, void* ws) {
   w.xd = reinterpret_cast<float*>(b + L.xd);
   w.nchunk = L.nchunk;
   w.max_tiles = L.max_tiles;
+  w.num_cus = 1;
   return w;
 }
 
-// Once per device: is it a gfx950 with 64-wide wavefronts?
-int check_device() {
+// Once per device: is it a gfx950 with 64-wide wavefronts, and how many CUs?
+int check_device(int* num_cus) {
   static std::mutex mu;
   static signed char state[64];  // 0 unknown, 1 ok, -1 unsupported
+  static int cus[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return LAT_MOE_EDEVICE;
   std::lock_guard<std::mutex> g(mu);
@@ -79,7 +85,9 @@ int check_device() {
     hipDeviceProp_t p;
     if (hipGetDeviceProperties(&p, dev) != hipSuccess) return LAT_MOE_EDEVICE;
     state[dev] = (strncmp(p.gcnArchName, "gfx950", 6) == 0 && p.warpSize == 64) ? 1 : -1;
+    cus[dev] = p.multiProcessorCount > 0 ? p.multiProcessorCount : 1;
   }
+  if (num_cus) *num_cus = cus[dev];
   return state[dev] == 1 ? LAT_MOE_OK : LAT_MOE_EDEVICE;
 }
 
@@ -104,12 +112,14 @@ int forward_impl(const void* x, const int32_t* idx, const float* w, const void* 
   const Layout L = layout(s);
   if (s->T == 0) return LAT_MOE_OK;
   if (ws_bytes < L.total) return LAT_MOE_EWORKSPACE;
-  int rc = check_device();
+  int num_cus = 1;
+  int rc = check_device(&num_cus);
   if (rc != LAT_MOE_OK) return rc;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   const Shapes sh{s->T, s->L, s->F, s->E, s->k};
-  const Work wk = carve(L, ws);
+  Work wk = carve(L, ws);
+  wk.num_cus = num_cus;
   const uint8_t* xb = static_cast<const uint8_t*>(x);
   hipEvent_t const* ev = (dbg && dbg->stage_events) ? reinterpret_cast<hipEvent_t const*>(dbg->stage_events) : nullptr;
   auto mark = [&](int i) { return ev ? hipEventRecord(ev[i], st) : hipSuccess; };
@@ -168,7 +178,7 @@ int lat_moe_quantize_q8_1(const float* x, int64_t rows, int32_t cols, void* out_
   if (rows < 0 || cols < 32 || cols % 32) return LAT_MOE_EINVAL;
   if (rows == 0) return LAT_MOE_OK;
   if (!x || !out_q8_1 || !aligned16(x) || !aligned16(out_q8_1)) return LAT_MOE_EINVAL;
-  int rc = check_device();
+  int rc = check_device(nullptr);
   if (rc != LAT_MOE_OK) return rc;
   if (launch_quantize_q8_1(x, rows, cols, static_cast<uint8_t*>(out_q8_1), static_cast<hipStream_t>(stream)) !=
       hipSuccess)

@@ -45,6 +45,7 @@ struct Work {
   int8_t* xc;           // [T][L] activation codes (q8_1 blocks split into codes ...)
   float* xd;            // [T][L/32] ... and fp32 block scales)
   int nchunk, max_tiles;
+  int num_cus;          // compute units of the current device (persistent grids)
 };
 
 struct Shapes {
@@ -60,12 +61,48 @@ __device__ __forceinline__ uint32_t float_to_half_bits(float f) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);  // v_cvt_f16_f32, nearest-even
 }
 
+// MFMA accumulator init that makes an int32 result readable as fp32: the bit
+// pattern 0x4B400000 is 1.5 * 2^23, and adding an int32 I with |I| < 2^22 to
+// those bits gives exactly the float 1.5 * 2^23 + I.
+constexpr int kMagicBits = 0x4B400000;
+constexpr float kMagic = 12582912.0f;
+
+// Reinterprets an int32 MFMA result element as fp32 (through a union:
+// __builtin_bit_cast on an extracted vector element miscompiles here).
+__device__ __forceinline__ float as_float(int v) {
+  union {
+    int i;
+    float f;
+  } u;
+  u.i = v;
+  return u.f;
+}
+
 // Materialises v as an fp32 register value: the optimizer cannot fuse the
 // operation that produced it into what consumes it (for instance fp32 multiply
 // then fp16 conversion into one singly-rounded v_fma_mix).
 __device__ __forceinline__ float fp32_barrier(float v) {
   asm volatile("" : "+v"(v));
   return v;
+}
+
+// Raw buffer loads (gfx9 buffer resource, stride 0).  A load whose 32-bit
+// offset is at or past num_records returns zero without touching memory, so
+// padding lanes load from kOutOfRange instead of branching around the load.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kOutOfRange = (int)0x80000000u;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint32_t buf_u16(rsrc_t r, int voff, int soff) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+}
+__device__ __forceinline__ uint32_t buf_u32(rsrc_t r, int voff, int soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+__device__ __forceinline__ uint4 buf_u128(rsrc_t r, int voff, int soff) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  return uint4{v[0], v[1], v[2], v[3]};
 }
 
 // Kernel launchers (each returns hipGetLastError() after the enqueue).
