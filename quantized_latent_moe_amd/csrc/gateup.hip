@@ -6,62 +6,53 @@
 // in [-128, 124], so one integer dot covers a whole 32-value activation block
 // (lat_q3k_w11.cu commit message).
 //
-// Persistent kernel: one workgroup of 8 waves per CU walks the work items
-// (token tile of up to kTileN = 128 sorted pairs, 64 features) round-robin:
-// item i = tile * nft + feature tile, workgroup w takes w, w + G, w + 2G, ...
-// With G a multiple of the feature-tile count a workgroup keeps one feature
-// tile, and since workgroups are dealt to the 8 XCDs round-robin, each XCD's
-// L2 serves a fixed subset of every expert's rows.
-// Wave w owns the gate and the up 32x32 tile of features f0 + 32*(w&1) .. +31
-// and tokens 32*(w>>1) .. +31: both MFMAs share the activation fragment, and
-// gate and up of each (feature, token) meet in one lane for SwiGLU.  A wave
-// whose 32 tokens are all padding skips its MFMAs and fold.
+// Persistent kernel: one workgroup per CU walks the work items (token tile of
+// up to kTileN = 128 sorted pairs, 64 features) round-robin: item
+// i = tile * nft + feature tile, workgroup w takes w, w + G, w + 2G, ...  With
+// G a multiple of the feature-tile count a workgroup keeps one feature tile,
+// and since workgroups are dealt to the 8 XCDs round-robin, each XCD's L2
+// serves a fixed subset of every expert's rows.
 //
-// K (= L) is walked one Q3_K super-block (256 values) per step; the steps of
-// all the workgroup's items form one pipeline, two barriers per step:
-//   L(g)  global loads of step g into registers (issued two steps ahead):
-//         Q3_K blocks as 16-bit words (rows are only 2-byte aligned; lanes
-//         read consecutive words, 56 per block of which the last is an
-//         out-of-range load), the tokens' int8 codes (16-byte loads) and fp32
-//         block scales, all through buffer loads whose out-of-range offset
-//         returns zeros for padding;
-//   S(g)  those registers into LDS (raw blocks, operand B, scales);
-//   U(g)  unpack: per (row, half, j) 32 codes from 16-byte LDS reads,
-//         (4 - c) * sigma with one v_perm_b32 per 4 values against an 8-entry
-//         table built from the sub-block scale, 16-byte writes to operand A;
-//   M(g)  v_mfma_i32_32x32x32_i8 per 32-value block with the accumulator
-//         initialised to the bits of 1.5 * 2^23, so each result (minus the
-//         block dot) reads as the float 1.5 * 2^23 - I32 with no conversion;
-//         t = fma(-d_x, f, 1.5 * 2^23 * d_x) is exactly fl(d_x * I32) (the
-//         constant has at most 13 significant bits), acc_sb += t, and once per
-//         super-block acc += d_w[row][sb] * acc_sb.
-// Step g's iteration runs S(g+1) | barrier | L(g+2), U(g+1), M(g) | barrier,
-// with operands A and B double-buffered, so the unpack of the next step and
-// this step's MFMA + fold interleave.
-// Epilogue (after an item's last step): H = G * sigmoid(G) * U, then per 32
-// features of a token (16 in this lane, 16 in lane ^ 32) the q8_1 rule: amax,
-// d = amax/127, id = 1/d, q = round-half-away(H * id) with IEEE divisions;
-// codes and fp16 (d, s) go to the workspace in sorted order.
+// The workgroup's 12 waves have two roles (3 waves per SIMD):
+//   8 consumer waves: wave c owns the gate and the up 32x32 tile of features
+//     f0 + 32*(c&1) .. +31 and tokens 32*(c>>1) .. +31 (both MFMAs share the
+//     activation fragment; gate and up of a (feature, token) meet in one lane
+//     for SwiGLU).  Per K step of 256 values: v_mfma_i32_32x32x32_i8 per
+//     32-value block (zero accumulator, the result is minus the block dot
+//     I32), acc_sb = fma(d_x, float(I32), acc_sb) (exact conversion,
+//     |I32| < 2^20), and once per step acc += d_w[row][sb] * acc_sb.  A wave
+//     whose 32 tokens are all padding skips its MFMAs.
+//   4 producer waves: producer p owns weight rows 32p .. 32p+31 of the item
+//     (gate rows, then up rows) and tokens 32p .. 32p+31.  Per K step it loads
+//     into registers, through buffer loads whose out-of-range offset returns
+//     zeros for padding, its rows' Q3_K blocks as 16-bit words (rows are only
+//     2-byte aligned; 8 lanes read 16 contiguous bytes of a row), its tokens'
+//     int8 codes (16-byte loads) and fp32 block scales; writes them to LDS;
+//     and unpacks its rows from LDS: per (row, half, j) 32 codes become
+//     (4 - c) * sigma with one v_perm_b32 per 4 values against an 8-entry
+//     table built from the sub-block scale.  Only the producer itself reads
+//     its raw rows, so no barrier separates its stores from its unpack.
+// Step g: producers build operands of step g+1 in the other LDS buffer and
+// issue the global loads of step g+2; consumers run the MFMAs of step g; one
+// barrier.
+// Epilogue (after an item's last step, consumers): H = G * sigmoid(G) * U,
+// then per 32 features of a token (16 in this lane, 16 in lane ^ 32) the q8_1
+// rule: amax, d = amax/127, id = 1/d, q = round-half-away(H * id) with IEEE
+// divisions; codes and fp16 (d, s) go to the workspace in sorted order.
 #include "lat_moe_internal.h"
 
 namespace latmoe {
 namespace {
 
-constexpr int kThreads = 512;
+constexpr int kConsumers = 8, kProducers = 4;
+constexpr int kThreads = 64 * (kConsumers + kProducers);  // 768
 constexpr int kFT = 64;              // features per work item
 constexpr int kRows = 2 * kFT;       // weight rows per work item (gate + up)
 constexpr int kNT = kTileN;          // tokens per work item
 constexpr int kRawStride = 112;      // staged Q3_K block, bytes (110 rounded up to 16)
 constexpr int kOpStride = 256 + 16;  // int8 operand row in LDS (bytes); 16 mod 256: conflict-free b128
-constexpr int kWords = kQ3kBytes / 2;               // 55 16-bit words per block
-constexpr int kSlots = kRawStride / 2;              // 56 staged words per block (the last one reads as 0)
-constexpr int kRawPer = kRows * kSlots / kThreads;  // 14
-static_assert(kRows * kSlots % kThreads == 0, "raw staging split");
-constexpr int kXPer = kNT * 16 / kThreads;                      // 16-byte code pieces per thread (4)
-constexpr int kDPer = kNT * 8 / kThreads;                       // block scales per thread (2)
-static_assert(kNT * 16 % kThreads == 0 && kNT * 8 % kThreads == 0, "staging split");
-static_assert(kRows * 8 == 2 * kThreads, "unpack split: two (row, half, j) tasks per thread");
-static_assert(kNT == 4 * 32 && kFT == 2 * 32, "8 waves = 2 feature halves x 4 token slices");
+static_assert(kRows == 32 * kProducers && kNT == 32 * kProducers, "a producer owns 32 rows and 32 tokens");
+static_assert(kNT == 4 * 32 && kFT == 2 * 32, "8 consumers = 2 feature halves x 4 token slices");
 
 __device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
   return (uint32_t)(a & 0xff) | ((uint32_t)(b & 0xff) << 8) | ((uint32_t)(c & 0xff) << 16) |
@@ -95,7 +86,7 @@ __global__ __launch_bounds__(kThreads) void k_gateup(const int8_t* __restrict__ 
   __shared__ __align__(16) int8_t Bs[2][kNT * kOpStride];
   __shared__ __align__(16) float dxs[2][kNT * 8];  // [token][block], negated
   __shared__ __align__(16) float dws[2][kRows];
-  __shared__ int32_t ids[2][kNT];  // pair ids (or -1) of the loader's next items
+  __shared__ int32_t ids[2][kNT];  // token ids (or -1) of the producers' next items
 
   const int nft = (F + kFT - 1) / kFT;
   const int n_items = misc[kMiscTiles] * nft;
@@ -103,111 +94,121 @@ __global__ __launch_bounds__(kThreads) void k_gateup(const int8_t* __restrict__ 
   if ((int)blockIdx.x >= n_items) return;
   const int my_items = (n_items - 1 - (int)blockIdx.x) / G + 1;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int fsub = wave & 1, tsub = wave >> 1;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: role branches stay scalar
+  const bool producer = wave >= kConsumers;
   const int nsb = L / 256, nxb = L / 32;
   const int row_bytes = nsb * kQ3kBytes;
   const int n_steps = my_items * nsb;
-  const int col = lane & 31, khalf = lane >> 5;
 
-  // ---- loader: walks (item, super-block) two steps ahead of the MFMAs.
-  // Offsets are fixed per item (the super-block goes into the scalar offset);
-  // rows past F and padding tokens get an out-of-range offset.  The pair ids
-  // of the loader's next item are fetched into LDS one item ahead (read after
-  // at least one barrier).
+  // =========================== producer state ===========================
+  const int p = wave - kConsumers;  // producer index (meaningful for producers)
+  const int ptid = tid - 64 * kConsumers;  // 0 .. 255 for producers
   const rsrc_t rx_src = make_rsrc(xc, (uint32_t)(T * L));
   const rsrc_t rd_src = make_rsrc(xd, (uint32_t)(T * nxb * 4));
   rsrc_t rw_src;
-  int qoff[kRawPer], xoff[kXPer], doff[kDPer];
-  int lj = 0, lsb = 0;
+  // raw: rows 32p + 8g + (lane >> 3), words (lane & 7) + 8m (m < 7; word 55
+  // re-reads word 0 and lands in the staging pad).  codes: tokens
+  // 32p + 4a + (lane >> 4), 16-byte chunk lane & 15.  scales: tokens
+  // 32p + 8c + (lane >> 3), block lane & 7.
+  int qoff[4], xoff[8], doff[4];
+  const int w55 = (lane & 7) == 7 ? -kQ3kBytes : 0;
+  int lj = 0, lsb = 0, qf0 = -1;
+  bool need_setup = true;
   auto fetch_ids = [&](int j) {
     if (j < my_items) {
       const Item it = item_info((int)blockIdx.x + j * G, nft, tiles, offsets);
-      if (tid < kNT) ids[j & 1][tid] = tid < it.cnt ? perm[it.pos0 + tid] : -1;
+      if (ptid < kNT) ids[j & 1][ptid] = ptid < it.cnt ? perm[it.pos0 + ptid] / k : -1;
     }
   };
   auto setup = [&](int j) {
     const Item it = item_info((int)blockIdx.x + j * G, nft, tiles, offsets);
     const int e = __builtin_amdgcn_readfirstlane(it.e);  // uniform: the descriptor lives in SGPRs
     rw_src = make_rsrc(gu + (int64_t)e * 2 * F * row_bytes, (uint32_t)(2 * F * row_bytes));
+    if (it.f0 != qf0) {  // once per workgroup when the grid is a multiple of nft
+      qf0 = it.f0;
 #pragma unroll
-    for (int m = 0; m < kRawPer; ++m) {
-      const int i = tid + kThreads * m;
-      const int r = i / kSlots, w = i - r * kSlots;
-      const int rl = r < kFT ? r : r - kFT;
-      const int row = (r < kFT ? 0 : F) + it.f0 + rl;
-      qoff[m] = (w < kWords && it.f0 + rl < F) ? row * row_bytes + 2 * w : kOutOfRange;
+      for (int g = 0; g < 4; ++g) {
+        const int r = 32 * p + 8 * g + (lane >> 3);  // item row
+        const int rl = r < kFT ? r : r - kFT;
+        const int row = (r < kFT ? 0 : F) + it.f0 + rl;
+        qoff[g] = it.f0 + rl < F ? row * row_bytes + 2 * (lane & 7) : kOutOfRange;
+      }
     }
 #pragma unroll
-    for (int m = 0; m < kXPer; ++m) {
-      const int p = ids[j & 1][(tid + kThreads * m) >> 4];
-      xoff[m] = p >= 0 ? (p / k) * L + (tid & 15) * 16 : kOutOfRange;
+    for (int a = 0; a < 8; ++a) {
+      const int t = ids[j & 1][32 * p + 4 * a + (lane >> 4)];
+      xoff[a] = t >= 0 ? t * L + 16 * (lane & 15) : kOutOfRange;
     }
 #pragma unroll
-    for (int m = 0; m < kDPer; ++m) {
-      const int p = ids[j & 1][(tid + kThreads * m) >> 3];
-      doff[m] = p >= 0 ? ((p / k) * nxb + (tid & 7)) * 4 : kOutOfRange;
+    for (int c = 0; c < 4; ++c) {
+      const int t = ids[j & 1][32 * p + 8 * c + (lane >> 3)];
+      doff[c] = t >= 0 ? (t * nxb + (lane & 7)) * 4 : kOutOfRange;
     }
     fetch_ids(j + 1);
   };
-  uint32_t rq[kRawPer];
-  uint4 rx[kXPer];
-  uint32_t rd[kDPer];
-  // L: sets up a new item when the loader enters one, then only moves bits
-  // into registers (arithmetic on a loaded value would make the compiler wait
-  // for it) and advances the loader.
-  bool need_setup = true;
+  uint32_t rq[4][7];
+  uint4 rx[8];
+  uint32_t rd[4];
+  // L: sets up a new item when the loader enters one (reading the ids that
+  // fetch_ids wrote at least one barrier earlier), then only moves bits into
+  // registers and advances the loader.
   auto load_next = [&]() {
     if (need_setup) {
-      setup(lj);  // reads the ids fetch_ids(lj) wrote at least one barrier ago
+      setup(lj);
       need_setup = false;
     }
-    // scalar offsets (readfirstlane keeps them in SGPRs, as the buffer loads need)
-    const int sq = __builtin_amdgcn_readfirstlane(lsb * kQ3kBytes);
+    const int sq = __builtin_amdgcn_readfirstlane(lsb * kQ3kBytes);  // scalar offsets stay in SGPRs
     const int sx = __builtin_amdgcn_readfirstlane(lsb * 256);
     const int sd = __builtin_amdgcn_readfirstlane(lsb * 32);
 #pragma unroll
-    for (int m = 0; m < kRawPer; ++m) rq[m] = buf_u16(rw_src, qoff[m], sq);
+    for (int g = 0; g < 4; ++g) {
 #pragma unroll
-    for (int m = 0; m < kXPer; ++m) rx[m] = buf_u128(rx_src, xoff[m], sx);
+      for (int m = 0; m < 6; ++m) rq[g][m] = buf_u16(rw_src, qoff[g] + 16 * m, sq);
+      rq[g][6] = buf_u16(rw_src, qoff[g] + 96 + w55, sq);
+    }
 #pragma unroll
-    for (int m = 0; m < kDPer; ++m) rd[m] = buf_u32(rd_src, doff[m], sd);
+    for (int a = 0; a < 8; ++a) rx[a] = buf_u128(rx_src, xoff[a], sx);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) rd[c] = buf_u32(rd_src, doff[c], sd);
     if (++lsb == nsb) {
       lsb = 0;
       need_setup = ++lj < my_items;
     }
   };
-  // S: registers -> LDS buffer b.
-  auto store = [&](int b) {
+  // S + U: registers -> LDS buffer b (raw rows, operand B, scales), then the
+  // producer's own rows unpacked into operand A of buffer b and dws[b].
+  auto build = [&](int b) {
+    uint16_t* raw16 = reinterpret_cast<uint16_t*>(raw) + (32 * p + (lane >> 3)) * (kRawStride / 2) + (lane & 7);
 #pragma unroll
-    for (int m = 0; m < kRawPer; ++m) reinterpret_cast<uint16_t*>(raw)[tid + kThreads * m] = (uint16_t)rq[m];
+    for (int g = 0; g < 4; ++g)
 #pragma unroll
-    for (int m = 0; m < kXPer; ++m) {
-      const int piece = tid + kThreads * m;
-      *reinterpret_cast<uint4*>(Bs[b] + (piece >> 4) * kOpStride + (piece & 15) * 16) = rx[m];
-    }
+      for (int m = 0; m < 7; ++m) raw16[8 * g * (kRawStride / 2) + 8 * m] = (uint16_t)rq[g][m];
 #pragma unroll
-    for (int m = 0; m < kDPer; ++m) dxs[b][tid + kThreads * m] = -as_float((int)rd[m]);  // minus: operand A is -w
-  };
-  // U: raw -> operand A of buffer b, row scales -> dws[b].
-  auto unpack = [&](int b) {
+    for (int a = 0; a < 8; ++a)
+      *reinterpret_cast<uint4*>(Bs[b] + (32 * p + 4 * a + (lane >> 4)) * kOpStride + 16 * (lane & 15)) = rx[a];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int task = tid + kThreads * u;
-      const int ur = task & (kRows - 1), uq = task >> 7, un = uq >> 2, uj = uq & 3;
-      const uint8_t* ublk = raw + ur * kRawStride;
-      const uint4 h0 = *reinterpret_cast<const uint4*>(ublk);
-      const uint4 h1 = *reinterpret_cast<const uint4*>(ublk + 16);
+    for (int c = 0; c < 4; ++c)
+      dxs[b][(32 * p + 8 * c + (lane >> 3)) * 8 + (lane & 7)] = -as_float((int)rd[c]);  // minus: operand A is -w
+    // unpack: this lane's row ur, tasks (un, uj) = (u >> 1, 2 (u & 1) + (lane >> 5))
+    const int ur = 32 * p + (lane & 31);
+    const uint8_t* ublk = raw + ur * kRawStride;
+    const uint4 h0 = *reinterpret_cast<const uint4*>(ublk);
+    const uint4 h1 = *reinterpret_cast<const uint4*>(ublk + 16);
+    const uint4 scw = *reinterpret_cast<const uint4*>(ublk + 96);  // scales[12] | d | pad
+    const uint32_t hm[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+    const uint32_t scb[3] = {scw.x, scw.y, scw.z};
+    if (lane < 32) dws[b][ur] = half_bits_to_float(scw.w & 0xffffu);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int un = u >> 1, uj = 2 * (u & 1) + (lane >> 5);
       const uint4 q0 = *reinterpret_cast<const uint4*>(ublk + 32 + 32 * un);
       const uint4 q1 = *reinterpret_cast<const uint4*>(ublk + 48 + 32 * un);
-      const uint4 scw = *reinterpret_cast<const uint4*>(ublk + 96);  // scales[12] | d | pad
-      const uint32_t hm[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
       const uint32_t qs[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-      const uint32_t scb[3] = {scw.x, scw.y, scw.z};
       uint32_t tlo[2], thi[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const int s = 8 * un + 2 * uj + t;
+        const int s = 8 * un + 2 * uj + t;  // sub-block of 16 values
         const int sl = s & 7;
         const int lo = (int)((scb[sl >> 2] >> (8 * (sl & 3) + (s < 8 ? 0 : 4))) & 15u);
         const int hi = (int)((scb[2] >> (8 * (s & 3) + 2 * (s >> 2))) & 3u);
@@ -227,140 +228,147 @@ __global__ __launch_bounds__(kThreads) void k_gateup(const int8_t* __restrict__ 
       uint4* udst = reinterpret_cast<uint4*>(As[b] + ur * kOpStride + 128 * un + 32 * uj);
       udst[0] = uint4{o[0], o[1], o[2], o[3]};
       udst[1] = uint4{o[4], o[5], o[6], o[7]};
-      if (uq == 0) dws[b][ur] = half_bits_to_float(scw.w & 0xffffu);
     }
   };
 
-  v16i magic;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) magic[i] = kMagicBits;
+  // =========================== consumer state ===========================
+  const int fsub = wave & 1, tsub = (wave >> 1) & 3;
+  const int col = lane & 31, khalf = lane >> 5;
+  const v16i zero = {};
   float accg[16], accu[16];
-
-  // ---- prologue: L(0), S(0), U(0), L(1)
-  fetch_ids(0);
-  __syncthreads();
-  load_next();
-  store(0);
-  __syncthreads();
-  if (n_steps > 1) load_next();
-  unpack(0);
-  __syncthreads();
-
   int cj = 0, csb = 0;  // item index and super-block of the MFMA step
   Item cur = item_info((int)blockIdx.x, nft, tiles, offsets);
-  for (int g = 0; g < n_steps; ++g) {
-    const int b = g & 1;
-    if (g + 1 < n_steps) store(b ^ 1);
-    __syncthreads();
-    if (g + 2 < n_steps) load_next();
-    if (g + 1 < n_steps) unpack(b ^ 1);
 
-    // ---- M(g): MFMA per 32-value block, fp32 fold
+  auto mfma_step = [&](int b) {
     const bool active = 32 * tsub < cur.cnt;
     if (csb == 0) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) accg[i] = accu[i] = 0.f;
     }
-    if (active) {
-      const int8_t* ag = As[b] + (32 * fsub + col) * kOpStride + 16 * khalf;
-      const int8_t* au = As[b] + (kFT + 32 * fsub + col) * kOpStride + 16 * khalf;
-      const int8_t* bp = Bs[b] + (32 * tsub + col) * kOpStride + 16 * khalf;
-      const float4 dx0 = *reinterpret_cast<const float4*>(&dxs[b][(32 * tsub + col) * 8]);
-      const float4 dx1 = *reinterpret_cast<const float4*>(&dxs[b][(32 * tsub + col) * 8 + 4]);
-      const float dxv[8] = {dx0.x, dx0.y, dx0.z, dx0.w, dx1.x, dx1.y, dx1.z, dx1.w};  // -d_x
-      int probe_pair = -1;
-      if (PROBE) {
-        const int n = 32 * tsub + col;
-        if (n < cur.cnt) probe_pair = perm[cur.pos0 + n];
-      }
-      float sbg[16], sbu[16];
+    if (!active) return;
+    const int8_t* ag = As[b] + (32 * fsub + col) * kOpStride + 16 * khalf;
+    const int8_t* au = As[b] + (kFT + 32 * fsub + col) * kOpStride + 16 * khalf;
+    const int8_t* bp = Bs[b] + (32 * tsub + col) * kOpStride + 16 * khalf;
+    const float4 dx0 = *reinterpret_cast<const float4*>(&dxs[b][(32 * tsub + col) * 8]);
+    const float4 dx1 = *reinterpret_cast<const float4*>(&dxs[b][(32 * tsub + col) * 8 + 4]);
+    const float dxv[8] = {dx0.x, dx0.y, dx0.z, dx0.w, dx1.x, dx1.y, dx1.z, dx1.w};  // -d_x
+    int probe_pair = -1;
+    if (PROBE) {
+      const int n = 32 * tsub + col;
+      if (n < cur.cnt) probe_pair = perm[cur.pos0 + n];
+    }
+    float sbg[16], sbu[16];
+    v4i va = *reinterpret_cast<const v4i*>(ag);
+    v4i vu = *reinterpret_cast<const v4i*>(au);
+    v4i vb = *reinterpret_cast<const v4i*>(bp);
 #pragma unroll
-      for (int kb = 0; kb < 8; ++kb) {
-        const v4i va = *reinterpret_cast<const v4i*>(ag + 32 * kb);
-        const v4i vu = *reinterpret_cast<const v4i*>(au + 32 * kb);
-        const v4i vb = *reinterpret_cast<const v4i*>(bp + 32 * kb);
-        const v16i ig = __builtin_amdgcn_mfma_i32_32x32x32_i8(va, vb, magic, 0, 0, 0);
-        const v16i iu = __builtin_amdgcn_mfma_i32_32x32x32_i8(vu, vb, magic, 0, 0, 0);
-        const float d = dxv[kb];
-        const float c = -kMagic * d;  // exact
+    for (int kb = 0; kb < 8; ++kb) {
+      const v16i ig = __builtin_amdgcn_mfma_i32_32x32x32_i8(va, vb, zero, 0, 0, 0);  // -I32
+      const v16i iu = __builtin_amdgcn_mfma_i32_32x32x32_i8(vu, vb, zero, 0, 0, 0);
+      if (kb < 7) {  // next block's operands
+        va = *reinterpret_cast<const v4i*>(ag + 32 * (kb + 1));
+        vu = *reinterpret_cast<const v4i*>(au + 32 * (kb + 1));
+        vb = *reinterpret_cast<const v4i*>(bp + 32 * (kb + 1));
+      }
+      const float d = dxv[kb];  // -d_x
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        sbg[i] = kb == 0 ? d * (float)ig[i] : __builtin_fmaf(d, (float)ig[i], sbg[i]);
+        sbu[i] = kb == 0 ? d * (float)iu[i] : __builtin_fmaf(d, (float)iu[i], sbu[i]);
+      }
+      if (PROBE && probe_pair >= 0) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float tg = __builtin_fmaf(d, as_float(ig[i]), c);  // fl(d_x * I32)
-          const float tu = __builtin_fmaf(d, as_float(iu[i]), c);
-          sbg[i] = kb == 0 ? tg : sbg[i] + tg;
-          sbu[i] = kb == 0 ? tu : sbu[i] + tu;
+          const int f = cur.f0 + 32 * fsub + 8 * (i >> 2) + 4 * khalf + (i & 3);
+          const int rg = f - probe.row0, ru = F + f - probe.row0;
+          const int64_t o = (int64_t)probe_pair * probe.rows;
+          if (f < F && rg >= 0 && rg < probe.rows) probe.out[(o + rg) * nxb + csb * 8 + kb] = -ig[i];
+          if (f < F && ru >= 0 && ru < probe.rows) probe.out[(o + ru) * nxb + csb * 8 + kb] = -iu[i];
         }
-        if (PROBE && probe_pair >= 0) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int f = cur.f0 + 32 * fsub + 8 * (i >> 2) + 4 * khalf + (i & 3);
-            const int rg = f - probe.row0, ru = F + f - probe.row0;
-            const int64_t o = (int64_t)probe_pair * probe.rows;
-            if (f < F && rg >= 0 && rg < probe.rows) probe.out[(o + rg) * nxb + csb * 8 + kb] = kMagicBits - ig[i];
-            if (f < F && ru >= 0 && ru < probe.rows) probe.out[(o + ru) * nxb + csb * 8 + kb] = kMagicBits - iu[i];
-          }
-        }
-      }
-      const float4* dgp = reinterpret_cast<const float4*>(dws[b] + 32 * fsub + 4 * khalf);
-      const float4* dup = reinterpret_cast<const float4*>(dws[b] + kFT + 32 * fsub + 4 * khalf);
-#pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        const float4 wg = dgp[2 * qq], wu = dup[2 * qq];  // rows 8qq + 4khalf + 0..3
-        accg[4 * qq + 0] = __builtin_fmaf(wg.x, sbg[4 * qq + 0], accg[4 * qq + 0]);
-        accg[4 * qq + 1] = __builtin_fmaf(wg.y, sbg[4 * qq + 1], accg[4 * qq + 1]);
-        accg[4 * qq + 2] = __builtin_fmaf(wg.z, sbg[4 * qq + 2], accg[4 * qq + 2]);
-        accg[4 * qq + 3] = __builtin_fmaf(wg.w, sbg[4 * qq + 3], accg[4 * qq + 3]);
-        accu[4 * qq + 0] = __builtin_fmaf(wu.x, sbu[4 * qq + 0], accu[4 * qq + 0]);
-        accu[4 * qq + 1] = __builtin_fmaf(wu.y, sbu[4 * qq + 1], accu[4 * qq + 1]);
-        accu[4 * qq + 2] = __builtin_fmaf(wu.z, sbu[4 * qq + 2], accu[4 * qq + 2]);
-        accu[4 * qq + 3] = __builtin_fmaf(wu.w, sbu[4 * qq + 3], accu[4 * qq + 3]);
       }
     }
+    const float4* dgp = reinterpret_cast<const float4*>(dws[b] + 32 * fsub + 4 * khalf);
+    const float4* dup = reinterpret_cast<const float4*>(dws[b] + kFT + 32 * fsub + 4 * khalf);
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      const float4 wg = dgp[2 * qq], wu = dup[2 * qq];  // rows 8qq + 4khalf + 0..3
+      accg[4 * qq + 0] = __builtin_fmaf(wg.x, sbg[4 * qq + 0], accg[4 * qq + 0]);
+      accg[4 * qq + 1] = __builtin_fmaf(wg.y, sbg[4 * qq + 1], accg[4 * qq + 1]);
+      accg[4 * qq + 2] = __builtin_fmaf(wg.z, sbg[4 * qq + 2], accg[4 * qq + 2]);
+      accg[4 * qq + 3] = __builtin_fmaf(wg.w, sbg[4 * qq + 3], accg[4 * qq + 3]);
+      accu[4 * qq + 0] = __builtin_fmaf(wu.x, sbu[4 * qq + 0], accu[4 * qq + 0]);
+      accu[4 * qq + 1] = __builtin_fmaf(wu.y, sbu[4 * qq + 1], accu[4 * qq + 1]);
+      accu[4 * qq + 2] = __builtin_fmaf(wu.z, sbu[4 * qq + 2], accu[4 * qq + 2]);
+      accu[4 * qq + 3] = __builtin_fmaf(wu.w, sbu[4 * qq + 3], accu[4 * qq + 3]);
+    }
+  };
 
-    if (++csb == nsb) {
-      // ---- epilogue of item cj: SwiGLU, q8_1 rounding of H per 32 features
-      if (active) {
-        // The q8_1 rule rounds every product to fp32 on its own (no FMA, no
-        // fused multiply-convert to fp16).
+  auto epilogue = [&]() {
+    // The q8_1 rule rounds every product to fp32 on its own (no FMA, no fused
+    // multiply-convert to fp16).
 #pragma clang fp contract(off)
-        const int n = 32 * tsub + col;
-        const int fb = cur.f0 + 32 * fsub;  // first feature of this 32-feature block
-        float h[16];
-        float amax = 0.f;
+    if (32 * tsub >= cur.cnt) return;
+    const int n = 32 * tsub + col;
+    const int fb = cur.f0 + 32 * fsub;  // first feature of this 32-feature block
+    float h[16];
+    float amax = 0.f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float gv = accg[i];
-          const float sig = __builtin_amdgcn_rcpf(1.0f + __expf(-gv));  // sigmoid (approximate reciprocal)
-          h[i] = gv * sig * accu[i];
-          amax = fmaxf(amax, fabsf(h[i]));
-        }
-        amax = fmaxf(amax, __shfl_xor(amax, 32));
-        const float d = amax / 127.0f;
-        const float id = d != 0.0f ? 1.0f / d : 0.0f;
-        int q[16];
-        int sum = 0;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          q[i] = (int)__builtin_roundf(h[i] * id);
-          sum += q[i];
-        }
-        sum += __shfl_xor(sum, 32);
-        if (n < cur.cnt && fb < F) {
-          const int64_t pos = cur.pos0 + n;
-          int8_t* dst = h_codes + pos * F + fb + 4 * khalf;
-#pragma unroll
-          for (int qq = 0; qq < 4; ++qq)
-            *reinterpret_cast<uint32_t*>(dst + 8 * qq) =
-                pack4(q[4 * qq], q[4 * qq + 1], q[4 * qq + 2], q[4 * qq + 3]);
-          if (khalf == 0)
-            h_ds[pos * (F / 32) + fb / 32] =
-                float_to_half_bits(d) | (float_to_half_bits(fp32_barrier(d * (float)sum)) << 16);
-        }
-      }
-      csb = 0;
-      if (++cj < my_items) cur = item_info((int)blockIdx.x + cj * G, nft, tiles, offsets);
+    for (int i = 0; i < 16; ++i) {
+      const float gv = accg[i];
+      const float sig = __builtin_amdgcn_rcpf(1.0f + __expf(-gv));  // sigmoid (approximate reciprocal)
+      h[i] = gv * sig * accu[i];
+      amax = fmaxf(amax, fabsf(h[i]));
     }
+    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    const float d = amax / 127.0f;
+    const float id = d != 0.0f ? 1.0f / d : 0.0f;
+    int q[16];
+    int sum = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      q[i] = (int)__builtin_roundf(h[i] * id);
+      sum += q[i];
+    }
+    sum += __shfl_xor(sum, 32);
+    if (n < cur.cnt && fb < F) {
+      const int64_t pos = cur.pos0 + n;
+      int8_t* dst = h_codes + pos * F + fb + 4 * khalf;
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq)
+        *reinterpret_cast<uint32_t*>(dst + 8 * qq) = pack4(q[4 * qq], q[4 * qq + 1], q[4 * qq + 2], q[4 * qq + 3]);
+      if (khalf == 0)
+        h_ds[pos * (F / 32) + fb / 32] =
+            float_to_half_bits(d) | (float_to_half_bits(fp32_barrier(d * (float)sum)) << 16);
+    }
+  };
+
+  // The two roles run separate loops (so their registers are not live at the
+  // same time) with the same barriers: two in the prologue, one per step.
+  if (producer) {
+    // prologue: operands of step 0 in buffer 0, loads of step 1 in flight
+    fetch_ids(0);
     __syncthreads();
+    load_next();
+    build(0);
+    __syncthreads();
+    if (n_steps > 1) load_next();
+    for (int g = 0; g < n_steps; ++g) {
+      if (g + 1 < n_steps) build((g & 1) ^ 1);
+      if (g + 2 < n_steps) load_next();
+      __syncthreads();
+    }
+  } else {
+    __syncthreads();
+    __syncthreads();
+    for (int g = 0; g < n_steps; ++g) {
+      mfma_step(g & 1);
+      if (++csb == nsb) {
+        epilogue();
+        csb = 0;
+        if (++cj < my_items) cur = item_info((int)blockIdx.x + cj * G, nft, tiles, offsets);
+      }
+      __syncthreads();
+    }
   }
 }
 
