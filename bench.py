@@ -17,6 +17,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
@@ -25,6 +26,8 @@ sys.path.insert(0, ROOT)
 
 PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA, 5.0 POP/s
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, 8 TB/s
+# fp32 VALU instructions without packed math: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
+PEAK_VALU_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12   # 39.3 T lane-ops/s
 METRIC = "expert-stage prefill tokens/s at T=5268; % int8 MFMA peak; HBM GB/s"
 
 
@@ -39,8 +42,13 @@ def algorithmic(wl, idx):
     dn_bytes = wl.L * (wl.F // 32) * 18
     ops_gateup = 2 * pv * 2 * wl.F * wl.L
     ops_down = 2 * pv * wl.L * wl.F
+    # per-block scale folds: one (convert or scale) and one accumulate per
+    # 32-value block result
+    fold_gateup = 2 * pv * 2 * wl.F * (wl.L // 32)
+    fold_down = 2 * pv * wl.L * (wl.F // 32)
     nbytes = (active * (gu_bytes + dn_bytes) + wl.T * (wl.L // 32) * 36 + wl.T * wl.k * 8 + wl.T * wl.L * 4)
     return dict(pairs=pv, active=active, ops_gateup=ops_gateup, ops_down=ops_down, bytes=nbytes,
+                fold_gateup=fold_gateup, fold_down=fold_down,
                 gu_bytes_active=active * gu_bytes, dn_bytes_active=active * dn_bytes)
 
 
@@ -132,16 +140,69 @@ def cpu_baseline(wl, target_s):
             "sample": f"first {n} of {wl.T} tokens of {wl.name} ({n * wl.k} routed pairs), {dt:.1f} s"}
 
 
+KERNEL_SOURCES = {"k_gateup": "gateup.hip", "k_down": "down.hip"}
+
+
+def kernel_source_hash(kernel):
+    """sha256 over the kernel's source file and the shared internal header."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in (KERNEL_SOURCES[kernel], "lat_moe_internal.h"):
+        h.update(open(os.path.join(ROOT, "quantized_latent_moe_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
+
+
 def read_traffic(kernel, workload):
-    """HBM bytes per launch from the committed counter summary, if one exists
-    for this kernel and workload (profiles/<kernel>_<workload>_traffic.txt)."""
+    """HBM bytes per launch from the committed counter summary
+    (profiles/<kernel>_<workload>_traffic.txt), or None if there is none or the
+    kernel's source has changed since the counters were taken."""
     p = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.txt")
     if not os.path.exists(p):
         return None
-    for line in open(p):
-        if line.startswith("hbm_bytes_per_launch"):
-            return int(float(line.split()[1]))
-    return None
+    vals = dict(line.split()[:2] for line in open(p) if line.startswith(("hbm_bytes_per_launch", "source_sha256")))
+    if vals.get("source_sha256") != kernel_source_hash(kernel) or "hbm_bytes_per_launch" not in vals:
+        return None
+    return int(float(vals["hbm_bytes_per_launch"]))
+
+
+def _pmc_rows(d):
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+        rows += list(csv.DictReader(open(f)))
+    return rows
+
+
+def pmc_summary(fetch_dir, write_dir, kernel, copy_mib):
+    """HBM bytes per launch of `kernel` from FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch), each scaled by what the same counter reads for the plain copy of
+    copy_mib MiB (torch.neg, one read and one write of every byte)."""
+    n = copy_mib << 20
+    out = {}
+    for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        per = {}
+        for r in _pmc_rows(d):
+            if r["Counter_Name"] != name:
+                continue
+            per.setdefault((r["Kernel_Name"], r["Dispatch_Id"]), 0.0)
+            per[(r["Kernel_Name"], r["Dispatch_Id"])] += float(r["Counter_Value"]) * 1024.0
+        copy = [v for (k, _), v in per.items() if "elementwise" in k]
+        kern = [v for (k, _), v in per.items() if re.search(r"::%s[<(]" % kernel, k)]
+        if not copy or not kern:
+            sys.exit(f"{name}: no copy ({len(copy)}) or {kernel} ({len(kern)}) dispatches in {d}")
+        copy_b = max(copy)                    # the copy dispatches (ignore smaller elementwise kernels)
+        scale = n / copy_b
+        out[name] = (sum(kern) / len(kern), copy_b, scale, len(kern))
+    fetch = out["FETCH_SIZE"][0] * out["FETCH_SIZE"][2]
+    write = out["WRITE_SIZE"][0] * out["WRITE_SIZE"][2]
+    print(f"kernel {kernel}")
+    for name, (kb, cb, sc, nk) in out.items():
+        print(f"{name}: {kb:.0f} B per launch (mean of {nk} dispatches); copy of {n} B reads as {cb:.0f} B; "
+              f"scale {sc:.4f}")
+    print(f"hbm_read_bytes_per_launch {fetch:.0f}")
+    print(f"hbm_write_bytes_per_launch {write:.0f}")
+    print(f"hbm_bytes_per_launch {fetch + write:.0f}")
 
 
 def main():
@@ -153,10 +214,18 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="first run a plain device copy of MIB MiB (three times), the reference for counter scaling")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of --calibrate-copy and exit")
+    ap.add_argument("--kernel", default="k_gateup", help="kernel the --pmc-summary is for")
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.kernel, args.calibrate_copy or 256)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the expert stage here is built and timed on a single MI355X "
-              f"(--gpus {args.gpus} is not supported; token-parallel sharding is described in DESIGN.md).",
+              f"(--gpus {args.gpus} is not supported: the token-parallel sharding across GPUs is not built).",
               file=sys.stderr)
         sys.exit(2)
 
@@ -165,6 +234,14 @@ def main():
     torch.cuda.set_device(0)
     wl = WORKLOADS[args.workload]
     print(f"[bench] workload {wl}", file=sys.stderr, flush=True)
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)   # reads n bytes, writes n bytes
+        torch.cuda.synchronize()
+        del src, dst
     st = Stage(wl)
     alg = algorithmic(wl, st.inputs.router_idx)
     ms, wall_ms = st.time_steps(args.steps, args.warmup)
@@ -174,13 +251,19 @@ def main():
     print("[bench] stage ms: " + ", ".join(f"{n}={v:.4f}" for n, v in zip(names, stages)), file=sys.stderr,
           flush=True)
     ops = {"gateup": alg["ops_gateup"], "down": alg["ops_down"]}
+    folds = {"gateup": alg["fold_gateup"], "down": alg["fold_down"]}
     dom = max(("gateup", "down"), key=lambda n: stages[names.index(n)])
     dom_ms = stages[names.index(dom)]
     achieved = ops[dom] / (dom_ms * 1e-3) / 1e12
     kernel = {"gateup": "k_gateup", "down": "k_down"}[dom]
+    fold_tops = folds[dom] / (dom_ms * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": kernel, "achieved": round(achieved, 2), "peak": PEAK_INT8_TOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 4),
-                "traffic": read_traffic(kernel, wl.name)}
+                "traffic": read_traffic(kernel, wl.name), "launch_ms": round(dom_ms, 5),
+                # the per-block fp32 scale fold on the VALU, the tighter ceiling of an
+                # int8 GEMM with one scale per 32 values (2 VALU ops per block result)
+                "fold_valu": {"achieved": round(fold_tops, 2), "peak": round(PEAK_VALU_TOPS, 1),
+                              "unit": "T lane-op/s", "frac": round(fold_tops / PEAK_VALU_TOPS, 4)}}
     total_ops = alg["ops_gateup"] + alg["ops_down"]
     out = {
         "metric": METRIC,
