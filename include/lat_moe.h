@@ -54,8 +54,8 @@ extern "C" {
 
 /* Shapes of one call.  Supported: T >= 0, T * k < 2^31, L % 256 == 0
  * (256 <= L <= 65536), F % 32 == 0 (32 <= F <= 65536), 1 <= E <= 1024,
- * 1 <= k <= E, T * L < 2^31, and one expert's gate/up weights below 2 GiB
- * (2F * L/256 * 110 < 2^31 bytes). */
+ * 1 <= k <= E, T * L < 2^31, T * k * F < 2^31, and one expert's weights
+ * below 2 GiB (2F * L/256 * 110 and L * F/32 * 18 bytes < 2^31). */
 typedef struct lat_moe_shapes {
   int64_t T; /* tokens */
   int32_t L; /* latent dimension */

@@ -22,8 +22,10 @@ bool shapes_ok(const lat_moe_shapes* s) {
   if (s->T * (int64_t)s->k >= (int64_t)1 << 31) return false;
   // one expert's gate/up rows stay below 2 GiB (kernels address within an expert with 32-bit offsets)
   if ((int64_t)2 * s->F * (s->L / 256) * 110 >= (int64_t)1 << 31) return false;
-  // the activation codes too ([T][L] int8, 32-bit offsets)
+  // the activation codes, H codes and one expert's down weights too (32-bit offsets)
   if (s->T * (int64_t)s->L >= (int64_t)1 << 31) return false;
+  if (s->T * (int64_t)s->k * s->F >= (int64_t)1 << 31) return false;
+  if ((int64_t)s->L * (s->F / 32) * 18 >= (int64_t)1 << 31) return false;
   return true;
 }
 

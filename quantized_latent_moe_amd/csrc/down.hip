@@ -47,12 +47,15 @@ __device__ __forceinline__ uint32_t iq4_lookup(uint32_t nib) {
   const uint32_t sel = nib & 0x07070707u;
   const uint32_t lo = __builtin_amdgcn_perm(kTab1, kTab0, sel);
   const uint32_t hi = __builtin_amdgcn_perm(kTab3, kTab2, sel);
-  const uint32_t m = ((nib >> 3) & 0x01010101u) * 0xffu;
+  const uint32_t b3 = (nib >> 3) & 0x01010101u;
+  uint32_t b3s = b3 << 8;
+  asm("" : "+v"(b3s));  // keeps b3 * 255 as a shift and a subtract (a multiply is quarter rate)
+  const uint32_t m = b3s - b3;  // 0xff in every byte whose index has bit 3 set
   return (lo & ~m) | (hi & m);
 }
 
 template <bool PROBE, bool ALIGNED16>
-__global__ __launch_bounds__(kThreads) void k_down(const uint8_t* __restrict__ dn, const float* __restrict__ router_w,
+__global__ __launch_bounds__(kThreads) void k_down_generic(const uint8_t* __restrict__ dn, const float* __restrict__ router_w,
                                                    const int32_t* __restrict__ perm,
                                                    const int32_t* __restrict__ tiles,
                                                    const int32_t* __restrict__ offsets,
@@ -238,14 +241,307 @@ __global__ __launch_bounds__(kThreads) void k_down(const uint8_t* __restrict__ d
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Main path (F % 256 == 0, so every 8-block K step of a row is 144 contiguous,
+// 16-byte-aligned bytes): a persistent, warp-specialized kernel.
+//
+// One workgroup of 12 waves per CU walks the items (expert, tile of up to 128
+// sorted pairs, 128 output rows) round-robin: item i = tile * nlt + row tile,
+// workgroup w takes w, w + G, ...; with G a multiple of nlt = L/128 it keeps
+// one row tile, and the 8 XCDs each serve a fixed eighth of every expert's
+// rows from L2.
+//   8 consumer waves: wave c owns rows 32*(c&3) .. +31 against tokens
+//     64*(c>>2) .. +63 (two 32x32 tiles sharing the weight fragment).  Per
+//     block: J = v_mfma_i32_32x32x32_i8 with the accumulator initialised to
+//     the bits of 1.5 * 2^23, so the result reads as the float 1.5 * 2^23 + J;
+//     t = fma(d_H, f, -1.5 * 2^23 * d_H) is exactly fl(d_H * J) (d_H is the
+//     lane's token), acc = fma(d_dn, t, acc) (d_dn per row, from fp16).
+//   4 producer waves: producer p owns rows 32p .. +31 and tokens 32p .. +31.
+//     Per step it loads its rows' 144-byte chunks (16-byte buffer loads), its
+//     tokens' H codes and fp16 d_H (out-of-range offsets give zeros for
+//     padding), writes them to LDS, and expands its rows' IQ4_NL blocks: two
+//     lanes per row, each reading 72 bytes (4 blocks) and turning 4 indices
+//     into 4 table bytes with two v_perm_b32 and a select.
+// Operand rows are 256 bytes with their 16-byte chunks XOR-swizzled by the
+// row's low 4 bits (conflict-free 16-byte reads without padding); operands
+// and scales are double-buffered, one barrier per step.
+constexpr int kWsConsumers = 8, kWsProducers = 4;
+constexpr int kWsThreads = 64 * (kWsConsumers + kWsProducers);  // 768
+constexpr int kWsLT = 128;                                      // output rows per item
+constexpr int kWsNT = kTileN;                                   // tokens per item
+constexpr int kWsStep = 8 * kIq4Bytes;                          // 144 raw bytes per row and step
+static_assert(kWsLT == 32 * kWsProducers && kWsNT == 32 * kWsProducers, "a producer owns 32 rows and 32 tokens");
+
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 256 + ((chunk ^ (row & 15)) << 4); }
+
+// Position of row r (0..127) in the per-block d_dn vector: the 16 rows a lane
+// of a 32x32 tile holds (8(i/4) + 4*half + i%4) are contiguous.
+__device__ __forceinline__ int dd_pos(int r) {
+  const int q = (r >> 3) & 3, h = (r >> 2) & 1, m = r & 3;
+  return (r & ~31) + 16 * h + 4 * q + m;
+}
+
+struct DItem {
+  int e, pos0, cnt, l0;
+};
+
+__device__ __forceinline__ DItem ditem(int i, int nlt, const int32_t* tiles, const int32_t* offsets) {
+  DItem it;
+  const int tile = i / nlt;
+  it.l0 = (i - tile * nlt) * kWsLT;
+  it.e = tiles[2 * tile];
+  it.pos0 = tiles[2 * tile + 1];
+  it.cnt = min(kWsNT, offsets[it.e + 1] - it.pos0);
+  return it;
+}
+
+template <bool PROBE>
+__global__ __launch_bounds__(kWsThreads) void k_down(const uint8_t* __restrict__ dn, const float* __restrict__ router_w,
+                                                     const int32_t* __restrict__ perm,
+                                                     const int32_t* __restrict__ tiles,
+                                                     const int32_t* __restrict__ offsets,
+                                                     const int32_t* __restrict__ misc, int pairs, int L, int F,
+                                                     const int8_t* __restrict__ h_codes,
+                                                     const uint32_t* __restrict__ h_ds, float* __restrict__ slots,
+                                                     ProbeRows probe) {
+  __shared__ __align__(16) uint8_t raw[kWsLT * kWsStep];
+  __shared__ __align__(16) int8_t As[2][kWsLT * 256];
+  __shared__ __align__(16) int8_t Bs[2][kWsNT * 256];
+  __shared__ __align__(16) _Float16 dds[2][8][kWsLT];  // d_dn per block, rows in dd_pos order
+  __shared__ __align__(16) float dhs[2][kWsNT][8];      // d_H per token and block
+
+  const int nlt = L / kWsLT;
+  const int n_items = misc[kMiscTiles] * nlt;
+  const int G = gridDim.x;
+  if ((int)blockIdx.x >= n_items) return;
+  const int my_items = (n_items - 1 - (int)blockIdx.x) / G + 1;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: role branches stay scalar
+  const int nfb = F / 32, nsb = F / 256;
+  const int row_bytes = nfb * kIq4Bytes;
+  const int n_steps = my_items * nsb;
+
+  if (wave >= kWsConsumers) {
+    // =============================== producer ===============================
+    const int p = wave - kWsConsumers;
+    const rsrc_t rh_src = make_rsrc(h_codes, (uint32_t)(pairs * F));
+    const rsrc_t rs_src = make_rsrc(h_ds, (uint32_t)(pairs * nfb * 4));
+    rsrc_t rw_src;
+    // raw: piece i = lane + 64m (m < 5, i < 288) of this producer's 32 rows x
+    // 9 pieces; H codes: token 32p + 4a + (lane >> 4), chunk lane & 15; d_H:
+    // token 32p + 8c + (lane >> 3), block lane & 7.
+    int qoff[5], hoff[8], soff[4];
+    int lj = 0, lsb = 0, ql0 = -1;
+    bool need_setup = true;
+    auto setup = [&](int j) {
+      const DItem it = ditem((int)blockIdx.x + j * G, nlt, tiles, offsets);
+      const int e = __builtin_amdgcn_readfirstlane(it.e);
+      rw_src = make_rsrc(dn + (int64_t)e * L * row_bytes, (uint32_t)(L * row_bytes));
+      if (it.l0 != ql0) {  // once per workgroup when the grid is a multiple of nlt
+        ql0 = it.l0;
+#pragma unroll
+        for (int m = 0; m < 5; ++m) {
+          const int i = lane + 64 * m, r = i / 9, c = i - 9 * r;
+          const int row = it.l0 + 32 * p + r;
+          qoff[m] = (i < 288 && row < L) ? row * row_bytes + 16 * c : kOutOfRange;
+        }
+      }
+#pragma unroll
+      for (int a = 0; a < 8; ++a) {
+        const int n = 32 * p + 4 * a + (lane >> 4);
+        hoff[a] = n < it.cnt ? (it.pos0 + n) * F + 16 * (lane & 15) : kOutOfRange;
+      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int n = 32 * p + 8 * c + (lane >> 3);
+        soff[c] = n < it.cnt ? ((it.pos0 + n) * nfb + (lane & 7)) * 4 : kOutOfRange;
+      }
+    };
+    uint4 rq[5], rx[8];
+    uint32_t rd[4];
+    auto load_next = [&]() {
+      if (need_setup) {
+        setup(lj);
+        need_setup = false;
+      }
+      const int sq = __builtin_amdgcn_readfirstlane(lsb * kWsStep);  // scalar offsets stay in SGPRs
+      const int sx = __builtin_amdgcn_readfirstlane(lsb * 256);
+      const int sd = __builtin_amdgcn_readfirstlane(lsb * 32);
+#pragma unroll
+      for (int m = 0; m < 5; ++m) rq[m] = buf_u128(rw_src, qoff[m], sq);
+#pragma unroll
+      for (int a = 0; a < 8; ++a) rx[a] = buf_u128(rh_src, hoff[a], sx);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) rd[c] = buf_u32(rs_src, soff[c], sd);
+      if (++lsb == nsb) {
+        lsb = 0;
+        need_setup = ++lj < my_items;
+      }
+    };
+    auto build = [&](int b) {
+      uint4* raw16 = reinterpret_cast<uint4*>(raw + 32 * p * kWsStep);
+#pragma unroll
+      for (int m = 0; m < 5; ++m)
+        if (m < 4 || lane < 32) raw16[lane + 64 * m] = rq[m];
+#pragma unroll
+      for (int a = 0; a < 8; ++a) {
+        const int n = 32 * p + 4 * a + (lane >> 4);
+        *reinterpret_cast<uint4*>(Bs[b] + swz(n, lane & 15)) = rx[a];
+      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c) dhs[b][32 * p + 8 * c + (lane >> 3)][lane & 7] = half_bits_to_float(rd[c] & 0xffffu);
+      // expand: row 32p + (lane & 31), blocks 4*(lane >> 5) .. +3 from the 72
+      // bytes at 72*(lane >> 5) of the row's chunk
+      const int r = 32 * p + (lane & 31), hb = lane >> 5;
+      const uint2* src = reinterpret_cast<const uint2*>(raw + r * kWsStep + 72 * hb);
+      uint32_t w[18];
+#pragma unroll
+      for (int i = 0; i < 9; ++i) {
+        const uint2 v = src[i];
+        w[2 * i] = v.x;
+        w[2 * i + 1] = v.y;
+      }
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int o = 18 * kk;  // block kk: d at bytes o..o+1, indices at o+2..o+17
+        const uint32_t dbits = (o & 2) ? (w[o >> 2] >> 16) : (w[o >> 2] & 0xffffu);
+        uint32_t nib[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int ob = o + 2 + 4 * jj;
+          nib[jj] = (ob & 3) ? __builtin_amdgcn_alignbyte(w[(ob >> 2) + 1], w[ob >> 2], ob & 3) : w[ob >> 2];
+        }
+        // element l < 16: low nibble of byte l; element l + 16: high nibble
+        const uint4 lo = {iq4_lookup(nib[0] & 0x0f0f0f0fu), iq4_lookup(nib[1] & 0x0f0f0f0fu),
+                          iq4_lookup(nib[2] & 0x0f0f0f0fu), iq4_lookup(nib[3] & 0x0f0f0f0fu)};
+        const uint4 hi = {iq4_lookup((nib[0] >> 4) & 0x0f0f0f0fu), iq4_lookup((nib[1] >> 4) & 0x0f0f0f0fu),
+                          iq4_lookup((nib[2] >> 4) & 0x0f0f0f0fu), iq4_lookup((nib[3] >> 4) & 0x0f0f0f0fu)};
+        const int kg = 4 * hb + kk;
+        *reinterpret_cast<uint4*>(As[b] + swz(r, 2 * kg)) = lo;
+        *reinterpret_cast<uint4*>(As[b] + swz(r, 2 * kg + 1)) = hi;
+        dds[b][kg][dd_pos(r)] = __builtin_bit_cast(_Float16, (uint16_t)dbits);
+      }
+    };
+
+    load_next();
+    build(0);
+    __syncthreads();
+    if (n_steps > 1) load_next();
+    for (int g = 0; g < n_steps; ++g) {
+      if (g + 1 < n_steps) build((g & 1) ^ 1);
+      if (g + 2 < n_steps) load_next();
+      __syncthreads();
+    }
+    return;
+  }
+
+  // =============================== consumer ===============================
+  const int rs = wave & 3, th = wave >> 2;
+  const int col = lane & 31, khalf = lane >> 5;
+  const int xo = (khalf ^ (col & 15)) << 4;  // chunk (2kb + khalf) of a row with these low bits: 32kb ^ xo
+  v16i magic;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) magic[i] = kMagicBits;
+  float acc0[16], acc1[16];
+  int cj = 0, csb = 0;
+  DItem cur = ditem((int)blockIdx.x, nlt, tiles, offsets);
+  int pair0 = -1, pair1 = -1;
+  float w0 = 0.f, w1 = 0.f;
+  __syncthreads();
+  for (int g = 0; g < n_steps; ++g) {
+    const int b = g & 1;
+    const int n0 = 64 * th + col, n1 = n0 + 32;
+    if (csb == 0) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc0[i] = acc1[i] = 0.f;
+      pair0 = n0 < cur.cnt ? perm[cur.pos0 + n0] : -1;
+      pair1 = n1 < cur.cnt ? perm[cur.pos0 + n1] : -1;
+      w0 = pair0 >= 0 ? router_w[pair0] : 0.f;
+      w1 = pair1 >= 0 ? router_w[pair1] : 0.f;
+    }
+    if (64 * th < cur.cnt) {
+      const int8_t* ap = As[b] + (32 * rs + col) * 256;
+      const int8_t* bp0 = Bs[b] + n0 * 256;
+      const int8_t* bp1 = Bs[b] + n1 * 256;
+      const float4 h00 = *reinterpret_cast<const float4*>(&dhs[b][n0][0]);
+      const float4 h01 = *reinterpret_cast<const float4*>(&dhs[b][n0][4]);
+      const float4 h10 = *reinterpret_cast<const float4*>(&dhs[b][n1][0]);
+      const float4 h11 = *reinterpret_cast<const float4*>(&dhs[b][n1][4]);
+      const float dh0[8] = {h00.x, h00.y, h00.z, h00.w, h01.x, h01.y, h01.z, h01.w};
+      const float dh1[8] = {h10.x, h10.y, h10.z, h10.w, h11.x, h11.y, h11.z, h11.w};
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb) {
+        const int off = (32 * kb) ^ xo;
+        const v4i va = *reinterpret_cast<const v4i*>(ap + off);
+        const v4i vb0 = *reinterpret_cast<const v4i*>(bp0 + off);
+        const v4i vb1 = *reinterpret_cast<const v4i*>(bp1 + off);
+        const v16i j0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(va, vb0, magic, 0, 0, 0);
+        const v16i j1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(va, vb1, magic, 0, 0, 0);
+        // d_dn of this lane's 16 rows for block kb (fp16, contiguous)
+        const uint4 dq0 = *reinterpret_cast<const uint4*>(&dds[b][kb][32 * rs + 16 * khalf]);
+        const uint4 dq1 = *reinterpret_cast<const uint4*>(&dds[b][kb][32 * rs + 16 * khalf + 8]);
+        const uint32_t dq[8] = {dq0.x, dq0.y, dq0.z, dq0.w, dq1.x, dq1.y, dq1.z, dq1.w};
+        const float c0 = -kMagic * dh0[kb], c1 = -kMagic * dh1[kb];  // exact
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float dd = half_bits_to_float((i & 1) ? (dq[i >> 1] >> 16) : (dq[i >> 1] & 0xffffu));
+          acc0[i] = __builtin_fmaf(dd, __builtin_fmaf(dh0[kb], as_float(j0[i]), c0), acc0[i]);
+          acc1[i] = __builtin_fmaf(dd, __builtin_fmaf(dh1[kb], as_float(j1[i]), c1), acc1[i]);
+        }
+        if (PROBE) {
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const int pr = t ? pair1 : pair0;
+            if (pr >= 0) {
+#pragma unroll
+              for (int i = 0; i < 16; ++i) {
+                const int l = cur.l0 + 32 * rs + 8 * (i >> 2) + 4 * khalf + (i & 3);
+                const int rr = l - probe.row0;
+                if (rr >= 0 && rr < probe.rows)
+                  probe.out[((int64_t)pr * probe.rows + rr) * nfb + csb * 8 + kb] =
+                      (t ? j1[i] : j0[i]) - kMagicBits;
+              }
+            }
+          }
+        }
+      }
+    }
+    if (++csb == nsb) {
+      // ---- weighted output rows into the pairs' slots
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int pr = t ? pair1 : pair0;
+        const float wgt = t ? w1 : w0;
+        if (pr >= 0) {
+          float* dst = slots + (int64_t)pr * L + cur.l0 + 32 * rs + 4 * khalf;
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) {
+            const float* a = t ? acc1 : acc0;
+            float4 v;
+            v.x = a[4 * qq + 0] * wgt;
+            v.y = a[4 * qq + 1] * wgt;
+            v.z = a[4 * qq + 2] * wgt;
+            v.w = a[4 * qq + 3] * wgt;
+            *reinterpret_cast<float4*>(dst + 8 * qq) = v;
+          }
+        }
+      }
+      csb = 0;
+      if (++cj < my_items) cur = ditem((int)blockIdx.x + cj * G, nlt, tiles, offsets);
+    }
+    __syncthreads();
+  }
+}
+
 template <bool PROBE>
 void launch_variant(bool aligned, dim3 grid, hipStream_t st, const uint8_t* dn, const float* router_w,
                     const Shapes& s, const Work& w, ProbeRows probe) {
   if (aligned)
-    hipLaunchKernelGGL((k_down<PROBE, true>), grid, dim3(kThreads), 0, st, dn, router_w, w.perm, w.tiles, w.offsets,
+    hipLaunchKernelGGL((k_down_generic<PROBE, true>), grid, dim3(kThreads), 0, st, dn, router_w, w.perm, w.tiles, w.offsets,
                        w.misc, s.L, s.F, w.h_codes, w.h_ds, w.slots, probe);
   else
-    hipLaunchKernelGGL((k_down<PROBE, false>), grid, dim3(kThreads), 0, st, dn, router_w, w.perm, w.tiles, w.offsets,
+    hipLaunchKernelGGL((k_down_generic<PROBE, false>), grid, dim3(kThreads), 0, st, dn, router_w, w.perm, w.tiles, w.offsets,
                        w.misc, s.L, s.F, w.h_codes, w.h_ds, w.slots, probe);
 }
 
@@ -253,6 +549,21 @@ void launch_variant(bool aligned, dim3 grid, hipStream_t st, const uint8_t* dn, 
 
 hipError_t launch_down(const uint8_t* dn, const float* router_w, const Shapes& s, const Work& w,
                        const ProbeRows* probe, hipStream_t st) {
+  const ProbeRows none = {nullptr, 0, 0};
+  if (s.F % 256 == 0 && ((uintptr_t)dn & 15u) == 0) {
+    // one persistent workgroup per CU, a multiple of the row-tile count when possible
+    const int nlt = s.L / kWsLT;
+    int grid = w.num_cus;
+    if (grid >= nlt) grid -= grid % nlt;
+    const int pairs = (int)s.pairs();
+    if (probe)
+      hipLaunchKernelGGL(k_down<true>, dim3(grid), dim3(kWsThreads), 0, st, dn, router_w, w.perm, w.tiles, w.offsets,
+                         w.misc, pairs, s.L, s.F, w.h_codes, w.h_ds, w.slots, *probe);
+    else
+      hipLaunchKernelGGL(k_down<false>, dim3(grid), dim3(kWsThreads), 0, st, dn, router_w, w.perm, w.tiles,
+                         w.offsets, w.misc, pairs, s.L, s.F, w.h_codes, w.h_ds, w.slots, none);
+    return hipGetLastError();
+  }
   const dim3 grid(w.max_tiles, s.L / kLT);
   // 16-byte staging needs every row (and so every 8-block step) 16-byte aligned;
   // that also means F is a multiple of 256, so every step is a full 144-byte chunk.
@@ -260,7 +571,7 @@ hipError_t launch_down(const uint8_t* dn, const float* router_w, const Shapes& s
   if (probe)
     launch_variant<true>(aligned, grid, st, dn, router_w, s, w, *probe);
   else
-    launch_variant<false>(aligned, grid, st, dn, router_w, s, w, ProbeRows{nullptr, 0, 0});
+    launch_variant<false>(aligned, grid, st, dn, router_w, s, w, none);
   return hipGetLastError();
 }
 
