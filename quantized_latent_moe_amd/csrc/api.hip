@@ -126,8 +126,7 @@ int forward_impl(const void* x, const int32_t* idx, const float* w, const void* 
   hipEvent_t const* ev = (dbg && dbg->stage_events) ? reinterpret_cast<hipEvent_t const*>(dbg->stage_events) : nullptr;
   auto mark = [&](int i) { return ev ? hipEventRecord(ev[i], st) : hipSuccess; };
   if (mark(0) != hipSuccess) return LAT_MOE_ELAUNCH;
-  if (launch_route(idx, sh, wk, st) != hipSuccess) return LAT_MOE_ELAUNCH;
-  if (launch_x_split(xb, sh, wk, st) != hipSuccess) return LAT_MOE_ELAUNCH;
+  if (launch_route(idx, xb, sh, wk, st) != hipSuccess) return LAT_MOE_ELAUNCH;
   if (mark(1) != hipSuccess) return LAT_MOE_ELAUNCH;
   ProbeRows pg{nullptr, 0, 0}, pd{nullptr, 0, 0};
   if (dbg && dbg->gateup_i32) pg = ProbeRows{dbg->gateup_i32, dbg->gu_row0, dbg->gu_rows};

@@ -15,7 +15,7 @@ constexpr int kIq4Bytes = 18;    // 32 weights
 constexpr int kQ81Bytes = 36;    // 32 values
 
 // Pair ids are grouped per route chunk of this many pairs (one workgroup each).
-constexpr int kRouteChunk = 4096;
+constexpr int kRouteChunk = 1024;
 // Token (sorted pair) tile of the grouped GEMMs.
 constexpr int kTileN = 128;
 
@@ -106,8 +106,8 @@ __device__ __forceinline__ uint4 buf_u128(rsrc_t r, int voff, int soff) {
 }
 
 // Kernel launchers (each returns hipGetLastError() after the enqueue).
-hipError_t launch_route(const int32_t* idx, const Shapes& s, const Work& w, hipStream_t st);
-hipError_t launch_x_split(const uint8_t* x, const Shapes& s, const Work& w, hipStream_t st);
+// Sorts pairs by expert and splits the q8_1 activations x into codes and scales.
+hipError_t launch_route(const int32_t* idx, const uint8_t* x, const Shapes& s, const Work& w, hipStream_t st);
 hipError_t launch_gateup(const Shapes& s, const Work& w, const uint8_t* gu, const ProbeRows* probe, hipStream_t st);
 hipError_t launch_down(const uint8_t* dn, const float* router_w, const Shapes& s, const Work& w,
                        const ProbeRows* probe, hipStream_t st);

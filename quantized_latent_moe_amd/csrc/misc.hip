@@ -85,22 +85,6 @@ __global__ __launch_bounds__(256) void k_export_h(const int32_t* __restrict__ pe
   for (int w = 0; w < 8; ++w) dst[1 + w] = src[w];
 }
 
-// q8_1 activation blocks -> int8 codes [T][L] and fp32 scales [T][L/32], so the
-// gate/up kernel reads codes with aligned 16-byte loads.
-__global__ __launch_bounds__(256) void k_x_split(const uint8_t* __restrict__ x, int64_t nblocks,
-                                                 int8_t* __restrict__ xc, float* __restrict__ xd) {
-  const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (b >= nblocks) return;
-  const uint32_t* src = reinterpret_cast<const uint32_t*>(x + b * kQ81Bytes);
-  uint4 lo, hi;
-  lo.x = src[1]; lo.y = src[2]; lo.z = src[3]; lo.w = src[4];
-  hi.x = src[5]; hi.y = src[6]; hi.z = src[7]; hi.w = src[8];
-  uint4* dst = reinterpret_cast<uint4*>(xc + b * 32);
-  dst[0] = lo;
-  dst[1] = hi;
-  xd[b] = half_bits_to_float(src[0] & 0xffffu);
-}
-
 __global__ __launch_bounds__(256) void k_fill_zero(uint32_t* __restrict__ p, int64_t nwords) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i < nwords) p[i] = 0u;
@@ -118,12 +102,6 @@ inline unsigned blocks_for(int64_t n) { return (unsigned)((n + 255) / 256); }
 hipError_t launch_combine(const int32_t* idx, const Shapes& s, const Work& w, float* y, hipStream_t st) {
   const int64_t n = s.T * (s.L / 4);
   hipLaunchKernelGGL(k_combine, dim3(blocks_for(n)), dim3(256), 0, st, idx, w.slots, s.T, s.L, s.E, s.k, y);
-  return hipGetLastError();
-}
-
-hipError_t launch_x_split(const uint8_t* x, const Shapes& s, const Work& w, hipStream_t st) {
-  const int64_t nb = s.T * (s.L / 32);
-  hipLaunchKernelGGL(k_x_split, dim3(blocks_for(nb)), dim3(256), 0, st, x, nb, w.xc, w.xd);
   return hipGetLastError();
 }
 

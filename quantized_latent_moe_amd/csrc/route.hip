@@ -3,20 +3,176 @@
 // The grouped GEMMs read every expert's weights in place and need the pairs
 // routed to each expert together ("each expert read where it is", page "Run
 // Edge0-145B Q3_K on AMD HIP (Linux, gfx1100) #1", lat_q3k_w11.cu commit).
-// Three passes, no host synchronisation:
-//   1. per chunk of kRouteChunk pairs: LDS histogram of expert ids;
-//   2. one workgroup: per-expert exclusive prefix over chunks, expert offsets,
-//      and the table of (expert, token tile) work items for the GEMMs;
-//   3. per chunk: stable scatter of pair ids (ascending within an expert),
-//      ranks inside a wave from ballots over the id bits.
+// Result: perm (pair ids grouped by expert, ascending within an expert),
+// offsets[E+1], the table of (expert, first position) token tiles of kTileN
+// pairs, and the dropped / valid / tile counts.  No host synchronisation.
+//
+// Up to kSmallPairs pairs: one workgroup does everything (LDS histogram, block
+// scan, tile table, stable scatter in rounds of 1024 pairs).  Larger: three
+// passes over chunks of kRouteChunk pairs (per-chunk histograms; one
+// workgroup scanning chunks and experts; per-chunk stable scatter).  In both
+// the first launch carries extra workgroups that split the q8_1 activations
+// into int8 codes and fp32 scales (independent work, one launch fewer).
+// Stable ranks inside a wave come from ballots over the bits of the id.
 #include "lat_moe_internal.h"
 
 namespace latmoe {
 namespace {
 
+constexpr int kSmallPairs = 4096;
+constexpr int kSplitPerBlock = 1024;  // q8_1 blocks split per extra workgroup
+
+// q8_1 block b -> 32 codes at xc + 32b and the fp32 scale xd[b].
+__device__ __forceinline__ void split_block(const uint8_t* __restrict__ x, int64_t b, int8_t* __restrict__ xc,
+                                            float* __restrict__ xd) {
+  const uint32_t* src = reinterpret_cast<const uint32_t*>(x + b * kQ81Bytes);
+  uint4 lo, hi;
+  lo.x = src[1]; lo.y = src[2]; lo.z = src[3]; lo.w = src[4];
+  hi.x = src[5]; hi.y = src[6]; hi.z = src[7]; hi.w = src[8];
+  uint4* dst = reinterpret_cast<uint4*>(xc + b * 32);
+  dst[0] = lo;
+  dst[1] = hi;
+  xd[b] = half_bits_to_float(src[0] & 0xffffu);
+}
+
+// Exclusive prefix sum over the workgroup (blockDim.x a multiple of 64, at
+// most 1024); *total receives the sum.  scratch: 16 ints of LDS.
+__device__ int block_exclusive_scan(int v, int* scratch, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) scratch[wave] = x;
+  __syncthreads();
+  if (wave == 0) {
+    int s = lane < nw ? scratch[lane] : 0;
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) {
+      const int y = __shfl_up(s, d);
+      if (lane >= d) s += y;
+    }
+    if (lane < nw) scratch[lane] = s;
+  }
+  __syncthreads();
+  const int before = wave > 0 ? scratch[wave - 1] : 0;
+  *total = scratch[nw - 1];
+  __syncthreads();  // scratch may be reused right after
+  return before + x - v;
+}
+
+// Offsets, tile table and counts from per-expert totals cnt[e] (e < E <=
+// blockDim.x = 1024, in LDS); leaves each expert's first position in
+// first[e].  Every thread of the workgroup calls it.
+__device__ void finish_offsets(const int* cnt, int* first, int E, int bad, int32_t* __restrict__ offsets,
+                               int32_t* __restrict__ tiles, int32_t* __restrict__ misc, int* scratch) {
+  const int e = threadIdx.x;
+  const int c = e < E ? cnt[e] : 0;
+  const int nt = (c + kTileN - 1) / kTileN;
+  int total, ttotal;
+  const int off = block_exclusive_scan(c, scratch, &total);
+  const int toff = block_exclusive_scan(nt, scratch, &ttotal);
+  if (e < E) {
+    first[e] = off;
+    offsets[e] = off;
+    for (int i = 0; i < nt; ++i) {
+      tiles[2 * (toff + i)] = e;
+      tiles[2 * (toff + i) + 1] = off + i * kTileN;
+    }
+  }
+  if (threadIdx.x == 0) {
+    offsets[E] = total;
+    misc[kMiscTiles] = ttotal;
+    misc[kMiscDropped] = bad;
+    misc[kMiscValid] = total;
+  }
+}
+
+// Stable ranks of this wave's lanes among lanes with the same id; returns
+// the rank and sets *cnt to the number of such lanes (0 for invalid ids).
+__device__ __forceinline__ int wave_rank(int e, bool valid, int nbits, int* cnt) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  uint64_t same = __ballot(valid);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (e >> b) & 1;
+    const uint64_t m = __ballot(bit);
+    same &= bit ? m : ~m;
+  }
+  *cnt = valid ? __popcll(same) : 0;
+  return __popcll(same & below);
+}
+
+// ---- small batches: everything in workgroup 0; workgroups 1.. split x.
+__global__ __launch_bounds__(1024) void k_route_small(const int32_t* __restrict__ idx, int n, int E, int nbits,
+                                                      int32_t* __restrict__ offsets, int32_t* __restrict__ tiles,
+                                                      int32_t* __restrict__ misc, int32_t* __restrict__ perm,
+                                                      const uint8_t* __restrict__ x, int64_t nxb,
+                                                      int8_t* __restrict__ xc, float* __restrict__ xd) {
+  if (blockIdx.x > 0) {
+    const int64_t b = (int64_t)(blockIdx.x - 1) * kSplitPerBlock + threadIdx.x;
+    if (b < nxb) split_block(x, b, xc, xd);
+    return;
+  }
+  extern __shared__ int32_t sm[];  // cnt[E] | base[E] | wcnt[16][E]
+  __shared__ int scratch[16];
+  __shared__ int bad;
+  int* cnt = sm;
+  int* base = sm + E;
+  int* wcnt = sm + 2 * E;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
+  for (int i = threadIdx.x; i < 16 * E; i += blockDim.x) wcnt[i] = 0;
+  if (threadIdx.x == 0) bad = 0;
+  __syncthreads();
+  for (int p = threadIdx.x; p < n; p += blockDim.x) {
+    const int e = idx[p];
+    if ((unsigned)e < (unsigned)E)
+      atomicAdd(&cnt[e], 1);
+    else
+      atomicAdd(&bad, 1);
+  }
+  __syncthreads();
+  finish_offsets(cnt, base, E, bad, offsets, tiles, misc, scratch);
+  __syncthreads();
+  // stable scatter, 1024 pairs per round: rank in wave + counts of earlier waves
+  const int wave = threadIdx.x >> 6;
+  for (int r0 = 0; r0 < n; r0 += blockDim.x) {
+    const int p = r0 + threadIdx.x;
+    const int e = p < n ? idx[p] : -1;
+    const bool valid = (unsigned)e < (unsigned)E;
+    int c;
+    const int rank = wave_rank(e, valid, nbits, &c);
+    if (valid && rank == 0) wcnt[wave * E + e] = c;
+    __syncthreads();
+    if (valid) {
+      int before = 0;
+      for (int w = 0; w < wave; ++w) before += wcnt[w * E + e];  // 0 where a wave had no such id
+      perm[base[e] + before + rank] = p;
+    }
+    __syncthreads();
+    if (valid && rank == 0) {
+      atomicAdd(&base[e], c);
+      wcnt[wave * E + e] = 0;
+    }
+    __syncthreads();
+  }
+}
+
+// ---- large batches, pass 1: per-chunk histograms; workgroups past the
+// chunks split x.
 __global__ __launch_bounds__(256) void k_route_hist(const int32_t* __restrict__ idx, int64_t n_pairs, int E,
-                                                    int32_t* __restrict__ chunk_hist,
-                                                    int32_t* __restrict__ chunk_bad) {
+                                                    int nchunk, int32_t* __restrict__ chunk_hist,
+                                                    int32_t* __restrict__ chunk_bad, const uint8_t* __restrict__ x,
+                                                    int64_t nxb, int8_t* __restrict__ xc,
+                                                    float* __restrict__ xd) {
+  if ((int)blockIdx.x >= nchunk) {
+    const int64_t b0 = (int64_t)(blockIdx.x - nchunk) * kSplitPerBlock;
+    for (int i = threadIdx.x; i < kSplitPerBlock; i += blockDim.x)
+      if (b0 + i < nxb) split_block(x, b0 + i, xc, xd);
+    return;
+  }
   extern __shared__ int32_t hist[];  // [E]
   __shared__ int32_t bad;
   for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
@@ -36,13 +192,16 @@ __global__ __launch_bounds__(256) void k_route_hist(const int32_t* __restrict__ 
   if (threadIdx.x == 0) chunk_bad[blockIdx.x] = bad;
 }
 
+// Pass 2 (one workgroup): chunk prefixes per expert (in place), offsets,
+// tiles, counts.
 __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ chunk_hist,
                                                      const int32_t* __restrict__ chunk_bad, int nchunk, int E,
                                                      int32_t* __restrict__ offsets, int32_t* __restrict__ tiles,
                                                      int32_t* __restrict__ misc) {
-  __shared__ int32_t s_cnt[1024];
-  __shared__ int32_t s_off[1024];
-  __shared__ int32_t s_toff[1024];
+  __shared__ int32_t cnt[1024];
+  __shared__ int32_t first[1024];
+  __shared__ int scratch[16];
+  __shared__ int bad;
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
     int run = 0;
     for (int c = 0; c < nchunk; ++c) {
@@ -50,36 +209,18 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ chunk
       chunk_hist[(int64_t)c * E + e] = run;
       run += v;
     }
-    s_cnt[e] = run;
+    cnt[e] = run;
   }
+  int b = 0;
+  for (int c = threadIdx.x; c < nchunk; c += blockDim.x) b += chunk_bad[c];
+  if (threadIdx.x == 0) bad = 0;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int off = 0, toff = 0;
-    for (int e = 0; e < E; ++e) {
-      s_off[e] = off;
-      s_toff[e] = toff;
-      offsets[e] = off;
-      off += s_cnt[e];
-      toff += (s_cnt[e] + kTileN - 1) / kTileN;
-    }
-    offsets[E] = off;
-    int bad = 0;
-    for (int c = 0; c < nchunk; ++c) bad += chunk_bad[c];
-    misc[kMiscTiles] = toff;
-    misc[kMiscDropped] = bad;
-    misc[kMiscValid] = off;
-  }
+  if (b) atomicAdd(&bad, b);
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    const int nt = (s_cnt[e] + kTileN - 1) / kTileN;
-    for (int i = 0; i < nt; ++i) {
-      const int slot = s_toff[e] + i;
-      tiles[2 * slot] = e;
-      tiles[2 * slot + 1] = s_off[e] + i * kTileN;
-    }
-  }
+  finish_offsets(cnt, first, E, bad, offsets, tiles, misc, scratch);
 }
 
+// Pass 3: per chunk, stable scatter of pair ids.
 __global__ __launch_bounds__(256) void k_route_scatter(const int32_t* __restrict__ idx, int64_t n_pairs, int E,
                                                        int nbits, const int32_t* __restrict__ chunk_prefix,
                                                        const int32_t* __restrict__ offsets,
@@ -92,23 +233,16 @@ __global__ __launch_bounds__(256) void k_route_scatter(const int32_t* __restrict
     for (int w = 0; w < 4; ++w) wcnt[w * E + e] = 0;
   }
   __syncthreads();
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int wave = threadIdx.x >> 6;
   const int64_t cbase = (int64_t)blockIdx.x * kRouteChunk;
   for (int r = 0; r < kRouteChunk / 256; ++r) {
     const int64_t p = cbase + r * 256 + threadIdx.x;
     const int e = p < n_pairs ? idx[p] : -1;
     const bool valid = (unsigned)e < (unsigned)E;
-    uint64_t same = __ballot(valid);
-    for (int b = 0; b < nbits; ++b) {
-      const bool bit = (e >> b) & 1;
-      const uint64_t m = __ballot(bit);
-      same &= bit ? m : ~m;
-    }
-    const int rank = __popcll(same & below);
-    const int cnt = __popcll(same);
+    int c;
+    const int rank = wave_rank(e, valid, nbits, &c);
     const bool leader = valid && rank == 0;
-    if (leader) wcnt[wave * E + e] = cnt;
+    if (leader) wcnt[wave * E + e] = c;
     __syncthreads();
     if (valid) {
       int before = 0;
@@ -117,7 +251,7 @@ __global__ __launch_bounds__(256) void k_route_scatter(const int32_t* __restrict
     }
     __syncthreads();
     if (leader) {
-      atomicAdd(&base[e], cnt);
+      atomicAdd(&base[e], c);
       wcnt[wave * E + e] = 0;
     }
     __syncthreads();
@@ -126,12 +260,19 @@ __global__ __launch_bounds__(256) void k_route_scatter(const int32_t* __restrict
 
 }  // namespace
 
-hipError_t launch_route(const int32_t* idx, const Shapes& s, const Work& w, hipStream_t st) {
+hipError_t launch_route(const int32_t* idx, const uint8_t* x, const Shapes& s, const Work& w, hipStream_t st) {
   const int64_t n = s.pairs();
   int nbits = 0;
   while ((1 << nbits) < s.E) ++nbits;
-  hipLaunchKernelGGL(k_route_hist, dim3(w.nchunk), dim3(256), s.E * sizeof(int32_t), st, idx, n, s.E,
-                     w.chunk_hist, w.chunk_bad);
+  const int64_t nxb = s.T * (s.L / 32);
+  const unsigned xblocks = (unsigned)((nxb + kSplitPerBlock - 1) / kSplitPerBlock);
+  if (n <= kSmallPairs && s.E <= 512) {  // (2 + 16) * E ints of LDS
+    hipLaunchKernelGGL(k_route_small, dim3(1 + xblocks), dim3(1024), (2 + 16) * s.E * sizeof(int32_t), st, idx,
+                       (int)n, s.E, nbits, w.offsets, w.tiles, w.misc, w.perm, x, nxb, w.xc, w.xd);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(k_route_hist, dim3(w.nchunk + xblocks), dim3(256), s.E * sizeof(int32_t), st, idx, n, s.E,
+                     w.nchunk, w.chunk_hist, w.chunk_bad, x, nxb, w.xc, w.xd);
   hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(1024), 0, st, w.chunk_hist, w.chunk_bad, w.nchunk, s.E, w.offsets,
                      w.tiles, w.misc);
   hipLaunchKernelGGL(k_route_scatter, dim3(w.nchunk), dim3(256), 5 * s.E * sizeof(int32_t), st, idx, n, s.E, nbits,
