@@ -131,10 +131,15 @@ int forward_impl(const void* x, const int32_t* idx, const float* w, const void* 
   ProbeRows pg{nullptr, 0, 0}, pd{nullptr, 0, 0};
   if (dbg && dbg->gateup_i32) pg = ProbeRows{dbg->gateup_i32, dbg->gu_row0, dbg->gu_rows};
   if (dbg && dbg->down_i32) pd = ProbeRows{dbg->down_i32, dbg->dn_row0, dbg->dn_rows};
-  if (launch_gateup(sh, wk, static_cast<const uint8_t*>(gu), pg.out ? &pg : nullptr, st) != hipSuccess)
+  const bool small = small_path(sh);  // decode-sized batch: GEMV-shaped kernels
+  const uint8_t* gub = static_cast<const uint8_t*>(gu);
+  const uint8_t* dnb = static_cast<const uint8_t*>(dn);
+  if ((small ? launch_gateup_small(sh, wk, gub, pg.out ? &pg : nullptr, st)
+             : launch_gateup(sh, wk, gub, pg.out ? &pg : nullptr, st)) != hipSuccess)
     return LAT_MOE_ELAUNCH;
   if (mark(2) != hipSuccess) return LAT_MOE_ELAUNCH;
-  if (launch_down(static_cast<const uint8_t*>(dn), w, sh, wk, pd.out ? &pd : nullptr, st) != hipSuccess)
+  if ((small ? launch_down_small(dnb, w, sh, wk, pd.out ? &pd : nullptr, st)
+             : launch_down(dnb, w, sh, wk, pd.out ? &pd : nullptr, st)) != hipSuccess)
     return LAT_MOE_ELAUNCH;
   if (mark(3) != hipSuccess) return LAT_MOE_ELAUNCH;
   if (launch_combine(idx, sh, wk, y, st) != hipSuccess) return LAT_MOE_ELAUNCH;

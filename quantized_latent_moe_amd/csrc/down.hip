@@ -33,27 +33,6 @@ constexpr int kRawHalfPer = kRawHalf / kThreads;               // 9
 static_assert(kRawHalf % kThreads == 0, "staging split");
 static_assert(kNT * 16 == 2 * kThreads && kNT * 8 == kThreads && kLT * 8 == kThreads, "staging split");
 
-// The IQ4_NL non-linear table (ggml), packed as four little-endian words.
-constexpr int kIq4Table[16] = {-127, -104, -83, -65, -49, -35, -22, -10, 1, 13, 25, 38, 53, 69, 89, 113};
-constexpr uint32_t tab_word(int w) {
-  return (uint32_t)(kIq4Table[4 * w] & 0xff) | ((uint32_t)(kIq4Table[4 * w + 1] & 0xff) << 8) |
-         ((uint32_t)(kIq4Table[4 * w + 2] & 0xff) << 16) | ((uint32_t)(kIq4Table[4 * w + 3] & 0xff) << 24);
-}
-constexpr uint32_t kTab0 = tab_word(0), kTab1 = tab_word(1), kTab2 = tab_word(2), kTab3 = tab_word(3);
-static_assert(kTab0 == 0xBFAD9881u && kTab3 == 0x71594535u, "IQ4_NL table packing");
-
-// 4 nibble indices (one per byte) -> 4 table bytes.
-__device__ __forceinline__ uint32_t iq4_lookup(uint32_t nib) {
-  const uint32_t sel = nib & 0x07070707u;
-  const uint32_t lo = __builtin_amdgcn_perm(kTab1, kTab0, sel);
-  const uint32_t hi = __builtin_amdgcn_perm(kTab3, kTab2, sel);
-  const uint32_t b3 = (nib >> 3) & 0x01010101u;
-  uint32_t b3s = b3 << 8;
-  asm("" : "+v"(b3s));  // keeps b3 * 255 as a shift and a subtract (a multiply is quarter rate)
-  const uint32_t m = b3s - b3;  // 0xff in every byte whose index has bit 3 set
-  return (lo & ~m) | (hi & m);
-}
-
 template <bool PROBE, bool ALIGNED16>
 __global__ __launch_bounds__(kThreads) void k_down_generic(const uint8_t* __restrict__ dn, const float* __restrict__ router_w,
                                                    const int32_t* __restrict__ perm,

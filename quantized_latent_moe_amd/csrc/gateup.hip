@@ -212,9 +212,7 @@ __global__ __launch_bounds__(kThreads) void k_gateup(const int8_t* __restrict__ 
         const int sl = s & 7;
         const int lo = (int)((scb[sl >> 2] >> (8 * (sl & 3) + (s < 8 ? 0 : 4))) & 15u);
         const int hi = (int)((scb[2] >> (8 * (s & 3) + 2 * (s >> 2))) & 3u);
-        const int sg = (lo | (hi << 4)) - 32;
-        tlo[t] = pack4(4 * sg, 3 * sg, 2 * sg, sg);
-        thi[t] = pack4(0, -sg, -2 * sg, -3 * sg);
+        q3_tables((lo | (hi << 4)) - 32, tlo[t], thi[t]);
       }
       const int qshift = 2 * uj;       // low two bits of element 128un + 32uj + l: bit 2uj of qs[l]
       const int hs = 4 * un + uj - 2;  // its high bit (bit 4un + uj of hmask[l]) moves to bit 2

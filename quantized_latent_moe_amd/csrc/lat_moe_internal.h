@@ -86,6 +86,43 @@ __device__ __forceinline__ float fp32_barrier(float v) {
   return v;
 }
 
+// Operand table of a Q3_K sub-block with signed scale sg = sc6 - 32: byte c
+// of (thi:tlo) is (4 - c) * sg for the 3-bit code c, so v_perm_b32(thi, tlo,
+// codes) expands four codes at once.  Products are formed two at a time in
+// 16-bit halves (their low bytes are the int8 values) and gathered by v_perm.
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void q3_tables(int sg, uint32_t& tlo, uint32_t& thi) {
+  const s16x2 v = {(short)sg, (short)sg};
+  const s16x2 a = v * (s16x2){4, 3};
+  const s16x2 b = v * (s16x2){2, 1};
+  const s16x2 c = v * (s16x2){-1, -2};
+  const s16x2 d = v * (s16x2){-3, 0};
+  tlo = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, b), __builtin_bit_cast(uint32_t, a), 0x06040200u);
+  thi = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, d), __builtin_bit_cast(uint32_t, c), 0x0402000Cu);
+}
+
+// IQ4_NL: the 16-entry non-linear table (ggml) packed as four little-endian
+// words, and a lookup of 4 indices (one per byte, 0..15) -> 4 table bytes with
+// two v_perm_b32 and a byte select.
+constexpr int kIq4Table[16] = {-127, -104, -83, -65, -49, -35, -22, -10, 1, 13, 25, 38, 53, 69, 89, 113};
+constexpr uint32_t iq4_tab_word(int w) {
+  return (uint32_t)(kIq4Table[4 * w] & 0xff) | ((uint32_t)(kIq4Table[4 * w + 1] & 0xff) << 8) |
+         ((uint32_t)(kIq4Table[4 * w + 2] & 0xff) << 16) | ((uint32_t)(kIq4Table[4 * w + 3] & 0xff) << 24);
+}
+constexpr uint32_t kIq4Tab0 = iq4_tab_word(0), kIq4Tab1 = iq4_tab_word(1), kIq4Tab2 = iq4_tab_word(2),
+                   kIq4Tab3 = iq4_tab_word(3);
+static_assert(kIq4Tab0 == 0xBFAD9881u && kIq4Tab3 == 0x71594535u, "IQ4_NL table packing");
+__device__ __forceinline__ uint32_t iq4_lookup(uint32_t nib) {
+  const uint32_t sel = nib & 0x07070707u;
+  const uint32_t lo = __builtin_amdgcn_perm(kIq4Tab1, kIq4Tab0, sel);
+  const uint32_t hi = __builtin_amdgcn_perm(kIq4Tab3, kIq4Tab2, sel);
+  const uint32_t b3 = (nib >> 3) & 0x01010101u;
+  uint32_t b3s = b3 << 8;
+  asm("" : "+v"(b3s));  // keeps b3 * 255 as a shift and a subtract (a multiply is quarter rate)
+  const uint32_t m = b3s - b3;  // 0xff in every byte whose index has bit 3 set
+  return (lo & ~m) | (hi & m);
+}
+
 // Raw buffer loads (gfx9 buffer resource, stride 0).  A load whose 32-bit
 // offset is at or past num_records returns zero without touching memory, so
 // padding lanes load from kOutOfRange instead of branching around the load.
@@ -111,6 +148,14 @@ hipError_t launch_route(const int32_t* idx, const uint8_t* x, const Shapes& s, c
 hipError_t launch_gateup(const Shapes& s, const Work& w, const uint8_t* gu, const ProbeRows* probe, hipStream_t st);
 hipError_t launch_down(const uint8_t* dn, const float* router_w, const Shapes& s, const Work& w,
                        const ProbeRows* probe, hipStream_t st);
+// Batches of at most kSmallMaxPairs pairs (L <= 1024, F <= 2048) take the
+// GEMV-shaped gate/up and down kernels.
+constexpr int kSmallMaxPairs = 64;
+bool small_path(const Shapes& s);
+hipError_t launch_gateup_small(const Shapes& s, const Work& w, const uint8_t* gu, const ProbeRows* probe,
+                               hipStream_t st);
+hipError_t launch_down_small(const uint8_t* dn, const float* router_w, const Shapes& s, const Work& w,
+                             const ProbeRows* probe, hipStream_t st);
 hipError_t launch_combine(const int32_t* idx, const Shapes& s, const Work& w, float* y, hipStream_t st);
 hipError_t launch_quantize_q8_1(const float* x, int64_t rows, int cols, uint8_t* out, hipStream_t st);
 hipError_t launch_export_h(const Shapes& s, const Work& w, uint8_t* h_out, hipStream_t st);

@@ -86,6 +86,9 @@ SMALL = [
     Workload("ragged", T=200, L=512, F=288, E=6, k=3, zipf_s=1.1, seed=3),
     Workload("ragged_masked", T=150, L=768, F=160, E=9, k=4, zipf_s=1.1, n_masked=2, seed=4),
     WORKLOADS["decode"],
+    # batches of at most 64 pairs take the GEMV-shaped kernels
+    Workload("few_tokens", T=6, L=768, F=160, E=5, k=4, zipf_s=1.1, seed=9),
+    Workload("few_tokens_crowded", T=16, L=256, F=96, E=2, k=2, seed=10),
 ]
 
 
