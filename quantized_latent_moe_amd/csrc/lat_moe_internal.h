@@ -102,8 +102,9 @@ __device__ __forceinline__ void q3_tables(int sg, uint32_t& tlo, uint32_t& thi) 
 }
 
 // IQ4_NL: the 16-entry non-linear table (ggml) packed as four little-endian
-// words, and a lookup of 4 indices (one per byte, 0..15) -> 4 table bytes with
-// two v_perm_b32 and a byte select.
+// words, and a lookup of 4 indices (one per byte, 0..15) -> 4 table bytes:
+// two v_perm_b32 look up the low 3 bits in both 8-entry halves, a third picks
+// byte b of the low half or byte b of the high half by bit 3 of index b.
 constexpr int kIq4Table[16] = {-127, -104, -83, -65, -49, -35, -22, -10, 1, 13, 25, 38, 53, 69, 89, 113};
 constexpr uint32_t iq4_tab_word(int w) {
   return (uint32_t)(kIq4Table[4 * w] & 0xff) | ((uint32_t)(kIq4Table[4 * w + 1] & 0xff) << 8) |
@@ -116,11 +117,9 @@ __device__ __forceinline__ uint32_t iq4_lookup(uint32_t nib) {
   const uint32_t sel = nib & 0x07070707u;
   const uint32_t lo = __builtin_amdgcn_perm(kIq4Tab1, kIq4Tab0, sel);
   const uint32_t hi = __builtin_amdgcn_perm(kIq4Tab3, kIq4Tab2, sel);
-  const uint32_t b3 = (nib >> 3) & 0x01010101u;
-  uint32_t b3s = b3 << 8;
-  asm("" : "+v"(b3s));  // keeps b3 * 255 as a shift and a subtract (a multiply is quarter rate)
-  const uint32_t m = b3s - b3;  // 0xff in every byte whose index has bit 3 set
-  return (lo & ~m) | (hi & m);
+  // selector byte b: b (from lo) or 4 + b (from hi); bit 3 of the index moves to bit 2
+  const uint32_t pick = ((nib >> 1) & 0x04040404u) | 0x03020100u;
+  return __builtin_amdgcn_perm(hi, lo, pick);
 }
 
 // Raw buffer loads (gfx9 buffer resource, stride 0).  A load whose 32-bit

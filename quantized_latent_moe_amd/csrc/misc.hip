@@ -4,6 +4,8 @@
 namespace latmoe {
 namespace {
 
+constexpr int kCombineUnroll = 8;  // slots per token whose loads are all issued up front
+
 // y[t][l] = sum_{j=0..k-1, id valid} slot[t*k + j][l], slots taken in order.
 // Each slot already holds router_w[t][j] * O (down epilogue).
 __global__ __launch_bounds__(256) void k_combine(const int32_t* __restrict__ idx, const float* __restrict__ slots,
@@ -14,14 +16,34 @@ __global__ __launch_bounds__(256) void k_combine(const int32_t* __restrict__ idx
   const int64_t t = q / l4;
   const int l = (int)(q - t * l4) * 4;
   float4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < k; ++j) {
-    const int e = idx[t * k + j];
-    if ((unsigned)e >= (unsigned)E) continue;
-    const float4 v = *reinterpret_cast<const float4*>(slots + (t * k + j) * L + l);
-    acc.x += v.x;
-    acc.y += v.y;
-    acc.z += v.z;
-    acc.w += v.w;
+  if (k <= kCombineUnroll) {
+    // issue every slot load before summing (in slot order, as below)
+    float4 v[kCombineUnroll];
+#pragma unroll
+    for (int j = 0; j < kCombineUnroll; ++j) {
+      const int e = j < k ? idx[t * k + j] : -1;
+      v[j] = (unsigned)e < (unsigned)E ? *reinterpret_cast<const float4*>(slots + (t * k + j) * L + l)
+                                       : float4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int j = 0; j < kCombineUnroll; ++j) {
+      if (j < k) {
+        acc.x += v[j].x;
+        acc.y += v[j].y;
+        acc.z += v[j].z;
+        acc.w += v[j].w;
+      }
+    }
+  } else {
+    for (int j = 0; j < k; ++j) {
+      const int e = idx[t * k + j];
+      if ((unsigned)e >= (unsigned)E) continue;
+      const float4 v = *reinterpret_cast<const float4*>(slots + (t * k + j) * L + l);
+      acc.x += v.x;
+      acc.y += v.y;
+      acc.z += v.z;
+      acc.w += v.w;
+    }
   }
   *reinterpret_cast<float4*>(y + t * L + l) = acc;
 }
