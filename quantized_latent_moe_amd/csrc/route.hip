@@ -20,6 +20,7 @@ namespace latmoe {
 namespace {
 
 constexpr int kSmallPairs = 4096;
+constexpr int kScanStage = 16384;  // chunk-histogram entries the scan stages in LDS
 constexpr int kSplitPerBlock = 1024;  // q8_1 blocks split per extra workgroup
 
 // q8_1 block b -> 32 codes at xc + 32b and the fp32 scale xd[b].
@@ -202,14 +203,33 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ chunk
   __shared__ int32_t first[1024];
   __shared__ int scratch[16];
   __shared__ int bad;
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    int run = 0;
-    for (int c = 0; c < nchunk; ++c) {
-      const int v = chunk_hist[(int64_t)c * E + e];
-      chunk_hist[(int64_t)c * E + e] = run;
-      run += v;
+  __shared__ int32_t stage[kScanStage];  // the chunk histograms, when they fit
+  const int64_t nh = (int64_t)nchunk * E;
+  if (nh <= kScanStage) {
+    // coalesced copy to LDS, per-expert running sums there, prefixes back out
+    for (int i = threadIdx.x; i < nh; i += blockDim.x) stage[i] = chunk_hist[i];
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+      int run = 0;
+      for (int c = 0; c < nchunk; ++c) {
+        const int v = stage[c * E + e];
+        stage[c * E + e] = run;
+        run += v;
+      }
+      cnt[e] = run;
     }
-    cnt[e] = run;
+    __syncthreads();
+    for (int i = threadIdx.x; i < nh; i += blockDim.x) chunk_hist[i] = stage[i];
+  } else {
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+      int run = 0;
+      for (int c = 0; c < nchunk; ++c) {
+        const int v = chunk_hist[(int64_t)c * E + e];
+        chunk_hist[(int64_t)c * E + e] = run;
+        run += v;
+      }
+      cnt[e] = run;
+    }
   }
   int b = 0;
   for (int c = threadIdx.x; c < nchunk; c += blockDim.x) b += chunk_bad[c];
