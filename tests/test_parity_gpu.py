@@ -89,6 +89,10 @@ SMALL = [
     # batches of at most 64 pairs take the GEMV-shaped kernels
     Workload("few_tokens", T=6, L=768, F=160, E=5, k=4, zipf_s=1.1, seed=9),
     Workload("few_tokens_crowded", T=16, L=256, F=96, E=2, k=2, seed=10),
+    # more than 8 experts per token (combine's general loop)
+    Workload("wide_k", T=48, L=512, F=256, E=12, k=10, zipf_s=1.1, seed=11),
+    # more than 512 experts (the chunked route passes at a small batch)
+    Workload("many_experts", T=64, L=256, F=128, E=600, k=4, seed=12),
 ]
 
 
