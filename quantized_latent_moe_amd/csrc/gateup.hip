@@ -29,8 +29,9 @@
 //     2-byte aligned; 8 lanes read 16 contiguous bytes of a row), its tokens'
 //     int8 codes (16-byte loads) and fp32 block scales; writes them to LDS;
 //     and unpacks its rows from LDS: per (row, half, j) 32 codes become
-//     (4 - c) * sigma with one v_perm_b32 per 4 values against an 8-entry
-//     table built from the sub-block scale.  Only the producer itself reads
+//     (4 - c) * sigma with one v_perm_b32 per 4 values against the 8-entry
+//     table of the sub-block scale (one 8-byte LDS read from the 64 tables
+//     the workgroup builds at its start).  Only the producer itself reads
 //     its raw rows, so no barrier separates its stores from its unpack.
 // Step g: producers build operands of step g+1 in the other LDS buffer and
 // issue the global loads of step g+2; consumers run the MFMAs of step g; one
@@ -38,7 +39,8 @@
 // Epilogue (after an item's last step, consumers): H = G * sigmoid(G) * U,
 // then per 32 features of a token (16 in this lane, 16 in lane ^ 32) the q8_1
 // rule: amax, d = amax/127, id = 1/d, q = round-half-away(H * id) with IEEE
-// divisions; codes and fp16 (d, s) go to the workspace in sorted order.
+// divisions (the codes' sum by v_dot4 on the packed codes); codes and fp16
+// (d, s) go to the workspace in sorted order.
 #include "lat_moe_internal.h"
 
 namespace latmoe {
@@ -51,13 +53,12 @@ constexpr int kRows = 2 * kFT;       // weight rows per work item (gate + up)
 constexpr int kNT = kTileN;          // tokens per work item
 constexpr int kRawStride = 112;      // staged Q3_K block, bytes (110 rounded up to 16)
 constexpr int kOpStride = 256 + 16;  // int8 operand row in LDS (bytes); 16 mod 256: conflict-free b128
+// The pad bytes of operand rows are never read as operands.  Those of rows
+// 0..63 of As[0] hold the Q3_K operand table of each 6-bit scale sc (byte c =
+// (4 - c)(sc - 32), c = 0..7), written once per workgroup.
+constexpr int kTabOff = 256;
 static_assert(kRows == 32 * kProducers && kNT == 32 * kProducers, "a producer owns 32 rows and 32 tokens");
 static_assert(kNT == 4 * 32 && kFT == 2 * 32, "8 consumers = 2 feature halves x 4 token slices");
-
-__device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
-  return (uint32_t)(a & 0xff) | ((uint32_t)(b & 0xff) << 8) | ((uint32_t)(c & 0xff) << 16) |
-         ((uint32_t)(d & 0xff) << 24);
-}
 
 struct Item {
   int e, pos0, cnt, f0;
@@ -212,7 +213,9 @@ __global__ __launch_bounds__(kThreads) void k_gateup(const int8_t* __restrict__ 
         const int sl = s & 7;
         const int lo = (int)((scb[sl >> 2] >> (8 * (sl & 3) + (s < 8 ? 0 : 4))) & 15u);
         const int hi = (int)((scb[2] >> (8 * (s & 3) + 2 * (s >> 2))) & 3u);
-        q3_tables((lo | (hi << 4)) - 32, tlo[t], thi[t]);
+        const uint2 tb = *reinterpret_cast<const uint2*>(As[0] + (lo | (hi << 4)) * kOpStride + kTabOff);
+        tlo[t] = tb.x;
+        thi[t] = tb.y;
       }
       const int qshift = 2 * uj;       // low two bits of element 128un + 32uj + l: bit 2uj of qs[l]
       const int hs = 4 * un + uj - 2;  // its high bit (bit 4un + uj of hmask[l]) moves to bit 2
@@ -320,20 +323,20 @@ __global__ __launch_bounds__(kThreads) void k_gateup(const int8_t* __restrict__ 
     amax = fmaxf(amax, __shfl_xor(amax, 32));
     const float d = amax / 127.0f;
     const float id = d != 0.0f ? 1.0f / d : 0.0f;
-    int q[16];
+    uint32_t pk[4];
     int sum = 0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      q[i] = (int)__builtin_roundf(h[i] * id);
-      sum += q[i];
+    for (int qq = 0; qq < 4; ++qq) {
+      pk[qq] = pack_codes(round_half_away(h[4 * qq] * id), round_half_away(h[4 * qq + 1] * id),
+                          round_half_away(h[4 * qq + 2] * id), round_half_away(h[4 * qq + 3] * id));
+      sum = __builtin_amdgcn_sdot4((int)pk[qq], 0x01010101, sum, false);  // sum of the four codes
     }
     sum += __shfl_xor(sum, 32);
     if (n < cur.cnt && fb < F) {
       const int64_t pos = cur.pos0 + n;
       int8_t* dst = h_codes + pos * F + fb + 4 * khalf;
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq)
-        *reinterpret_cast<uint32_t*>(dst + 8 * qq) = pack4(q[4 * qq], q[4 * qq + 1], q[4 * qq + 2], q[4 * qq + 3]);
+      for (int qq = 0; qq < 4; ++qq) *reinterpret_cast<uint32_t*>(dst + 8 * qq) = pk[qq];
       if (khalf == 0)
         h_ds[pos * (F / 32) + fb / 32] =
             float_to_half_bits(d) | (float_to_half_bits(fp32_barrier(d * (float)sum)) << 16);
@@ -343,7 +346,13 @@ __global__ __launch_bounds__(kThreads) void k_gateup(const int8_t* __restrict__ 
   // The two roles run separate loops (so their registers are not live at the
   // same time) with the same barriers: two in the prologue, one per step.
   if (producer) {
-    // prologue: operands of step 0 in buffer 0, loads of step 1 in flight
+    // prologue: the scale tables, operands of step 0 in buffer 0, loads of
+    // step 1 in flight
+    if (ptid < 64) {
+      uint32_t tlo, thi;
+      q3_tables(ptid - 32, tlo, thi);
+      *reinterpret_cast<uint2*>(As[0] + ptid * kOpStride + kTabOff) = uint2{tlo, thi};
+    }
     fetch_ids(0);
     __syncthreads();
     load_next();

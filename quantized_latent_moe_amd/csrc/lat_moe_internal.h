@@ -86,6 +86,22 @@ __device__ __forceinline__ float fp32_barrier(float v) {
   return v;
 }
 
+// The q8_1 rule's round half away from zero, to int: adding the largest float
+// below one half with v's sign and truncating (v_cvt_i32_f32) gives roundf's
+// integer for every float |v| < 2^31 (an exhaustive host check over all fp32
+// values confirms it), in three VALU operations.  Callers keep FMA
+// contraction off so the add is not fused with the product that made v.
+__device__ __forceinline__ int round_half_away(float v) {
+  return (int)(v + __builtin_copysignf(0x1.fffffep-2f, v));
+}
+
+// Low bytes of four int32 codes as one word, byte i = code i (three v_perm_b32).
+__device__ __forceinline__ uint32_t pack_codes(int a, int b, int c, int d) {
+  const uint32_t lo = __builtin_amdgcn_perm((uint32_t)b, (uint32_t)a, 0x0C0C0400u);
+  const uint32_t hi = __builtin_amdgcn_perm((uint32_t)d, (uint32_t)c, 0x0C0C0400u);
+  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+}
+
 // Operand table of a Q3_K sub-block with signed scale sg = sc6 - 32: byte c
 // of (thi:tlo) is (4 - c) * sg for the 3-bit code c, so v_perm_b32(thi, tlo,
 // codes) expands four codes at once.  Products are formed two at a time in

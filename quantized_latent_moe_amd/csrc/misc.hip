@@ -76,13 +76,9 @@ __global__ __launch_bounds__(256) void k_quantize_q8_1(const float* __restrict__
   int sum = 0;
 #pragma unroll
   for (int w = 0; w < 8; ++w) {
-    uint32_t word = 0;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int q = (int)__builtin_roundf(v[4 * w + t] * id);
-      sum += q;
-      word |= (uint32_t)(q & 0xff) << (8 * t);
-    }
+    const uint32_t word = pack_codes(round_half_away(v[4 * w] * id), round_half_away(v[4 * w + 1] * id),
+                                     round_half_away(v[4 * w + 2] * id), round_half_away(v[4 * w + 3] * id));
+    sum = __builtin_amdgcn_sdot4((int)word, 0x01010101, sum, false);
     dst[1 + w] = word;
   }
   dst[0] = float_to_half_bits(d) | (float_to_half_bits(fp32_barrier(d * (float)sum)) << 16);

@@ -209,7 +209,7 @@ __global__ __launch_bounds__(kSmallThreads) void k_gateup_small(
       for (int o = 16; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 32));
       const float d = amax / 127.0f;
       const float id = d != 0.0f ? 1.0f / d : 0.0f;
-      const int qv = (int)__builtin_roundf(h * id);
+      const int qv = round_half_away(h * id);
       int sum = qv;
 #pragma unroll
       for (int o = 16; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 32);

@@ -202,3 +202,26 @@ def test_empty_batch_is_noop():
     lm.expert_forward(dummy, dummy, dummy, dummy, dummy, s, y, dummy)
     torch.cuda.synchronize()
     assert (y == 3.0).all()
+
+
+@pytest.mark.parametrize("wl", [SMALL[1], SMALL[4]], ids=lambda w: w.name)
+def test_workspace_contents_do_not_matter(wl):
+    """The workspace needs no initialisation: a workspace filled with garbage,
+    and one left over from a call with other shapes, give the same y bit for
+    bit as a fresh one."""
+    say(f"poisoned workspace {wl}")
+    I, xq = _case(wl)
+    g = Gpu(I, xq)
+    g.ws.zero_()
+    clean = g.forward()
+    for fill in (0xFF, 0x7F, 0x80):
+        g.ws.fill_(fill)
+        assert np.array_equal(g.forward(), clean), f"workspace filled with {fill:#x}"
+    # a larger call through the same workspace first, then this one again
+    big = Workload("big_first", T=300, L=wl.L, F=wl.F, E=wl.E + 3, k=wl.k, seed=wl.seed + 100)
+    Ib, xqb = _case(big)
+    gb = Gpu(Ib, xqb)
+    g.ws = torch.empty(max(g.ws.numel(), gb.ws.numel()), dtype=torch.uint8, device="cuda")
+    gb.ws = g.ws
+    gb.forward()
+    assert np.array_equal(g.forward(), clean), "after a larger call through the same workspace"
