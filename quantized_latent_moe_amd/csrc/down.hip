@@ -16,6 +16,8 @@
 // through the 16-entry table with two v_perm_b32 lookups and a byte select.
 // Epilogue: O * router_w[p] is written to the pair's slot row (pair order), so
 // the combine sums each token's k slots in a fixed order.
+#include <type_traits>
+
 #include "lat_moe_internal.h"
 
 namespace latmoe {
@@ -242,6 +244,8 @@ __global__ __launch_bounds__(kThreads) void k_down_generic(const uint8_t* __rest
 //     padding), writes them to LDS, and expands its rows' IQ4_NL blocks: two
 //     lanes per row, each reading 72 bytes (4 blocks) and turning 4 indices
 //     into 4 table bytes with two v_perm_b32 and a select.
+//     The next step's loads are issued between the LDS writes and the
+//     expansion, so their latency overlaps the expansion.
 // Operand rows are 256 bytes with their 16-byte chunks XOR-swizzled by the
 // row's low 4 bits (conflict-free 16-byte reads without padding); operands
 // and scales are double-buffered, one barrier per step.
@@ -358,7 +362,10 @@ __global__ __launch_bounds__(kWsThreads) void k_down(const uint8_t* __restrict__
         need_setup = ++lj < my_items;
       }
     };
-    auto build = [&](int b) {
+    // S: registers -> LDS buffer b.  The registers are free again after it,
+    // so the next step's loads are issued before the expansion (U) and their
+    // latency overlaps it.
+    auto stage = [&](int b) {
       uint4* raw16 = reinterpret_cast<uint4*>(raw + 32 * p * kWsStep);
 #pragma unroll
       for (int m = 0; m < 5; ++m)
@@ -370,6 +377,8 @@ __global__ __launch_bounds__(kWsThreads) void k_down(const uint8_t* __restrict__
       }
 #pragma unroll
       for (int c = 0; c < 4; ++c) dhs[b][32 * p + 8 * c + (lane >> 3)][lane & 7] = half_bits_to_float(rd[c] & 0xffffu);
+    };
+    auto unpack = [&](int b) {
       // expand: row 32p + (lane & 31), blocks 4*(lane >> 5) .. +3 from the 72
       // bytes at 72*(lane >> 5) of the row's chunk
       const int r = 32 * p + (lane & 31), hb = lane >> 5;
@@ -404,18 +413,24 @@ __global__ __launch_bounds__(kWsThreads) void k_down(const uint8_t* __restrict__
     };
 
     load_next();
-    build(0);
-    __syncthreads();
+    stage(0);
     if (n_steps > 1) load_next();
+    unpack(0);
+    __syncthreads();
     for (int g = 0; g < n_steps; ++g) {
-      if (g + 1 < n_steps) build((g & 1) ^ 1);
+      if (g + 1 < n_steps) stage((g & 1) ^ 1);
       if (g + 2 < n_steps) load_next();
+      if (g + 1 < n_steps) unpack((g & 1) ^ 1);
       __syncthreads();
     }
     return;
   }
 
   // =============================== consumer ===============================
+  // Wide items (more than 64 tokens): wave (rs, th) owns rows 32 rs .. +31 and
+  // tokens 64 th .. +63 as two 32-token halves.  Narrow items (at most 64
+  // tokens): it owns tokens 32 th .. +31 only, so all 8 waves (2 per SIMD)
+  // share the work; one wave per SIMD issues VALU at well under full rate.
   const int rs = wave & 3, th = wave >> 2;
   const int col = lane & 31, khalf = lane >> 5;
   const int xo = (khalf ^ (col & 15)) << 4;  // chunk (2kb + khalf) of a row with these low bits: 32kb ^ xo
@@ -427,90 +442,115 @@ __global__ __launch_bounds__(kWsThreads) void k_down(const uint8_t* __restrict__
   DItem cur = ditem((int)blockIdx.x, nlt, tiles, offsets);
   int pair0 = -1, pair1 = -1;
   float w0 = 0.f, w1 = 0.f;
-  __syncthreads();
-  for (int g = 0; g < n_steps; ++g) {
-    const int b = g & 1;
-    const int n0 = 64 * th + col, n1 = n0 + 32;
-    if (csb == 0) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc0[i] = acc1[i] = 0.f;
-      pair0 = n0 < cur.cnt ? perm[cur.pos0 + n0] : -1;
-      pair1 = n1 < cur.cnt ? perm[cur.pos0 + n1] : -1;
-      w0 = pair0 >= 0 ? router_w[pair0] : 0.f;
-      w1 = pair1 >= 0 ? router_w[pair1] : 0.f;
+  // one K step over both halves (TWO) or the first only
+  auto mma = [&](auto two_tag, auto grp_tag, int b) {
+    constexpr bool TWO = decltype(two_tag)::value;
+    constexpr int GRP = decltype(grp_tag)::value;
+    const int n0 = (TWO ? 64 : 32) * th + col, n1 = n0 + 32;
+    const int8_t* ap = As[b] + (32 * rs + col) * 256;
+    const int8_t* bp0 = Bs[b] + n0 * 256;
+    const int8_t* bp1 = Bs[b] + (TWO ? n1 : n0) * 256;
+    const float4 h00 = *reinterpret_cast<const float4*>(&dhs[b][n0][0]);
+    const float4 h01 = *reinterpret_cast<const float4*>(&dhs[b][n0][4]);
+    float4 h10 = h00, h11 = h01;
+    if (TWO) {
+      h10 = *reinterpret_cast<const float4*>(&dhs[b][n1][0]);
+      h11 = *reinterpret_cast<const float4*>(&dhs[b][n1][4]);
     }
-    if (64 * th < cur.cnt) {
-      const int8_t* ap = As[b] + (32 * rs + col) * 256;
-      const int8_t* bp0 = Bs[b] + n0 * 256;
-      const int8_t* bp1 = Bs[b] + n1 * 256;
-      const float4 h00 = *reinterpret_cast<const float4*>(&dhs[b][n0][0]);
-      const float4 h01 = *reinterpret_cast<const float4*>(&dhs[b][n0][4]);
-      const float4 h10 = *reinterpret_cast<const float4*>(&dhs[b][n1][0]);
-      const float4 h11 = *reinterpret_cast<const float4*>(&dhs[b][n1][4]);
-      const float dh0[8] = {h00.x, h00.y, h00.z, h00.w, h01.x, h01.y, h01.z, h01.w};
-      const float dh1[8] = {h10.x, h10.y, h10.z, h10.w, h11.x, h11.y, h11.z, h11.w};
+    const float dh0[8] = {h00.x, h00.y, h00.z, h00.w, h01.x, h01.y, h01.z, h01.w};
+    const float dh1[8] = {h10.x, h10.y, h10.z, h10.w, h11.x, h11.y, h11.z, h11.w};
 #pragma unroll
-      for (int kb = 0; kb < 8; ++kb) {
-        const int off = (32 * kb) ^ xo;
-        const v4i va = *reinterpret_cast<const v4i*>(ap + off);
-        const v4i vb0 = *reinterpret_cast<const v4i*>(bp0 + off);
+    for (int kb = 0; kb < 8; ++kb) {
+      // The two consumer waves of a SIMD (th = 0, 1) take turns at the higher
+      // priority, two blocks each, so both finish the step together.
+      if (kb % 2 == 0) {
+        if ((GRP ^ (kb / 2)) & 1) __builtin_amdgcn_s_setprio(1); else __builtin_amdgcn_s_setprio(0);
+      }
+      const int off = (32 * kb) ^ xo;
+      const v4i va = *reinterpret_cast<const v4i*>(ap + off);
+      const v4i vb0 = *reinterpret_cast<const v4i*>(bp0 + off);
+      const v16i j0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(va, vb0, magic, 0, 0, 0);
+      v16i j1 = magic;
+      if (TWO) {
         const v4i vb1 = *reinterpret_cast<const v4i*>(bp1 + off);
-        const v16i j0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(va, vb0, magic, 0, 0, 0);
-        const v16i j1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(va, vb1, magic, 0, 0, 0);
-        // d_dn of this lane's 16 rows for block kb (fp16, contiguous)
-        const uint4 dq0 = *reinterpret_cast<const uint4*>(&dds[b][kb][32 * rs + 16 * khalf]);
-        const uint4 dq1 = *reinterpret_cast<const uint4*>(&dds[b][kb][32 * rs + 16 * khalf + 8]);
-        const uint32_t dq[8] = {dq0.x, dq0.y, dq0.z, dq0.w, dq1.x, dq1.y, dq1.z, dq1.w};
-        const float c0 = -kMagic * dh0[kb], c1 = -kMagic * dh1[kb];  // exact
+        j1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(va, vb1, magic, 0, 0, 0);
+      }
+      // d_dn of this lane's 16 rows for block kb (fp16, contiguous)
+      const uint4 dq0 = *reinterpret_cast<const uint4*>(&dds[b][kb][32 * rs + 16 * khalf]);
+      const uint4 dq1 = *reinterpret_cast<const uint4*>(&dds[b][kb][32 * rs + 16 * khalf + 8]);
+      const uint32_t dq[8] = {dq0.x, dq0.y, dq0.z, dq0.w, dq1.x, dq1.y, dq1.z, dq1.w};
+      const float c0 = -kMagic * dh0[kb], c1 = -kMagic * dh1[kb];  // exact
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float dd = half_bits_to_float((i & 1) ? (dq[i >> 1] >> 16) : (dq[i >> 1] & 0xffffu));
-          acc0[i] = __builtin_fmaf(dd, __builtin_fmaf(dh0[kb], as_float(j0[i]), c0), acc0[i]);
-          acc1[i] = __builtin_fmaf(dd, __builtin_fmaf(dh1[kb], as_float(j1[i]), c1), acc1[i]);
-        }
-        if (PROBE) {
+      for (int i = 0; i < 16; ++i) {
+        const float dd = half_bits_to_float((i & 1) ? (dq[i >> 1] >> 16) : (dq[i >> 1] & 0xffffu));
+        acc0[i] = __builtin_fmaf(dd, __builtin_fmaf(dh0[kb], as_float(j0[i]), c0), acc0[i]);
+        if (TWO) acc1[i] = __builtin_fmaf(dd, __builtin_fmaf(dh1[kb], as_float(j1[i]), c1), acc1[i]);
+      }
+      if (PROBE) {
 #pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            const int pr = t ? pair1 : pair0;
-            if (pr >= 0) {
+        for (int t = 0; t < (TWO ? 2 : 1); ++t) {
+          const int pr = t ? pair1 : pair0;
+          if (pr >= 0) {
 #pragma unroll
-              for (int i = 0; i < 16; ++i) {
-                const int l = cur.l0 + 32 * rs + 8 * (i >> 2) + 4 * khalf + (i & 3);
-                const int rr = l - probe.row0;
-                if (rr >= 0 && rr < probe.rows)
-                  probe.out[((int64_t)pr * probe.rows + rr) * nfb + csb * 8 + kb] =
-                      (t ? j1[i] : j0[i]) - kMagicBits;
-              }
+            for (int i = 0; i < 16; ++i) {
+              const int l = cur.l0 + 32 * rs + 8 * (i >> 2) + 4 * khalf + (i & 3);
+              const int rr = l - probe.row0;
+              if (rr >= 0 && rr < probe.rows)
+                probe.out[((int64_t)pr * probe.rows + rr) * nfb + csb * 8 + kb] = (t ? j1[i] : j0[i]) - kMagicBits;
             }
           }
         }
       }
     }
-    if (++csb == nsb) {
-      // ---- weighted output rows into the pairs' slots
+  };
+  // one copy of the loop per token group th (the priority pattern is an immediate)
+  auto consumer_loop = [&](auto grp_tag) {
+    __syncthreads();
+    for (int g = 0; g < n_steps; ++g) {
+      const int b = g & 1;
+      const bool wide = cur.cnt > 64;
+      if (csb == 0) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int pr = t ? pair1 : pair0;
-        const float wgt = t ? w1 : w0;
-        if (pr >= 0) {
-          float* dst = slots + (int64_t)pr * L + cur.l0 + 32 * rs + 4 * khalf;
+        for (int i = 0; i < 16; ++i) acc0[i] = acc1[i] = 0.f;
+        const int n0 = (wide ? 64 : 32) * th + col, n1 = n0 + 32;
+        pair0 = n0 < cur.cnt ? perm[cur.pos0 + n0] : -1;
+        pair1 = wide && n1 < cur.cnt ? perm[cur.pos0 + n1] : -1;
+        w0 = pair0 >= 0 ? router_w[pair0] : 0.f;
+        w1 = pair1 >= 0 ? router_w[pair1] : 0.f;
+      }
+      if (wide) {
+        if (64 * th < cur.cnt) mma(std::true_type{}, grp_tag, b);
+      } else if (32 * th < cur.cnt) {
+        mma(std::false_type{}, grp_tag, b);
+      }
+      if (++csb == nsb) {
+        // ---- weighted output rows into the pairs' slots
 #pragma unroll
-          for (int qq = 0; qq < 4; ++qq) {
-            const float* a = t ? acc1 : acc0;
-            float4 v;
-            v.x = a[4 * qq + 0] * wgt;
-            v.y = a[4 * qq + 1] * wgt;
-            v.z = a[4 * qq + 2] * wgt;
-            v.w = a[4 * qq + 3] * wgt;
-            *reinterpret_cast<float4*>(dst + 8 * qq) = v;
+        for (int t = 0; t < 2; ++t) {
+          const int pr = t ? pair1 : pair0;
+          const float wgt = t ? w1 : w0;
+          if (pr >= 0) {
+            float* dst = slots + (int64_t)pr * L + cur.l0 + 32 * rs + 4 * khalf;
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+              const float* a = t ? acc1 : acc0;
+              float4 v;
+              v.x = a[4 * qq + 0] * wgt;
+              v.y = a[4 * qq + 1] * wgt;
+              v.z = a[4 * qq + 2] * wgt;
+              v.w = a[4 * qq + 3] * wgt;
+              *reinterpret_cast<float4*>(dst + 8 * qq) = v;
+            }
           }
         }
+        csb = 0;
+        if (++cj < my_items) cur = ditem((int)blockIdx.x + cj * G, nlt, tiles, offsets);
       }
-      csb = 0;
-      if (++cj < my_items) cur = ditem((int)blockIdx.x + cj * G, nlt, tiles, offsets);
+      __syncthreads();
     }
-    __syncthreads();
-  }
+  };
+  if (th) consumer_loop(std::integral_constant<int, 1>{});
+  else consumer_loop(std::integral_constant<int, 0>{});
 }
 
 template <bool PROBE>

@@ -33,14 +33,16 @@
 //     table of the sub-block scale (one 8-byte LDS read from the 64 tables
 //     the workgroup builds at its start).  Only the producer itself reads
 //     its raw rows, so no barrier separates its stores from its unpack.
-// Step g: producers build operands of step g+1 in the other LDS buffer and
-// issue the global loads of step g+2; consumers run the MFMAs of step g; one
-// barrier.
+// Step g: producers stage the loaded data of step g+1 in the other LDS buffer,
+// issue the global loads of step g+2, then unpack step g+1's weights;
+// consumers run the MFMAs of step g; one barrier.
 // Epilogue (after an item's last step, consumers): H = G * sigmoid(G) * U,
 // then per 32 features of a token (16 in this lane, 16 in lane ^ 32) the q8_1
 // rule: amax, d = amax/127, id = 1/d, q = round-half-away(H * id) with IEEE
 // divisions (the codes' sum by v_dot4 on the packed codes); codes and fp16
 // (d, s) go to the workspace in sorted order.
+#include <type_traits>
+
 #include "lat_moe_internal.h"
 
 namespace latmoe {
@@ -177,9 +179,10 @@ __global__ __launch_bounds__(kThreads) void k_gateup(const int8_t* __restrict__ 
       need_setup = ++lj < my_items;
     }
   };
-  // S + U: registers -> LDS buffer b (raw rows, operand B, scales), then the
-  // producer's own rows unpacked into operand A of buffer b and dws[b].
-  auto build = [&](int b) {
+  // S: registers -> LDS buffer b (raw rows, operand B, scales).  The
+  // registers are free again after it, so the next step's loads are issued
+  // before the unpack and their latency overlaps it.
+  auto stage = [&](int b) {
     uint16_t* raw16 = reinterpret_cast<uint16_t*>(raw) + (32 * p + (lane >> 3)) * (kRawStride / 2) + (lane & 7);
 #pragma unroll
     for (int g = 0; g < 4; ++g)
@@ -191,7 +194,10 @@ __global__ __launch_bounds__(kThreads) void k_gateup(const int8_t* __restrict__ 
 #pragma unroll
     for (int c = 0; c < 4; ++c)
       dxs[b][(32 * p + 8 * c + (lane >> 3)) * 8 + (lane & 7)] = -as_float((int)rd[c]);  // minus: operand A is -w
-    // unpack: this lane's row ur, tasks (un, uj) = (u >> 1, 2 (u & 1) + (lane >> 5))
+  };
+  // U: the producer's own staged rows unpacked into operand A of buffer b.
+  auto unpack = [&](int b) {
+    // this lane's row ur, tasks (un, uj) = (u >> 1, 2 (u & 1) + (lane >> 5))
     const int ur = 32 * p + (lane & 31);
     const uint8_t* ublk = raw + ur * kRawStride;
     const uint4 h0 = *reinterpret_cast<const uint4*>(ublk);
@@ -240,7 +246,8 @@ __global__ __launch_bounds__(kThreads) void k_gateup(const int8_t* __restrict__ 
   int cj = 0, csb = 0;  // item index and super-block of the MFMA step
   Item cur = item_info((int)blockIdx.x, nft, tiles, offsets);
 
-  auto mfma_step = [&](int b) {
+  auto mfma_step = [&](auto grp_tag, int b) {
+    constexpr int GRP = decltype(grp_tag)::value;
     const bool active = 32 * tsub < cur.cnt;
     if (csb == 0) {
 #pragma unroll
@@ -264,6 +271,11 @@ __global__ __launch_bounds__(kThreads) void k_gateup(const int8_t* __restrict__ 
     v4i vb = *reinterpret_cast<const v4i*>(bp);
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb) {
+      // The two consumer waves of a SIMD (groups 0 and 1) take turns at the
+      // higher priority, one block each, so both finish the step together
+      // (oldest-first issue alone lets one run ahead and the other finish
+      // alone at a fraction of the VALU rate).
+      if ((GRP ^ kb) & 1) __builtin_amdgcn_s_setprio(1); else __builtin_amdgcn_s_setprio(0);
       const v16i ig = __builtin_amdgcn_mfma_i32_32x32x32_i8(va, vb, zero, 0, 0, 0);  // -I32
       const v16i iu = __builtin_amdgcn_mfma_i32_32x32x32_i8(vu, vb, zero, 0, 0, 0);
       if (kb < 7) {  // next block's operands
@@ -346,6 +358,9 @@ __global__ __launch_bounds__(kThreads) void k_gateup(const int8_t* __restrict__ 
   // The two roles run separate loops (so their registers are not live at the
   // same time) with the same barriers: two in the prologue, one per step.
   if (producer) {
+    // Producers issue first when both roles have VALU work: their chain of
+    // loads, LDS staging and unpack gates the next step of all waves.
+    __builtin_amdgcn_s_setprio(2);
     // prologue: the scale tables, operands of step 0 in buffer 0, loads of
     // step 1 in flight
     if (ptid < 64) {
@@ -356,26 +371,34 @@ __global__ __launch_bounds__(kThreads) void k_gateup(const int8_t* __restrict__ 
     fetch_ids(0);
     __syncthreads();
     load_next();
-    build(0);
-    __syncthreads();
+    stage(0);
+    unpack(0);
+    __syncthreads();  // also orders fetch_ids(1) (in setup(0)) before setup(1)
     if (n_steps > 1) load_next();
     for (int g = 0; g < n_steps; ++g) {
-      if (g + 1 < n_steps) build((g & 1) ^ 1);
+      if (g + 1 < n_steps) stage((g & 1) ^ 1);
       if (g + 2 < n_steps) load_next();
+      if (g + 1 < n_steps) unpack((g & 1) ^ 1);
       __syncthreads();
     }
   } else {
-    __syncthreads();
-    __syncthreads();
-    for (int g = 0; g < n_steps; ++g) {
-      mfma_step(g & 1);
-      if (++csb == nsb) {
-        epilogue();
-        csb = 0;
-        if (++cj < my_items) cur = item_info((int)blockIdx.x + cj * G, nft, tiles, offsets);
-      }
+    // one copy of the loop per consumer group (wave >> 2): the group selects
+    // the priority pattern, which s_setprio takes as an immediate
+    auto consumer_loop = [&](auto grp_tag) {
       __syncthreads();
-    }
+      __syncthreads();
+      for (int g = 0; g < n_steps; ++g) {
+        mfma_step(grp_tag, g & 1);
+        if (++csb == nsb) {
+          epilogue();
+          csb = 0;
+          if (++cj < my_items) cur = item_info((int)blockIdx.x + cj * G, nft, tiles, offsets);
+        }
+        __syncthreads();
+      }
+    };
+    if (wave >> 2) consumer_loop(std::integral_constant<int, 1>{});
+    else consumer_loop(std::integral_constant<int, 0>{});
   }
 }
 
