@@ -27,21 +27,8 @@
 namespace latmoe {
 namespace {
 
-constexpr int kSmallTok = 8;  // tokens per pass
+constexpr int kSmallTok = 4;  // tokens per pass
 constexpr int kSmallThreads = 256;
-
-// N consecutive dwords starting at LDS byte offset `off` (even) of base (a
-// 16-byte-aligned LDS array), realigned.
-template <int N>
-__device__ __forceinline__ void lds_dwords(const uint8_t* base, int off, uint32_t (&out)[N]) {
-  const uint32_t* p = reinterpret_cast<const uint32_t*>(base + (off & ~3));
-  const int sh = off & 3;  // 0 or 2
-  uint32_t w[N + 1];
-#pragma unroll
-  for (int i = 0; i <= N; ++i) w[i] = p[i];
-#pragma unroll
-  for (int i = 0; i < N; ++i) out[i] = __builtin_amdgcn_alignbyte(w[i + 1], w[i], sh);
-}
 
 // ---------------------------------------------------------------------------
 // Gate/up: workgroup (tile j of the route table -> expert, 32 features f0).
@@ -61,11 +48,8 @@ __global__ __launch_bounds__(kSmallThreads) void k_gateup_small(
   const int f0 = blockIdx.y * 32;
   const int tid = threadIdx.x, lane = tid & 63;
   const int nsb = L / 256, nxb = L / 32, nsub = L / 16, row_bytes = nsb * kQ3kBytes;
-  const int chunk = 32 * row_bytes;  // 32 rows, a multiple of 16 bytes
-  const int wpieces = 2 * chunk / 16;
-  // LDS: raw[64][row_bytes] | xs[kSmallTok][L] | xds[kSmallTok][nxb] | xsum[kSmallTok][nsub] | gus[64][kSmallTok]
-  uint8_t* raw = smem;
-  int8_t* xs = reinterpret_cast<int8_t*>(smem + 2 * chunk);
+  // LDS: xs[kSmallTok][L] | xds[kSmallTok][nxb] | xsum[kSmallTok][nsub] | gus[64][kSmallTok]
+  int8_t* xs = reinterpret_cast<int8_t*>(smem);
   float* xds = reinterpret_cast<float*>(xs + kSmallTok * L);
   int* xsum = reinterpret_cast<int*>(xds + kSmallTok * nxb);
   float* gus = reinterpret_cast<float*>(xsum + kSmallTok * nsub);
@@ -73,18 +57,25 @@ __global__ __launch_bounds__(kSmallThreads) void k_gateup_small(
   const rsrc_t rw = make_rsrc(gu + (int64_t)e * 2 * F * row_bytes, (uint32_t)(2 * F * row_bytes));
   const rsrc_t rx = make_rsrc(xc, (uint32_t)(T * L));
   const rsrc_t rd = make_rsrc(xd, (uint32_t)(T * nxb * 4));
-  constexpr int kWPer = (2 * 32 * 4 * kQ3kBytes / 16 + kSmallThreads - 1) / kSmallThreads;  // L <= 1024: 7
-  constexpr int kXPer = kSmallTok * 1024 / 16 / kSmallThreads;                               // 2
-  uint4 wv[kWPer];
-#pragma unroll
-  for (int m = 0; m < kWPer; ++m) {
-    const int i = tid + kSmallThreads * m;
-    const int h = i >= wpieces / 2, pi = i - h * (wpieces / 2);
-    wv[m] = buf_u128(rw, i < wpieces ? (h ? F + f0 : f0) * row_bytes + 16 * pi : kOutOfRange, 0);
-  }
-
+  constexpr int kXPer = kSmallTok * 1024 / 16 / kSmallThreads;  // 2
   const int r = tid >> 2, q = tid & 3;
   const int wrow = r < 32 ? f0 + r : F + f0 + r - 32;  // weight row of the expert
+  // This thread's super-block (L <= 1024: at most one, sb = q) straight into
+  // registers: bytes 0..107 as 16-byte pieces and a 12-byte tail (buffer loads
+  // at 2-byte-aligned offsets return the bytes there), d as a 16-bit load.
+  // Adjacent threads read adjacent blocks, a wave 16 whole rows.
+  uint32_t blk[28];
+  {
+    const int boff = q < nsb ? wrow * row_bytes + q * kQ3kBytes : kOutOfRange;
+#pragma unroll
+    for (int c = 0; c < 6; ++c) {
+      const uint4 v = buf_u128(rw, boff, 16 * c);
+      blk[4 * c] = v.x, blk[4 * c + 1] = v.y, blk[4 * c + 2] = v.z, blk[4 * c + 3] = v.w;
+    }
+    const auto t = __builtin_amdgcn_raw_buffer_load_b96(rw, boff, 96, 0);
+    blk[24] = t[0], blk[25] = t[1], blk[26] = t[2];
+    blk[27] = buf_u16(rw, boff, 108);
+  }
   for (int g0 = 0; g0 < cnt; g0 += kSmallTok) {
     const int nt = min(kSmallTok, cnt - g0);
     // ---- the group's token rows (pair ids read straight from perm)
@@ -105,13 +96,6 @@ __global__ __launch_bounds__(kSmallThreads) void k_gateup_small(
       dv = buf_u32(rd, ok ? ((p / k) * nxb + b) * 4 : kOutOfRange, 0);
     }
     if (g0 > 0) __syncthreads();  // the previous group's reads of xs / gus are done
-    if (g0 == 0) {
-#pragma unroll
-      for (int m = 0; m < kWPer; ++m) {
-        const int i = tid + kSmallThreads * m;
-        if (i < wpieces) reinterpret_cast<uint4*>(raw)[i] = wv[m];
-      }
-    }
 #pragma unroll
     for (int m = 0; m < kXPer; ++m) {
       const int i = tid + kSmallThreads * m;
@@ -131,9 +115,8 @@ __global__ __launch_bounds__(kSmallThreads) void k_gateup_small(
     float acc[kSmallTok];
 #pragma unroll
     for (int tk = 0; tk < kSmallTok; ++tk) acc[tk] = 0.f;
-    for (int sb = q; sb < nsb; sb += 4) {
-      uint32_t blk[28];  // the 110-byte super-block (+2 bytes), realigned
-      lds_dwords<28>(raw, r * row_bytes + sb * kQ3kBytes, blk);
+    if (q < nsb) {
+      const int sb = q;
       const float dw = half_bits_to_float(blk[27] & 0xffffu);
       float asb[kSmallTok];
 #pragma unroll
@@ -239,26 +222,28 @@ __global__ __launch_bounds__(kSmallThreads) void k_down_small(
   const int l0 = blockIdx.y * 32;
   const int tid = threadIdx.x;
   const int nfb = F / 32, row_bytes = nfb * kIq4Bytes;
-  const int chunk = 32 * row_bytes;  // a multiple of 16 bytes
-  const int wpieces = chunk / 16;
-  uint8_t* raw = smem;                                          // [32][row_bytes]
-  int8_t* hs = reinterpret_cast<int8_t*>(smem + chunk);         // [kSmallTok][F]
+  int8_t* hs = reinterpret_cast<int8_t*>(smem);                // [kSmallTok][F]
   float* hds = reinterpret_cast<float*>(hs + kSmallTok * F);    // [kSmallTok][nfb]
 
   const rsrc_t rw = make_rsrc(dn + (int64_t)e * L * row_bytes, (uint32_t)(L * row_bytes));
   const rsrc_t rh = make_rsrc(h_codes, (uint32_t)(pairs * F));
   const rsrc_t rs = make_rsrc(h_ds, (uint32_t)(pairs * nfb * 4));
-  constexpr int kWPer = (32 * 64 * kIq4Bytes / 16 + kSmallThreads - 1) / kSmallThreads;  // F <= 2048: 9
-  constexpr int kHPer = kSmallTok * 2048 / 16 / kSmallThreads;                          // 4
-  constexpr int kDPer = kSmallTok * 64 / kSmallThreads;                                 // 2
-  uint4 wv[kWPer];
-#pragma unroll
-  for (int m = 0; m < kWPer; ++m) {
-    const int i = tid + kSmallThreads * m;
-    wv[m] = buf_u128(rw, i < wpieces ? l0 * row_bytes + 16 * i : kOutOfRange, 0);
-  }
-
+  constexpr int kHPer = kSmallTok * 2048 / 16 / kSmallThreads;  // 4
+  constexpr int kDPer = kSmallTok * 64 / kSmallThreads;         // 2
+  constexpr int kBPer = 2048 / 32 / 8;                          // blocks per thread (F <= 2048): 8
   const int r = tid >> 3, q = tid & 7;
+  // This thread's blocks q, q + 8, ... of row l0 + r straight into registers:
+  // d as a 16-bit load, the 16 index bytes as one 16-byte load at the block's
+  // byte 2 (buffer loads at 2-byte-aligned offsets return the bytes there).
+  uint32_t bd[kBPer];
+  uint4 bi[kBPer];
+#pragma unroll
+  for (int m = 0; m < kBPer; ++m) {
+    const int kb = q + 8 * m;
+    const int boff = kb < nfb ? (l0 + r) * row_bytes + kb * kIq4Bytes : kOutOfRange;
+    bd[m] = buf_u16(rw, boff, 0);
+    bi[m] = buf_u128(rw, boff, 2);
+  }
   for (int g0 = 0; g0 < cnt; g0 += kSmallTok) {
     const int nt = min(kSmallTok, cnt - g0);
     uint4 hv[kHPer];
@@ -276,13 +261,6 @@ __global__ __launch_bounds__(kSmallThreads) void k_down_small(
       dv[m] = buf_u32(rs, (tk < nt && i < kSmallTok * nfb) ? ((pos0 + g0 + tk) * nfb + bb) * 4 : kOutOfRange, 0);
     }
     if (g0 > 0) __syncthreads();
-    if (g0 == 0) {
-#pragma unroll
-      for (int m = 0; m < kWPer; ++m) {
-        const int i = tid + kSmallThreads * m;
-        if (i < wpieces) reinterpret_cast<uint4*>(raw)[i] = wv[m];
-      }
-    }
 #pragma unroll
     for (int m = 0; m < kHPer; ++m) {
       const int i = tid + kSmallThreads * m;
@@ -298,16 +276,17 @@ __global__ __launch_bounds__(kSmallThreads) void k_down_small(
     float acc[kSmallTok];
 #pragma unroll
     for (int tk = 0; tk < kSmallTok; ++tk) acc[tk] = 0.f;
-    for (int kb = q; kb < nfb; kb += 8) {
-      uint32_t blk[5];  // d (2 bytes) | 16 index bytes, realigned (+2 bytes)
-      lds_dwords<5>(raw, r * row_bytes + kb * kIq4Bytes, blk);
-      const float dd = half_bits_to_float(blk[0] & 0xffffu);
+#pragma unroll
+    for (int m = 0; m < kBPer; ++m) {
+      const int kb = q + 8 * m;
+      if (kb >= nfb) break;
+      const float dd = half_bits_to_float(bd[m] & 0xffffu);
+      const uint32_t nibs[4] = {bi[m].x, bi[m].y, bi[m].z, bi[m].w};  // index bytes 4w .. 4w+3
       uint32_t op[8];
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const uint32_t nib = __builtin_amdgcn_alignbyte(blk[w + 1], blk[w], 2);  // index bytes 4w .. 4w+3
-        op[w] = iq4_lookup(nib & 0x0f0f0f0fu);             // elements 4w .. 4w+3
-        op[4 + w] = iq4_lookup((nib >> 4) & 0x0f0f0f0fu);  // elements 16+4w ..
+        op[w] = iq4_lookup(nibs[w] & 0x0f0f0f0fu);             // elements 4w .. 4w+3
+        op[4 + w] = iq4_lookup((nibs[w] >> 4) & 0x0f0f0f0fu);  // elements 16+4w ..
       }
 #pragma unroll
       for (int tk = 0; tk < kSmallTok; ++tk) {
@@ -353,8 +332,7 @@ bool small_path(const Shapes& s) {
 hipError_t launch_gateup_small(const Shapes& s, const Work& w, const uint8_t* gu, const ProbeRows* probe,
                                hipStream_t st) {
   const int nxb = s.L / 32;
-  const size_t lds = 2 * 32 * (s.L / 256) * kQ3kBytes + kSmallTok * s.L + 4 * kSmallTok * nxb +
-                     4 * kSmallTok * (s.L / 16) + 4 * 64 * kSmallTok;
+  const size_t lds = kSmallTok * s.L + 4 * kSmallTok * nxb + 4 * kSmallTok * (s.L / 16) + 4 * 64 * kSmallTok;
   const dim3 grid((unsigned)(s.pairs() < s.E ? s.pairs() : s.E), s.F / 32);
   const ProbeRows none = {nullptr, 0, 0};
   if (probe)
@@ -369,7 +347,7 @@ hipError_t launch_gateup_small(const Shapes& s, const Work& w, const uint8_t* gu
 hipError_t launch_down_small(const uint8_t* dn, const float* router_w, const Shapes& s, const Work& w,
                              const ProbeRows* probe, hipStream_t st) {
   const int nfb = s.F / 32;
-  const size_t lds = 32 * nfb * kIq4Bytes + kSmallTok * s.F + 4 * kSmallTok * nfb;
+  const size_t lds = kSmallTok * s.F + 4 * kSmallTok * nfb;
   const dim3 grid((unsigned)(s.pairs() < s.E ? s.pairs() : s.E), s.L / 32);
   const ProbeRows none = {nullptr, 0, 0};
   if (probe)
