@@ -56,6 +56,9 @@ def lib() -> ctypes.CDLL:
         c.orc_down_combine.argtypes = [P, P, P, P, i64, i32, i32, i32, i32, P, i64, P]
         c.orc_probe_gateup.argtypes = [P, P, P, i64, i32, i32, i32, i32, i64, P, P, P, P]
         c.orc_probe_down.argtypes = [P, P, P, i64, i32, i32, i32, i32, i64, P, P, P]
+        c.orc_dequant_q8_0.argtypes = [P, i64, P]
+        c.orc_dense_q8_0.argtypes = [P, i64, P, i32, i32, P, i64, P]
+        c.orc_probe_dense.argtypes = [P, i64, P, i32, i32, i64, P, P, P]
         c.orc_num_threads.restype = ctypes.c_int
         c.orc_set_num_threads.argtypes = [ctypes.c_int]
     return _lib
@@ -201,4 +204,38 @@ def probe_down(h_q8, router_idx, down, L, F, E, pairs, rows):
     out = np.zeros((n, F // 32), np.int32)
     lib().orc_probe_down(_p(_c(h_q8, np.uint8)), _p(idx), _p(_c(down, np.uint8)), T, L, F, E, k, n, _p(pairs),
                          _p(rows), _p(out))
+    return out
+
+
+def dequant_q8_0(blocks: np.ndarray) -> np.ndarray:
+    b = _c(blocks, np.uint8)
+    n = b.size // 34
+    out = np.empty(n * 32, np.float64)
+    lib().orc_dequant_q8_0(_p(b), n, _p(out))
+    return out.reshape(b.shape[:-1] + (32,))
+
+
+def dense_q8_0(x_q8: np.ndarray, w_q8_0: np.ndarray, N: int, K: int,
+               tokens: Optional[Sequence[int]] = None) -> np.ndarray:
+    """Latent D / U projection: x q8_1 [T, K/32, 36] against Q8_0 weights
+    [N, K/32, 34] -> fp64 [n_tok, N] (block dots folded in fp64)."""
+    x = _c(x_q8, np.uint8)
+    T = x.size // ((K // 32) * 36)
+    tok = None if tokens is None else _c(tokens, np.int64)
+    n_tok = T if tok is None else tok.size
+    y = np.zeros((n_tok, N), np.float64)
+    lib().orc_dense_q8_0(_p(x), T, _p(_c(w_q8_0, np.uint8)), N, K, _p(tok), n_tok, _p(y))
+    return y
+
+
+def probe_dense(x_q8, w_q8_0, N, K, tokens, rows):
+    """Integer block dots of (token, weight row) probes -> int32 [n, K/32]."""
+    x = _c(x_q8, np.uint8)
+    T = x.size // ((K // 32) * 36)
+    tok = _c(tokens, np.int64)
+    rows = _c(rows, np.int32)
+    assert tok.size == rows.size and (tok.size == 0 or (tok.min() >= 0 and tok.max() < T))
+    assert rows.size == 0 or (rows.min() >= 0 and rows.max() < N)
+    out = np.zeros((tok.size, K // 32), np.int32)
+    lib().orc_probe_dense(_p(x), T, _p(_c(w_q8_0, np.uint8)), N, K, tok.size, _p(tok), _p(rows), _p(out))
     return out

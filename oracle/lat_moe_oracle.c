@@ -24,7 +24,12 @@
  * expert is a scheduling choice that does not change the result, so the
  * oracle simply walks the pairs token by token.
  *
- * The Q3_K / IQ4_NL / q8_1 bit layouts are ggml's public GGUF block formats;
+ * It also computes the two dense projections around the stage in a latent
+ * layer (D: hidden row -> latent row, stored as q8_1; U: latent row ->
+ * hidden row), Q8_0 weights against q8_1 activations with the same block
+ * structure (see the section near the end of the file).
+ *
+ * The Q3_K / IQ4_NL / q8_1 / Q8_0 bit layouts are ggml's public GGUF block formats;
  * the pages name them without restating them.  They are restated here from
  * that specification.
  *
@@ -458,6 +463,93 @@ void orc_probe_down(const uint8_t* h_q8, const int32_t* idx, const uint8_t* down
     }
     const uint8_t* wrow = down + ((int64_t)e * L + row[i]) * row_bytes;
     down_row_dots(wrow, h_q8 + p * hrow_bytes, F, out + i * nb, dd);
+  }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Latent D / U dense projections (Q8_0 weights x q8_1 activations)          */
+/* ------------------------------------------------------------------------ */
+
+/* Source: page "Run Edge0-145B Q3_K on AMD HIP (Linux, gfx1100) #1", the
+ * lat_dense_w11.cu commit message: the two dense projections of a latent
+ * layer (D into the latent rows, U back out of them) are Q8_0 x q8_1 integer
+ * dots per 32-value block, and D rounds its products to the latent rows'
+ * q8_1 blocks with the same rule as the stage's other q8_1 stores.
+ *
+ * Q8_0 (ggml): 32 weights in 34 bytes = d (fp16) | qs[32] (int8); weight
+ * i = d * qs[i]. */
+#define Q80_BYTES 34
+#define Q80_VALUES 32
+
+void orc_q8_0_decode(const uint8_t* blk, int8_t* q, double* d) {
+  for (int i = 0; i < Q80_VALUES; ++i) q[i] = (int8_t)blk[2 + i];
+  *d = orc_half_to_double(rd16(blk));
+}
+void orc_dequant_q8_0(const uint8_t* blocks, int64_t nblocks, double* out) {
+  for (int64_t b = 0; b < nblocks; ++b) {
+    int8_t q[Q80_VALUES];
+    double d;
+    orc_q8_0_decode(blocks + b * Q80_BYTES, q, &d);
+    for (int i = 0; i < Q80_VALUES; ++i) out[b * Q80_VALUES + i] = d * (double)q[i];
+  }
+}
+
+/* Block dots of weight row w (K/32 Q8_0 blocks) with activation row x
+ * (K/32 q8_1 blocks): D32[b] = sum_i qw(i) * qx(i); dw[b], dx[b] get the
+ * two block scales. */
+static void dense_row_dots(const uint8_t* w, const uint8_t* x, int K, int32_t* D32, double* dw, double* dx) {
+  int nb = K / Q80_VALUES;
+  for (int b = 0; b < nb; ++b) {
+    int8_t qw[Q80_VALUES], qx[Q81_VALUES];
+    orc_q8_0_decode(w + (int64_t)b * Q80_BYTES, qw, &dw[b]);
+    orc_q8_1_decode(x + (int64_t)b * Q81_BYTES, qx, &dx[b]);
+    int32_t acc = 0;
+    for (int i = 0; i < Q80_VALUES; ++i) acc += (int32_t)qw[i] * (int32_t)qx[i];
+    D32[b] = acc;
+  }
+}
+
+/* y[t][n] = sum over blocks b (ascending) of dw[n][b] * dx[t][b] * D32[t][n][b]
+ * in fp64, for the tokens tok[0..n_tok) (all T tokens when tok is NULL).
+ * x [T][K/32] q8_1, w [N][K/32] Q8_0, y [n_tok][N]. */
+void orc_dense_q8_0(const uint8_t* x_q8, int64_t T, const uint8_t* w, int N, int K, const int64_t* tok,
+                    int64_t n_tok, double* y) {
+  int nb = K / Q80_VALUES;
+  int64_t xrow = (int64_t)nb * Q81_BYTES, wrow = (int64_t)nb * Q80_BYTES;
+  (void)T;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t i = 0; i < n_tok; ++i) {
+    int64_t t = tok ? tok[i] : i;
+    int32_t* D32 = (int32_t*)malloc(sizeof(int32_t) * nb);
+    double* dw = (double*)malloc(sizeof(double) * nb);
+    double* dx = (double*)malloc(sizeof(double) * nb);
+    for (int n = 0; n < N; ++n) {
+      dense_row_dots(w + n * wrow, x_q8 + t * xrow, K, D32, dw, dx);
+      double acc = 0.0;
+      for (int b = 0; b < nb; ++b) acc += dw[b] * dx[b] * (double)D32[b];
+      y[i * N + n] = acc;
+    }
+    free(D32);
+    free(dw);
+    free(dx);
+  }
+}
+
+/* Dense block-dot probes: for probe i = (token tok[i], weight row row[i]),
+ * out[i][K/32] = D32. */
+void orc_probe_dense(const uint8_t* x_q8, int64_t T, const uint8_t* w, int N, int K, int64_t n, const int64_t* tok,
+                     const int32_t* row, int32_t* out) {
+  int nb = K / Q80_VALUES;
+  int64_t xrow = (int64_t)nb * Q81_BYTES, wrow = (int64_t)nb * Q80_BYTES;
+  (void)T;
+  (void)N;
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) {
+    double* dw = (double*)malloc(sizeof(double) * nb);
+    double* dx = (double*)malloc(sizeof(double) * nb);
+    dense_row_dots(w + row[i] * wrow, x_q8 + tok[i] * xrow, K, out + i * nb, dw, dx);
+    free(dw);
+    free(dx);
   }
 }
 

@@ -27,6 +27,19 @@ in this order):
 
 The Q3_K, IQ4_NL and q8_1 block layouts are ggml's (GGUF) formats; the pages
 on the latent expert stage name them without restating them.
+
+Latent D / U projection workloads (``DenseWorkload``; the dense projections
+into and out of the latent rows, Q8_0 weights), one ``default_rng(seed)``
+stream, in this order:
+
+1. ``x``: T x H float32 standard normal (hidden rows that D reads once they
+   are rounded to q8_1).
+2. D weights, Q8_0 blocks [L][H/32] x 34 bytes: int8 codes uniform in
+   -127..127, fp16 block scale at bytes 0..1 drawn from U(0.5, 1.5) * 2^-12
+   (so a projected value has a standard deviation of order one).
+3. ``z``: T x L float32 standard normal (latent rows that U reads, standing
+   in for the expert stage's output, once rounded to q8_1).
+4. U weights, Q8_0 blocks [H][L/32] x 34 bytes, drawn as in 2.
 """
 from __future__ import annotations
 
@@ -41,6 +54,8 @@ IQ4NL_BLOCK_BYTES = 18     # 32 weights: fp16 d, qs[16]
 IQ4NL_BLOCK_VALUES = 32
 Q8_1_BLOCK_BYTES = 36      # 32 values: fp16 d, fp16 s, int8 qs[32]
 Q8_1_BLOCK_VALUES = 32
+Q8_0_BLOCK_BYTES = 34      # 32 weights: fp16 d, int8 qs[32]
+Q8_0_BLOCK_VALUES = 32
 
 
 @dataclasses.dataclass(frozen=True)
@@ -138,3 +153,54 @@ def group_sizes(router_idx: np.ndarray, E: int) -> np.ndarray:
 def workload(name: str, seed: Optional[int] = None) -> Workload:
     wl = WORKLOADS[name]
     return wl if seed is None else wl.replace(seed=seed)
+
+
+@dataclasses.dataclass(frozen=True)
+class DenseWorkload:
+    """Shapes of the latent layer's dense projections: D maps hidden rows
+    (width H) to latent rows (width L), U maps latent rows back to width H."""
+    name: str
+    T: int          # tokens
+    H: int          # hidden width (multiple of 32)
+    L: int          # latent width (multiple of 32)
+    seed: int = 0
+
+    def replace(self, **kw) -> "DenseWorkload":
+        return dataclasses.replace(self, **kw)
+
+
+DENSE_WORKLOADS: Dict[str, DenseWorkload] = {
+    "du_tiny": DenseWorkload("du_tiny", T=37, H=512, L=256),
+    "du_decode": DenseWorkload("du_decode", T=4, H=4096, L=1024),
+    "du_prefill_5k": DenseWorkload("du_prefill_5k", T=5268, H=4096, L=1024),
+}
+
+
+@dataclasses.dataclass
+class DenseInputs:
+    wl: DenseWorkload
+    x: np.ndarray        # float32 [T, H]
+    d_q8_0: np.ndarray   # uint8 [L, H/32, 34]
+    z: np.ndarray        # float32 [T, L]
+    u_q8_0: np.ndarray   # uint8 [H, L/32, 34]
+
+
+def random_q8_0(rng: np.random.Generator, shape: tuple) -> np.ndarray:
+    """Q8_0 blocks with codes uniform in -127..127 and fp16 scales
+    d ~ U(0.5, 1.5) * 2^-12."""
+    b = np.empty(shape + (Q8_0_BLOCK_BYTES,), np.uint8)
+    b[..., 2:] = rng.integers(-127, 128, size=shape + (32,), dtype=np.int8).view(np.uint8)
+    d = (rng.uniform(0.5, 1.5, size=shape) * 2.0 ** -12).astype(np.float16)
+    b[..., 0:2] = d.view(np.uint8).reshape(shape + (2,))
+    return b
+
+
+def make_dense_inputs(wl: DenseWorkload) -> DenseInputs:
+    if wl.H % 32 or wl.L % 32 or wl.H <= 0 or wl.L <= 0 or wl.T < 0:
+        raise ValueError(f"unsupported dense workload shape {wl}")
+    rng = np.random.default_rng(wl.seed)
+    x = rng.standard_normal((wl.T, wl.H), dtype=np.float32)
+    dw = random_q8_0(rng, (wl.L, wl.H // 32))
+    z = rng.standard_normal((wl.T, wl.L), dtype=np.float32)
+    uw = random_q8_0(rng, (wl.H, wl.L // 32))
+    return DenseInputs(wl, x, dw, z, uw)

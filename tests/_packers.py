@@ -1,4 +1,4 @@
-"""Block *encoders* for the ggml Q3_K / IQ4_NL / q8_1 layouts (test helper).
+"""Block *encoders* for the ggml Q3_K / IQ4_NL / q8_1 / Q8_0 layouts (test helper).
 
 These write fields into bytes -- the inverse of the oracle's decoders -- so a
 round trip (pack here, decode in the oracle) pins the decoders' bit layout
@@ -6,6 +6,7 @@ without re-typing them.  Layouts (ggml GGUF block formats):
   Q3_K   110 B: hmask[32] | qs[64] | scales[12] | d fp16    (256 weights)
   IQ4_NL  18 B: d fp16 | qs[16]                               (32 weights)
   q8_1    36 B: d fp16 | s fp16 | qs[32] int8                 (32 values)
+  Q8_0    34 B: d fp16 | qs[32] int8                          (32 weights)
 """
 import numpy as np
 
@@ -64,4 +65,14 @@ def pack_q8_1(q: np.ndarray, d: np.ndarray, s: np.ndarray) -> np.ndarray:
     out[:, 0:2] = np.asarray(d, np.float16).view(np.uint8).reshape(n, 2)
     out[:, 2:4] = np.asarray(s, np.float16).view(np.uint8).reshape(n, 2)
     out[:, 4:36] = q.view(np.uint8)
+    return out
+
+
+def pack_q8_0(q: np.ndarray, d: np.ndarray) -> np.ndarray:
+    """q [n,32] int8, d [n] float16 -> [n,34] uint8."""
+    q = np.asarray(q, np.int8)
+    n = q.shape[0]
+    out = np.zeros((n, 34), np.uint8)
+    out[:, 0:2] = np.asarray(d, np.float16).view(np.uint8).reshape(n, 2)
+    out[:, 2:34] = q.view(np.uint8)
     return out
