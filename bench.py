@@ -118,6 +118,69 @@ class Stage:
         return [a / steps for a in acc]
 
 
+class DenseStage:
+    """The latent layer's D and U projections (Q8_0 x q8_1) resident on the GPU:
+    D takes the hidden rows (q8_1) to q8_1 latent rows, U takes latent rows
+    (q8_1) to fp32 hidden rows."""
+
+    def __init__(self, dwl):
+        import numpy as np
+        import torch
+        import quantized_latent_moe_amd as lm
+        from quantized_latent_moe_amd.inputs import make_dense_inputs
+        self.lm, self.torch, self.wl = lm, torch, dwl
+        I = make_dense_inputs(dwl)
+        dev = torch.device("cuda", 0)
+        t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+        self.xh = torch.empty((dwl.T, dwl.H // 32, 36), dtype=torch.uint8, device=dev)
+        self.zl = torch.empty((dwl.T, dwl.L // 32, 36), dtype=torch.uint8, device=dev)
+        lm.quantize_q8_1(t(I.x), self.xh)
+        lm.quantize_q8_1(t(I.z), self.zl)
+        self.dw, self.uw = t(I.d_q8_0), t(I.u_q8_0)
+        self.xl = torch.empty((dwl.T, dwl.L // 32, 36), dtype=torch.uint8, device=dev)
+        self.out = torch.empty((dwl.T, dwl.H), dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
+
+    def run_d(self):
+        w = self.wl
+        self.lm.dense_q8_0(self.xh, self.dw, w.T, w.L, w.H, None, self.xl)
+
+    def run_u(self):
+        w = self.wl
+        self.lm.dense_q8_0(self.zl, self.uw, w.T, w.H, w.L, self.out, None)
+
+    def time(self, fn, steps, warmup):
+        torch = self.torch
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    def report(self, steps, warmup):
+        w = self.wl
+        res = {"workload": w.name, "T": w.T, "H": w.H, "L": w.L}
+        for name, fn, N, K, out_bytes in (("D", self.run_d, w.L, w.H, w.T * (w.L // 32) * 36),
+                                          ("U", self.run_u, w.H, w.L, w.T * w.H * 4)):
+            ms = self.time(fn, steps, warmup)
+            ops = 2 * w.T * N * K
+            folds = 2 * w.T * N * (K // 32)
+            nbytes = N * (K // 32) * 34 + w.T * (K // 32) * 36 + out_bytes
+            fold_t = folds / (ms * 1e-3) / 1e12
+            res[name] = {"us": round(ms * 1e3, 2), "N": N, "K": K,
+                         "fold_valu": {"achieved": round(fold_t, 2), "peak": round(PEAK_VALU_TOPS, 1),
+                                       "unit": "T lane-op/s", "frac": round(fold_t / PEAK_VALU_TOPS, 4)},
+                         "int8_frac": round(ops / (ms * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4),
+                         "hbm_gbs": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+            print(f"[bench] {w.name} {name}: {ms * 1e3:.2f} us", file=sys.stderr, flush=True)
+        return res
+
+
 def cpu_baseline(wl, target_s):
     """The oracle, as it stands, on the first n tokens of the same workload."""
     import numpy as np
@@ -213,6 +276,8 @@ def main():
     ap.add_argument("--workload", default="prefill_5k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-du", action="store_true", help="skip the latent D / U projection timings")
+    ap.add_argument("--du-only", action="store_true", help="time only the latent D / U projections")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="first run a plain device copy of MIB MiB (three times), the reference for counter scaling")
@@ -242,6 +307,13 @@ def main():
             torch.neg(src, out=dst)   # reads n bytes, writes n bytes
         torch.cuda.synchronize()
         del src, dst
+    if args.du_only:
+        from quantized_latent_moe_amd.inputs import DENSE_WORKLOADS
+        for name in ("du_prefill_5k", "du_decode"):
+            ds = DenseStage(DENSE_WORKLOADS[name])
+            print(json.dumps(ds.report(args.steps, args.warmup)), flush=True)
+            del ds
+        return
     st = Stage(wl)
     alg = algorithmic(wl, st.inputs.router_idx)
     ms, wall_ms = st.time_steps(args.steps, args.warmup)
@@ -301,6 +373,15 @@ def main():
                          "stage_us": {n: round(v * 1e3, 2) for n, v in zip(names, dstage)}}
         print(f"[bench] decode {dms * 1e3:.2f} us/step, {gbs:.0f} GB/s", file=sys.stderr, flush=True)
         del ds
+    if not args.no_du:
+        from quantized_latent_moe_amd.inputs import DENSE_WORKLOADS
+        du = {}
+        for name in ("du_prefill_5k", "du_decode"):
+            ds = DenseStage(DENSE_WORKLOADS[name])
+            du[name] = ds.report(args.steps if name == "du_prefill_5k" else max(args.steps, 50), args.warmup)
+            del ds
+        out["latent_du"] = du
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a token sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)

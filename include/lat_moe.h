@@ -121,6 +121,34 @@ int lat_moe_expert_forward_debug(const void* x_q8_1, const int32_t* router_idx, 
  * store) and the same rule the stage applies to H. */
 int lat_moe_quantize_q8_1(const float* x, int64_t rows, int32_t cols, void* out_q8_1, void* stream);
 
+/* Latent D / U dense projection (page "Run Edge0-145B Q3_K on AMD HIP (Linux,
+ * gfx1100) #1", the lat_dense_w11.cu commit message: the two dense projections
+ * of a latent layer, D into the latent rows and U back out of them, as Q8_0 x
+ * q8_1 integer dots; D stores its products as the latent rows' q8_1 blocks):
+ *     y[t][n] = sum over 32-value blocks b of d_w[n][b] * d_x[t][b] * I[t][n][b],
+ *     I[t][n][b] = sum over the block of qw * qx   (int32, exact),
+ * scales folded in fp32.
+ *   x_q8_1   [T][K/32] q8_1 blocks            activations
+ *   w_q8_0   [N][K/32] Q8_0 blocks, 34 B each: d (fp16) | qs[32] (int8)
+ *   y_f32    [T][N] fp32, overwritten, or NULL
+ *   y_q8_1   [T][N/32] q8_1 blocks, overwritten, or NULL: y rounded with the
+ *            q8_1 rule above (the same bytes lat_moe_quantize_q8_1 makes of y_f32)
+ *   stream   hipStream_t
+ * Supported: T >= 0, K % 32 == 0, N % 32 == 0, 32 <= K, N <= 65536,
+ * N * K/32 * 34 < 2^31 and T * K/32 * 36 < 2^31 bytes.  At least one output
+ * must be given; pointers 16-byte aligned (the weight rows themselves are only
+ * 2-byte aligned and are read as such).  T = 0 enqueues nothing.  Outputs are
+ * deterministic.  No workspace. */
+int lat_moe_dense_q8_0(const void* x_q8_1, const void* w_q8_0, int64_t T, int32_t N, int32_t K, float* y_f32,
+                       void* y_q8_1, void* stream);
+
+/* As lat_moe_dense_q8_0, plus the integer block dots I of weight rows
+ * row0 .. row0+rows-1: dots_i32 [T][rows][K/32] int32 (device memory);
+ * 0 <= row0, 1 <= rows, row0 + rows <= N. */
+int lat_moe_dense_q8_0_debug(const void* x_q8_1, const void* w_q8_0, int64_t T, int32_t N, int32_t K,
+                             float* y_f32, void* y_q8_1, void* stream, int32_t* dots_i32, int32_t row0,
+                             int32_t rows);
+
 /* Static description of an error code. */
 const char* lat_moe_strerror(int code);
 

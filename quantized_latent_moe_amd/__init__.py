@@ -22,6 +22,8 @@ EXPORTED = (
     "lat_moe_expert_forward",
     "lat_moe_expert_forward_debug",
     "lat_moe_quantize_q8_1",
+    "lat_moe_dense_q8_0",
+    "lat_moe_dense_q8_0_debug",
     "lat_moe_strerror",
     "lat_moe_version",
 )
@@ -73,6 +75,11 @@ def lib() -> ctypes.CDLL:
         c.lat_moe_expert_forward_debug.restype = ctypes.c_int
         c.lat_moe_quantize_q8_1.argtypes = [P, ctypes.c_int64, ctypes.c_int32, P, P]
         c.lat_moe_quantize_q8_1.restype = ctypes.c_int
+        i32, i64 = ctypes.c_int32, ctypes.c_int64
+        c.lat_moe_dense_q8_0.argtypes = [P, P, i64, i32, i32, P, P, P]
+        c.lat_moe_dense_q8_0.restype = ctypes.c_int
+        c.lat_moe_dense_q8_0_debug.argtypes = [P, P, i64, i32, i32, P, P, P, P, i32, i32]
+        c.lat_moe_dense_q8_0_debug.restype = ctypes.c_int
         c.lat_moe_strerror.argtypes = [ctypes.c_int]
         c.lat_moe_strerror.restype = ctypes.c_char_p
         c.lat_moe_version.restype = ctypes.c_int
@@ -144,6 +151,17 @@ def quantize_q8_1(x, out, stream=None) -> None:
     """fp32 [rows, cols] -> q8_1 blocks (uint8 [rows, cols/32, 36])."""
     rows, cols = x.shape
     _check(lib().lat_moe_quantize_q8_1(_ptr(x), int(rows), int(cols), _ptr(out), _stream(stream)))
+
+
+def dense_q8_0(x_q8_1, w_q8_0, T: int, N: int, K: int, y_f32=None, y_q8_1=None, *, dots_i32=None, row0: int = 0,
+               stream=None) -> None:
+    """Latent D / U projection: q8_1 rows x_q8_1 (uint8 [T, K/32, 36]) against
+    Q8_0 weights (uint8 [N, K/32, 34]) -> y_f32 (fp32 [T, N]) and/or y_q8_1
+    (uint8 [T, N/32, 36]); dots_i32 (int32 [T, rows, K/32]) takes the block
+    dots of weight rows row0 .. row0+rows-1."""
+    rows = 0 if dots_i32 is None else int(dots_i32.shape[1])
+    _check(lib().lat_moe_dense_q8_0_debug(_ptr(x_q8_1), _ptr(w_q8_0), int(T), int(N), int(K), _ptr(y_f32),
+                                          _ptr(y_q8_1), _stream(stream), _ptr(dots_i32), int(row0), rows))
 
 
 def version() -> int:

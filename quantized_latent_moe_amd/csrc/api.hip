@@ -192,6 +192,34 @@ int lat_moe_quantize_q8_1(const float* x, int64_t rows, int32_t cols, void* out_
   return LAT_MOE_OK;
 }
 
+int lat_moe_dense_q8_0_debug(const void* x_q8_1, const void* w_q8_0, int64_t T, int32_t N, int32_t K,
+                             float* y_f32, void* y_q8_1, void* stream, int32_t* dots_i32, int32_t row0,
+                             int32_t rows) {
+  if (T < 0 || K < 32 || K > 65536 || K % 32 || N < 32 || N > 65536 || N % 32) return LAT_MOE_EINVAL;
+  if ((int64_t)N * (K / 32) * 34 >= (int64_t)1 << 31 || T * (K / 32) * 36 >= (int64_t)1 << 31) return LAT_MOE_EINVAL;
+  if (!y_f32 && !y_q8_1) return LAT_MOE_EINVAL;
+  if (dots_i32 && (row0 < 0 || rows < 1 || (int64_t)row0 + rows > N)) return LAT_MOE_EINVAL;
+  if (T == 0) return LAT_MOE_OK;
+  const void* need[] = {x_q8_1, w_q8_0};
+  for (const void* p : need)
+    if (!p || !aligned16(p)) return LAT_MOE_EINVAL;
+  if ((y_f32 && !aligned16(y_f32)) || (y_q8_1 && !aligned16(y_q8_1)) || (dots_i32 && !aligned16(dots_i32)))
+    return LAT_MOE_EINVAL;
+  int rc = check_device(nullptr);
+  if (rc != LAT_MOE_OK) return rc;
+  const ProbeRows probe{dots_i32, row0, rows};
+  if (launch_dense_q8_0(static_cast<const uint8_t*>(x_q8_1), static_cast<const uint8_t*>(w_q8_0), T, N, K, y_f32,
+                        static_cast<uint8_t*>(y_q8_1), dots_i32 ? &probe : nullptr,
+                        static_cast<hipStream_t>(stream)) != hipSuccess)
+    return LAT_MOE_ELAUNCH;
+  return LAT_MOE_OK;
+}
+
+int lat_moe_dense_q8_0(const void* x_q8_1, const void* w_q8_0, int64_t T, int32_t N, int32_t K, float* y_f32,
+                       void* y_q8_1, void* stream) {
+  return lat_moe_dense_q8_0_debug(x_q8_1, w_q8_0, T, N, K, y_f32, y_q8_1, stream, nullptr, 0, 0);
+}
+
 const char* lat_moe_strerror(int code) {
   switch (code) {
     case LAT_MOE_OK: return "ok";

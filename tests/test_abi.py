@@ -72,3 +72,22 @@ def test_strerror():
     for c in range(5):
         assert lm.strerror(c)
     assert "unknown" in lm.strerror(99)
+
+
+def test_dense_argument_errors_before_any_hip_call():
+    f = lm.lib().lat_moe_dense_q8_0
+    fd = lm.lib().lat_moe_dense_q8_0_debug
+    x, w, y, q = 0x10000, 0x20000, 0x30000, 0x40000  # aligned, never dereferenced on these paths
+    for T, N, K in [(4, 40, 64), (4, 64, 40), (4, 0, 64), (4, 64, 0), (-1, 64, 64), (4, 64, 1 << 17),
+                    (1 << 30, 64, 64), (4, 65536, 65536)]:
+        assert f(x, w, T, N, K, y, q, None) == 1, (T, N, K)
+    assert f(x, w, 4, 64, 64, None, None, None) == 1           # no output
+    assert f(x + 4, w, 4, 64, 64, y, None, None) == 1          # misaligned
+    assert f(x, w + 2, 4, 64, 64, y, None, None) == 1
+    assert f(x, w, 4, 64, 64, y + 8, None, None) == 1
+    assert f(x, w, 4, 64, 64, None, q + 4, None) == 1
+    assert f(None, w, 4, 64, 64, y, None, None) == 1
+    assert fd(x, w, 4, 64, 64, y, None, None, 0x50000, 60, 8) == 1  # probe rows beyond N
+    assert fd(x, w, 4, 64, 64, y, None, None, 0x50000, 0, 0) == 1
+    # T = 0 is a no-op that touches nothing
+    assert f(None, None, 0, 64, 64, y, None, None) == 0
