@@ -24,17 +24,27 @@
 // 8 q + 4 (lane >> 5) + i (q, i < 4), so d_x is one value per lane and d_w
 // four 16-byte LDS reads shared by both tiles.
 //
-// K steps of kKB blocks, double-buffered in LDS: every thread loads one
-// 16-byte half of a weight block's codes and two of activation codes
-// (buffer loads; Q8_0 rows are 34-byte blocks, read unaligned), plus the fp16
-// scales, and writes them to LDS as [block][half][row][16 B] so that a
-// fragment read is 1 KiB contiguous.  Loads for step g + 2 are issued before
-// the MFMAs of step g.
+// K steps of kKB blocks, double-buffered in LDS and with two register sets
+// of loads in flight: the workgroup's threads load 16-byte halves of weight
+// and activation blocks (buffer loads; Q8_0 rows are 34-byte blocks, read
+// unaligned) and the fp16 scales, the lanes of one load instruction walking
+// a few contiguous row segments (a lane per row would touch a cache line per
+// lane), and write them to LDS as (block, half) planes of 16-byte row slots,
+// so a fragment read is 1 KiB contiguous.
+//
+// Batches of at most kSmallTok tokens take k_dense_small instead: GEMV
+// shaped, one workgroup per 32 output rows (one q8_1 block of every token's
+// output), the lanes of a wave on consecutive blocks of one row (coalesced
+// weight reads), each lane's activation blocks held in registers for all the
+// rows it visits, integer dots by v_dot4, the fold per block in fp32, a
+// butterfly sum across the lanes of a row, and the q8_1 rounding from LDS.
 //
 // Work items are dealt XCD-major: workgroup w runs on XCD w % 8 and takes
 // item (w % 8) * ceil(items / 8) + w / 8, items ordered token tile major,
 // so each XCD's L2 holds one contiguous range of activation rows and the
 // weight rows it sweeps over.
+#include <type_traits>
+
 #include "lat_moe_internal.h"
 
 namespace latmoe {
@@ -43,18 +53,26 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kRowsWG = 64;   // weight rows per work item
 constexpr int kTokWG = 128;   // tokens per work item
-constexpr int kKB = 2;        // 32-value blocks per K step
+constexpr int kLogKB = 2;
+constexpr int kKB = 1 << kLogKB;  // 32-value blocks per K step
 constexpr int kQ80Bytes = 34;
 constexpr int kXcds = 8;
+// LDS slots of 16 bytes: (block, half) planes of rows/tokens, each plane
+// padded by 16 bytes so that the lanes of a load instruction, which walk the
+// (block, half) planes of one row, write to different banks.
+constexpr int kAPlane = kRowsWG * 16 + 16;
+constexpr int kBPlane = kTokWG * 16 + 16;
+constexpr int kDwStride = kRowsWG + 4;  // floats; 16-byte multiple, 4 banks apart
+constexpr int kDxStride = kTokWG + 4;
 
 struct Smem {
-  int8_t a[2][kKB][2][kRowsWG][16];  // weight codes [buf][block][half][row]
-  int8_t b[2][kKB][2][kTokWG][16];   // activation codes [buf][block][half][token]
-  float dw[2][kKB][kRowsWG];         // weight block scales
-  float dx[2][kKB][kTokWG];          // activation block scales
+  int8_t a[2][2 * kKB * kAPlane];   // weight codes, plane 2 b + half, row r at 16 r
+  int8_t b[2][2 * kKB * kBPlane];   // activation codes, plane 2 b + half, token t at 16 t
+  float dw[2][kKB * kDwStride + 4];  // weight block scales [block][row]; the last word takes stores of no task
+  float dx[2][kKB * kDxStride + 4];  // activation block scales [block][token]; likewise
 };
-static_assert(kRowsWG * kKB * 2 == kThreads, "one weight half-block per thread and step");
-static_assert(kTokWG * kKB * 2 == 2 * kThreads, "two activation half-blocks per thread and step");
+static_assert(kRowsWG == 64 && kTokWG == 128 && kThreads == 256 && kKB >= 2,
+              "the loader deals 64 rows and 128 tokens per step over 256 threads");
 
 template <bool PROBE>
 __global__ __launch_bounds__(kThreads) void k_dense_q8_0(const uint8_t* __restrict__ x, const uint8_t* __restrict__ w,
@@ -75,48 +93,79 @@ __global__ __launch_bounds__(kThreads) void k_dense_q8_0(const uint8_t* __restri
   const int wr = wave & 1, wc = wave >> 1;
 
   // ---- loader: fixed per-thread roles ----
-  // weight half-block: row row0 + (tid & 63), block (tid >> 7) of the step, half (tid >> 6) & 1
+  // Per step the workgroup moves kKB blocks of its 64 weight rows and 128
+  // tokens.  Task q = tid + 256 i walks (half, block) fastest, so the lanes of
+  // one load instruction read a few contiguous row segments (kKB blocks of a
+  // row are adjacent in memory): weight half-block (row q >> (kLogKB + 1),
+  // block (q >> 1) & (kKB - 1), half q & 1), activation half-block likewise
+  // with tokens, and the scales (row or token q >> kLogKB, block
+  // q & (kKB - 1)).
+  constexpr int kA = kKB / 2, kB = kKB;                           // 16-byte loads per thread
+  constexpr int kSA = (kRowsWG * kKB + kThreads - 1) / kThreads;  // weight scales per thread
+  constexpr int kSB = (kTokWG * kKB + kThreads - 1) / kThreads;   // activation scales per thread
   const rsrc_t rw = make_rsrc(w, (uint32_t)((int64_t)N * nb * kQ80Bytes));
   const rsrc_t rx = make_rsrc(x, (uint32_t)((int64_t)T * nb * kQ81Bytes));
-  const int a_row = row0 + (tid & 63), a_blk = tid >> 7, a_half = (tid >> 6) & 1;
-  const int a_off = a_row < N ? (a_row * nb + a_blk) * kQ80Bytes + 2 + 16 * a_half : kOutOfRange;
-  // weight scale (threads < 128): row row0 + (tid & 63), block tid >> 6
-  const int s_row = row0 + (tid & 63), s_blk = (tid >> 6) & 1;
-  const int sw_off = (tid < kRowsWG * kKB && s_row < N) ? (s_row * nb + s_blk) * kQ80Bytes : kOutOfRange;
-  // activation half-blocks: item q = tid + 256 j -> block q >> 8, half (q >> 7) & 1, token q & 127
-  int b_off[2];
+  int a_off[kA], b_off[kB], sa_off[kSA], sb_off[kSB];
+  int a_blk[kA], b_blk[kB], sa_blk[kSA], sb_blk[kSB];
+  int a_lds[kA], b_lds[kB], sa_lds[kSA], sb_lds[kSB];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int q = tid + kThreads * j;
-    const int t = tok0 + (q & 127);
-    b_off[j] = t < T ? (t * nb + (q >> 8)) * kQ81Bytes + 4 + 16 * ((q >> 7) & 1) : kOutOfRange;
+  for (int i = 0; i < kA; ++i) {
+    const int q = tid + kThreads * i, rl = q >> (kLogKB + 1), r = row0 + rl, h = q & 1;
+    a_blk[i] = (q >> 1) & (kKB - 1);
+    a_off[i] = r < N ? (r * nb + a_blk[i]) * kQ80Bytes + 2 + 16 * h : kOutOfRange;
+    a_lds[i] = (2 * a_blk[i] + h) * kAPlane + 16 * rl;
   }
-  // activation scale: token tok0 + (tid & 127), block tid >> 7
-  const int s_tok = tok0 + (tid & 127);
-  const int sx_off = s_tok < T ? (s_tok * nb + (tid >> 7)) * kQ81Bytes : kOutOfRange;
+#pragma unroll
+  for (int j = 0; j < kB; ++j) {
+    const int q = tid + kThreads * j, tl = q >> (kLogKB + 1), t = tok0 + tl, h = q & 1;
+    b_blk[j] = (q >> 1) & (kKB - 1);
+    b_off[j] = t < T ? (t * nb + b_blk[j]) * kQ81Bytes + 4 + 16 * h : kOutOfRange;
+    b_lds[j] = (2 * b_blk[j] + h) * kBPlane + 16 * tl;
+  }
+#pragma unroll
+  for (int i = 0; i < kSA; ++i) {
+    const int q = tid + kThreads * i, rl = q >> kLogKB, r = row0 + rl;
+    sa_blk[i] = q & (kKB - 1);
+    sa_off[i] = (q < kRowsWG * kKB && r < N) ? (r * nb + sa_blk[i]) * kQ80Bytes : kOutOfRange;
+    sa_lds[i] = q < kRowsWG * kKB ? sa_blk[i] * kDwStride + rl : kKB * kDwStride;
+  }
+#pragma unroll
+  for (int i = 0; i < kSB; ++i) {
+    const int q = tid + kThreads * i, tl = q >> kLogKB, t = tok0 + tl;
+    sb_blk[i] = q & (kKB - 1);
+    sb_off[i] = (q < kTokWG * kKB && t < T) ? (t * nb + sb_blk[i]) * kQ81Bytes : kOutOfRange;
+    sb_lds[i] = q < kTokWG * kKB ? sb_blk[i] * kDxStride + tl : kKB * kDxStride;
+  }
 
-  uint4 ra, rb[2];
-  uint32_t rsw, rsx;
-  int ls = 0;  // next step to load
-  auto load_next = [&]() {
+  // Two register sets of loaded data: set k & 1 holds step k until staged.
+  uint4 ra[2][kA], rb[2][kB];
+  uint32_t rsa[2][kSA], rsb[2][kSB];
+  auto load = [&](auto set_tag, int step) {
+    constexpr int S = decltype(set_tag)::value;
     // blocks past the end of K read as zeros (offset beyond the buffer)
-    const int kb0 = ls * kKB;
-    const bool a_in = kb0 + a_blk < nb, s_in = kb0 + s_blk < nb, x_in = kb0 + (tid >> 7) < nb;
+    const int kb0 = step * kKB;
     const int sw = __builtin_amdgcn_readfirstlane(kb0 * kQ80Bytes);
     const int sx = __builtin_amdgcn_readfirstlane(kb0 * kQ81Bytes);
-    ra = buf_u128(rw, a_in ? a_off : kOutOfRange, sw);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) rb[j] = buf_u128(rx, kb0 + ((tid + kThreads * j) >> 8) < nb ? b_off[j] : kOutOfRange, sx);
-    rsw = buf_u16(rw, s_in ? sw_off : kOutOfRange, sw);
-    rsx = buf_u16(rx, x_in ? sx_off : kOutOfRange, sx);
-    ++ls;
+    for (int i = 0; i < kA; ++i) ra[S][i] = buf_u128(rw, kb0 + a_blk[i] < nb ? a_off[i] : kOutOfRange, sw);
+#pragma unroll
+    for (int j = 0; j < kB; ++j) rb[S][j] = buf_u128(rx, kb0 + b_blk[j] < nb ? b_off[j] : kOutOfRange, sx);
+#pragma unroll
+    for (int i = 0; i < kSA; ++i) rsa[S][i] = buf_u16(rw, kb0 + sa_blk[i] < nb ? sa_off[i] : kOutOfRange, sw);
+#pragma unroll
+    for (int i = 0; i < kSB; ++i) rsb[S][i] = buf_u16(rx, kb0 + sb_blk[i] < nb ? sb_off[i] : kOutOfRange, sx);
   };
-  auto stage = [&](int buf) {
-    reinterpret_cast<uint4*>(&sm.a[buf][0][0][0][0])[tid] = ra;
+  auto stage = [&](auto set_tag, int buf) {
+    constexpr int S = decltype(set_tag)::value;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) reinterpret_cast<uint4*>(&sm.b[buf][0][0][0][0])[tid + kThreads * j] = rb[j];
-    if (tid < kRowsWG * kKB) (&sm.dw[buf][0][0])[tid] = half_bits_to_float(rsw);
-    (&sm.dx[buf][0][0])[tid] = half_bits_to_float(rsx);
+    for (int i = 0; i < kA; ++i) *reinterpret_cast<uint4*>(sm.a[buf] + a_lds[i]) = ra[S][i];
+#pragma unroll
+    for (int j = 0; j < kB; ++j) *reinterpret_cast<uint4*>(sm.b[buf] + b_lds[j]) = rb[S][j];
+    // no branches here (see the pipeline below): spare tasks store to a spare word
+#pragma unroll
+    for (int i = 0; i < kSA; ++i) sm.dw[buf][sa_lds[i]] = half_bits_to_float(rsa[S][i]);
+#pragma unroll
+    for (int i = 0; i < kSB; ++i) sm.dx[buf][sb_lds[i]] = half_bits_to_float(rsb[S][i]);
   };
 
   // ---- consumer state ----
@@ -139,18 +188,19 @@ __global__ __launch_bounds__(kThreads) void k_dense_q8_0(const uint8_t* __restri
     for (int kb = 0; kb < kKB; ++kb) {
       const int blk = step * kKB + kb;
       if (blk >= nb) break;
-      const v4i va = *reinterpret_cast<const v4i*>(&sm.a[buf][kb][kh][32 * wr + col][0]);
-      const v4i vb0 = *reinterpret_cast<const v4i*>(&sm.b[buf][kb][kh][64 * wc + col][0]);
-      const v4i vb1 = *reinterpret_cast<const v4i*>(&sm.b[buf][kb][kh][64 * wc + 32 + col][0]);
+      const v4i va = *reinterpret_cast<const v4i*>(sm.a[buf] + (2 * kb + kh) * kAPlane + 16 * (32 * wr + col));
+      const v4i vb0 = *reinterpret_cast<const v4i*>(sm.b[buf] + (2 * kb + kh) * kBPlane + 16 * (64 * wc + col));
+      const v4i vb1 =
+          *reinterpret_cast<const v4i*>(sm.b[buf] + (2 * kb + kh) * kBPlane + 16 * (64 * wc + 32 + col));
       const v16i r0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(va, vb0, magic, 0, 0, 0);
       const v16i r1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(va, vb1, magic, 0, 0, 0);
-      const float dx0 = sm.dx[buf][kb][64 * wc + col];
-      const float dx1 = sm.dx[buf][kb][64 * wc + 32 + col];
+      const float dx0 = sm.dx[buf][kb * kDxStride + 64 * wc + col];
+      const float dx1 = sm.dx[buf][kb * kDxStride + 64 * wc + 32 + col];
       const float m0 = -kMagic * dx0, m1 = -kMagic * dx1;
       float dwv[16];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const float4 d4 = *reinterpret_cast<const float4*>(&sm.dw[buf][kb][32 * wr + 8 * q + 4 * kh]);
+        const float4 d4 = *reinterpret_cast<const float4*>(&sm.dw[buf][kb * kDwStride + 32 * wr + 8 * q + 4 * kh]);
         dwv[4 * q] = d4.x;
         dwv[4 * q + 1] = d4.y;
         dwv[4 * q + 2] = d4.z;
@@ -180,15 +230,31 @@ __global__ __launch_bounds__(kThreads) void k_dense_q8_0(const uint8_t* __restri
     }
   };
 
-  // ---- pipeline: stage g+1, load g+2, compute g, barrier ----
-  load_next();
-  stage(0);
-  if (n_steps > 1) load_next();
+  // ---- pipeline ----
+  // Step g: the MFMAs of step g from LDS buffer g & 1; then step g+1 (register
+  // set (g+1) & 1) is staged into the other buffer and the loads of step g+3
+  // go into the freed set; barrier.  Loads are in flight for two steps, and
+  // staging comes after the MFMAs so that its wait for the loads (the
+  // compiler's count is conservative on the loop's first half) is mostly
+  // covered.  Loads and stores are issued on every step, also past the last
+  // one (those loads are out of range and return zeros without touching
+  // memory), so no branch blurs the compiler's wait counts.
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  load(S0{}, 0);
+  load(S1{}, 1);
+  stage(S0{}, 0);
+  load(S0{}, 2);
   __syncthreads();
-  for (int g = 0; g < n_steps; ++g) {
-    if (g + 1 < n_steps) stage((g + 1) & 1);
-    if (g + 2 < n_steps) load_next();
-    compute(g & 1, g);
+  for (int g = 0; g < n_steps; g += 2) {
+    compute(0, g);
+    stage(S1{}, 1);
+    load(S1{}, g + 3);
+    __syncthreads();
+    if (g + 1 >= n_steps) break;
+    compute(1, g + 1);
+    stage(S0{}, 0);
+    load(S0{}, g + 4);
     __syncthreads();
   }
 
@@ -236,10 +302,163 @@ __global__ __launch_bounds__(kThreads) void k_dense_q8_0(const uint8_t* __restri
   }
 }
 
+// ------------------------------------------------------------------------
+// Decode-sized batches.
+// ------------------------------------------------------------------------
+constexpr int kSmallTok = 8;      // largest batch of the GEMV-shaped kernel
+constexpr int kSmallRows = 32;    // output rows per workgroup (one q8_1 block)
+constexpr int kSmallThreads = 256;
+
+// Sum over the LPR lanes of each aligned lane group (LPR a power of two <= 64).
+template <int LPR>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int m = 1; m < LPR; m <<= 1) v += __shfl_xor(v, m);
+  return v;
+}
+
+// BPL: blocks per lane and row (the row's K/32 blocks are dealt to LPR lanes
+// round-robin); LPR: lanes per row.
+template <int BPL, int LPR, bool PROBE>
+__global__ __launch_bounds__(kSmallThreads) void k_dense_small(const uint8_t* __restrict__ x,
+                                                               const uint8_t* __restrict__ w, int T, int N, int K,
+                                                               float* __restrict__ y_f32, uint8_t* __restrict__ y_q8,
+                                                               ProbeRows probe) {
+  constexpr int kRowsPerIter = 64 / LPR;
+  constexpr int kRowsPerWave = kSmallRows / (kSmallThreads / 64);  // 8
+  static_assert(kRowsPerWave % kRowsPerIter == 0, "rows of a wave come in whole iterations");
+  __shared__ float ys[kSmallTok][kSmallRows];
+  const int nb = K / 32;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int row0 = blockIdx.x * kSmallRows;
+  const int li = lane & (LPR - 1), sub = lane / LPR;  // lane within its row group, row group
+  const rsrc_t rw = make_rsrc(w, (uint32_t)((int64_t)N * nb * kQ80Bytes));
+  const rsrc_t rx = make_rsrc(x, (uint32_t)((int64_t)T * nb * kQ81Bytes));
+
+  // this lane's activation blocks b = li + LPR j of every token, in registers
+  uint32_t xq[kSmallTok][BPL][8];
+  float xd[kSmallTok][BPL];
+#pragma unroll
+  for (int t = 0; t < kSmallTok; ++t)
+#pragma unroll
+    for (int j = 0; j < BPL; ++j) {
+      const int b = li + LPR * j;
+      const int off = (t < T && b < nb) ? (t * nb + b) * kQ81Bytes : kOutOfRange;
+      const uint4 c0 = buf_u128(rx, off, 4), c1 = buf_u128(rx, off, 20);
+      xq[t][j][0] = c0.x; xq[t][j][1] = c0.y; xq[t][j][2] = c0.z; xq[t][j][3] = c0.w;
+      xq[t][j][4] = c1.x; xq[t][j][5] = c1.y; xq[t][j][6] = c1.z; xq[t][j][7] = c1.w;
+      xd[t][j] = half_bits_to_float(buf_u16(rx, off, 0));
+    }
+
+#pragma unroll
+  for (int it = 0; it < kRowsPerWave / kRowsPerIter; ++it) {
+    const int rl = kRowsPerWave * wave + kRowsPerIter * it + sub;  // row within the workgroup
+    const int r = row0 + rl;
+    float part[kSmallTok];
+#pragma unroll
+    for (int t = 0; t < kSmallTok; ++t) part[t] = 0.f;
+#pragma unroll
+    for (int j = 0; j < BPL; ++j) {
+      const int b = li + LPR * j;
+      const int off = (r < N && b < nb) ? (r * nb + b) * kQ80Bytes : kOutOfRange;
+      const uint4 w0 = buf_u128(rw, off, 2), w1 = buf_u128(rw, off, 18);
+      const float dw = half_bits_to_float(buf_u16(rw, off, 0));
+      const uint32_t wq[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+      for (int t = 0; t < kSmallTok; ++t) {
+        if (t >= T) break;
+        int dot = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) dot = __builtin_amdgcn_sdot4((int)wq[k], (int)xq[t][j][k], dot, false);
+        part[t] = __builtin_fmaf(dw, xd[t][j] * (float)dot, part[t]);
+        if (PROBE && r < N && b < nb) {
+          const int pr = r - probe.row0;
+          if (pr >= 0 && pr < probe.rows) probe.out[((int64_t)t * probe.rows + pr) * nb + b] = dot;
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < kSmallTok; ++t) {
+      if (t >= T) break;
+      const float v = group_sum<LPR>(part[t]);
+      if (li == 0) ys[t][rl] = v;
+    }
+  }
+  __syncthreads();
+
+  if (y_f32) {
+    for (int i = tid; i < T * kSmallRows; i += kSmallThreads) {
+      const int t = i / kSmallRows, rl = i - t * kSmallRows;
+      if (row0 + rl < N) y_f32[(int64_t)t * N + row0 + rl] = ys[t][rl];
+    }
+  }
+  if (y_q8 && tid < 64 * ((T + 1) / 2)) {
+    // q8_1 rule over the 32 rows of a token, 32 lanes per token (two tokens a wave)
+#pragma clang fp contract(off)
+    const int t = tid >> 5, i = tid & 31;
+    const float v = ys[t < T ? t : 0][i];
+    float amax = fabsf(v);
+#pragma unroll
+    for (int m = 1; m < 32; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
+    const float d = amax / 127.0f;
+    const float id = d != 0.0f ? 1.0f / d : 0.0f;
+    const int q = round_half_away(v * id);
+    int sum = q;
+#pragma unroll
+    for (int m = 1; m < 32; m <<= 1) sum += __shfl_xor(sum, m);
+    if (t < T) {
+      uint8_t* blk = y_q8 + ((int64_t)t * (N / 32) + row0 / 32) * kQ81Bytes;
+      blk[4 + i] = (uint8_t)(int8_t)q;
+      if (i == 0)
+        *reinterpret_cast<uint32_t*>(blk) =
+            float_to_half_bits(d) | (float_to_half_bits(fp32_barrier(d * (float)sum)) << 16);
+    }
+  }
+}
+
+template <int BPL, int LPR>
+void launch_small(const uint8_t* x, const uint8_t* w, int T, int N, int K, float* y_f32, uint8_t* y_q8,
+                  const ProbeRows* probe, hipStream_t st) {
+  const dim3 grid(N / kSmallRows);
+  const ProbeRows none = {nullptr, 0, 0};
+  if (probe)
+    hipLaunchKernelGGL((k_dense_small<BPL, LPR, true>), grid, dim3(kSmallThreads), 0, st, x, w, T, N, K, y_f32, y_q8,
+                       *probe);
+  else
+    hipLaunchKernelGGL((k_dense_small<BPL, LPR, false>), grid, dim3(kSmallThreads), 0, st, x, w, T, N, K, y_f32,
+                       y_q8, none);
+}
+
+// The GEMV-shaped kernel's configuration for K/32 blocks, or false when the
+// batch or K is too large for it (its activation blocks live in registers).
+bool small_config(int64_t T, int nb, int* bpl, int* lpr) {
+  if (T > kSmallTok) return false;
+  if (nb <= 8) { *lpr = 8; *bpl = 1; return true; }
+  if (nb <= 16) { *lpr = 16; *bpl = 1; return true; }
+  if (nb <= 32) { *lpr = 32; *bpl = 1; return true; }
+  *lpr = 64;
+  if (nb <= 64) { *bpl = 1; return true; }
+  if (nb <= 128) { *bpl = 2; return true; }
+  if (nb <= 256 && T <= kSmallTok / 2) { *bpl = 4; return true; }
+  return false;
+}
+
 }  // namespace
 
 hipError_t launch_dense_q8_0(const uint8_t* x, const uint8_t* w, int64_t T, int N, int K, float* y_f32,
                              uint8_t* y_q8, const ProbeRows* probe, hipStream_t st) {
+  int bpl = 0, lpr = 0;
+  if (small_config(T, K / 32, &bpl, &lpr)) {
+    const int t = (int)T;
+    if (lpr == 8) launch_small<1, 8>(x, w, t, N, K, y_f32, y_q8, probe, st);
+    else if (lpr == 16) launch_small<1, 16>(x, w, t, N, K, y_f32, y_q8, probe, st);
+    else if (lpr == 32) launch_small<1, 32>(x, w, t, N, K, y_f32, y_q8, probe, st);
+    else if (bpl == 1) launch_small<1, 64>(x, w, t, N, K, y_f32, y_q8, probe, st);
+    else if (bpl == 2) launch_small<2, 64>(x, w, t, N, K, y_f32, y_q8, probe, st);
+    else launch_small<4, 64>(x, w, t, N, K, y_f32, y_q8, probe, st);
+    return hipGetLastError();
+  }
   const int n_rt = (N + kRowsWG - 1) / kRowsWG;
   const int n_tt = (int)((T + kTokWG - 1) / kTokWG);
   const int items = n_rt * n_tt;

@@ -105,6 +105,14 @@ SMALL = [
     (4, 1024, 4096, 5),    # decode-sized D
     (4, 4096, 1024, 6),    # decode-sized U
     (300, 160, 1056, 7),   # several tiles, 33 blocks
+    # the GEMV-shaped kernel of batches of at most 8 tokens, each lane layout
+    (5, 32, 96, 8),        # 3 blocks a row: 8 lanes a row
+    (3, 64, 512, 9),       # 16 blocks: 16 lanes a row
+    (8, 96, 2048, 10),     # 64 blocks: 64 lanes, one block each
+    (8, 64, 4096, 11),     # 128 blocks: two a lane
+    (4, 64, 8192, 12),     # 256 blocks: four a lane (batches of at most 4)
+    (7, 32, 1056, 13),     # 33 blocks, a partly idle lane group
+    (9, 64, 256, 14),      # one token more: the MFMA kernel
 ]
 
 
