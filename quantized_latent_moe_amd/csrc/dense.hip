@@ -33,16 +33,19 @@
 // so a fragment read is 1 KiB contiguous.
 //
 // Batches of at most kSmallTok tokens take k_dense_small instead: GEMV
-// shaped, one workgroup per 32 output rows (one q8_1 block of every token's
-// output), the lanes of a wave on consecutive blocks of one row (coalesced
-// weight reads), each lane's activation blocks held in registers for all the
-// rows it visits, integer dots by v_dot4, the fold per block in fp32, a
-// butterfly sum across the lanes of a row, and the q8_1 rounding from LDS.
+// shaped, one workgroup of up to 16 waves per 32 output rows (one q8_1 block
+// of every token's output).  The lanes of a wave take consecutive blocks of
+// one row (coalesced weight reads, issued first into registers), the
+// activation rows are copied into LDS once in contiguous 16-byte chunks,
+// integer dots by v_dot4, the fold per block in fp32, a butterfly sum across
+// the lanes of a row, and the q8_1 rounding from LDS.
 //
 // Work items are dealt XCD-major: workgroup w runs on XCD w % 8 and takes
-// item (w % 8) * ceil(items / 8) + w / 8, items ordered token tile major,
-// so each XCD's L2 holds one contiguous range of activation rows and the
-// weight rows it sweeps over.
+// item (w % 8) * ceil(items / 8) + w / 8 of an order that sweeps groups of
+// kGroupRows row tiles over every token tile, so an XCD works through a
+// contiguous stretch of that order and its L2 keeps the group's weight rows
+// (when all of W exceeds an XCD's 4 MiB L2, the plain token-major order
+// streams W from memory again for every token tile).
 #include <type_traits>
 
 #include "lat_moe_internal.h"
@@ -57,6 +60,7 @@ constexpr int kLogKB = 2;
 constexpr int kKB = 1 << kLogKB;  // 32-value blocks per K step
 constexpr int kQ80Bytes = 34;
 constexpr int kXcds = 8;
+constexpr int kGroupRows = 16;  // row tiles of one sweep over the token tiles (their weights stay in L2)
 // LDS slots of 16 bytes: (block, half) planes of rows/tokens, each plane
 // padded by 16 bytes so that the lanes of a load instruction, which walk the
 // (block, half) planes of one row, write to different banks.
@@ -76,14 +80,19 @@ static_assert(kRowsWG == 64 && kTokWG == 128 && kThreads == 256 && kKB >= 2,
 
 template <bool PROBE>
 __global__ __launch_bounds__(kThreads) void k_dense_q8_0(const uint8_t* __restrict__ x, const uint8_t* __restrict__ w,
-                                                         int T, int N, int K, int n_rt, int items, int per_xcd,
+                                                         int T, int N, int K, int n_rt, int n_tt, int items,
+                                                         int per_xcd,
                                                          float* __restrict__ y_f32, uint8_t* __restrict__ y_q8,
                                                          ProbeRows probe) {
   __shared__ __align__(16) Smem sm;
   const int wg = blockIdx.x;
   const int item = (wg % kXcds) * per_xcd + wg / kXcds;
   if (item >= items) return;
-  const int tt = item / n_rt, rt = item - tt * n_rt;
+  // grouped order: kGroupRows row tiles at a time, swept over every token tile
+  const int group = item / (kGroupRows * n_tt);
+  const int within = item - group * kGroupRows * n_tt;
+  const int g_rows = min(kGroupRows, n_rt - group * kGroupRows);
+  const int tt = within / g_rows, rt = group * kGroupRows + (within - (within / g_rows) * g_rows);
   const int row0 = rt * kRowsWG, tok0 = tt * kTokWG;
   const int nb = K / 32;
   const int n_steps = (nb + kKB - 1) / kKB;
@@ -307,7 +316,20 @@ __global__ __launch_bounds__(kThreads) void k_dense_q8_0(const uint8_t* __restri
 // ------------------------------------------------------------------------
 constexpr int kSmallTok = 8;      // largest batch of the GEMV-shaped kernel
 constexpr int kSmallRows = 32;    // output rows per workgroup (one q8_1 block)
-constexpr int kSmallThreads = 256;
+// Waves of a workgroup for LPR lanes per row: enough that each wave has one or
+// two rows (many loads in flight per CU: these few workgroups are latency
+// bound), at most 16.
+constexpr int small_waves(int lpr) { return 64 / lpr * 16 <= kSmallRows ? 16 : kSmallRows / (64 / lpr); }
+
+// 16 bytes from LDS at a 4-byte-aligned address (one ds_read_b128: gfx950
+// serves unaligned LDS accesses).
+__device__ __forceinline__ uint4 lds_u128_a4(const uint8_t* p) {
+  struct __attribute__((packed, aligned(4))) U {
+    uint32_t a, b, c, d;
+  };
+  const U v = *reinterpret_cast<const U*>(p);
+  return uint4{v.a, v.b, v.c, v.d};
+}
 
 // Sum over the LPR lanes of each aligned lane group (LPR a power of two <= 64).
 template <int LPR>
@@ -320,14 +342,17 @@ __device__ __forceinline__ float group_sum(float v) {
 // BPL: blocks per lane and row (the row's K/32 blocks are dealt to LPR lanes
 // round-robin); LPR: lanes per row.
 template <int BPL, int LPR, bool PROBE>
-__global__ __launch_bounds__(kSmallThreads) void k_dense_small(const uint8_t* __restrict__ x,
+__global__ __launch_bounds__(64 * small_waves(LPR)) void k_dense_small(const uint8_t* __restrict__ x,
                                                                const uint8_t* __restrict__ w, int T, int N, int K,
                                                                float* __restrict__ y_f32, uint8_t* __restrict__ y_q8,
                                                                ProbeRows probe) {
+  constexpr int kSmallThreads = 64 * small_waves(LPR);
   constexpr int kRowsPerIter = 64 / LPR;
-  constexpr int kRowsPerWave = kSmallRows / (kSmallThreads / 64);  // 8
-  static_assert(kRowsPerWave % kRowsPerIter == 0, "rows of a wave come in whole iterations");
+  constexpr int kRowsPerWave = kSmallRows / small_waves(LPR);
+  static_assert(kRowsPerWave % kRowsPerIter == 0 && kRowsPerWave >= kRowsPerIter,
+                "rows of a wave come in whole iterations");
   __shared__ float ys[kSmallTok][kSmallRows];
+  extern __shared__ __align__(16) uint8_t xraw[];  // the T activation rows as they are in memory (+16)
   const int nb = K / 32;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -336,23 +361,52 @@ __global__ __launch_bounds__(kSmallThreads) void k_dense_small(const uint8_t* __
   const rsrc_t rw = make_rsrc(w, (uint32_t)((int64_t)N * nb * kQ80Bytes));
   const rsrc_t rx = make_rsrc(x, (uint32_t)((int64_t)T * nb * kQ81Bytes));
 
-  // this lane's activation blocks b = li + LPR j of every token, in registers
-  uint32_t xq[kSmallTok][BPL][8];
-  float xd[kSmallTok][BPL];
+  // This wave's weight blocks (row of iteration it, block li + LPR j) into
+  // registers first, so their latency overlaps the activation staging below.
+  constexpr int kIters = kRowsPerWave / kRowsPerIter;
+  uint32_t wq[kIters][BPL][8];
+  float wd[kIters][BPL];
 #pragma unroll
-  for (int t = 0; t < kSmallTok; ++t)
+  for (int it = 0; it < kIters; ++it) {
+    const int r = row0 + kRowsPerWave * wave + kRowsPerIter * it + sub;
 #pragma unroll
     for (int j = 0; j < BPL; ++j) {
       const int b = li + LPR * j;
-      const int off = (t < T && b < nb) ? (t * nb + b) * kQ81Bytes : kOutOfRange;
-      const uint4 c0 = buf_u128(rx, off, 4), c1 = buf_u128(rx, off, 20);
-      xq[t][j][0] = c0.x; xq[t][j][1] = c0.y; xq[t][j][2] = c0.z; xq[t][j][3] = c0.w;
-      xq[t][j][4] = c1.x; xq[t][j][5] = c1.y; xq[t][j][6] = c1.z; xq[t][j][7] = c1.w;
-      xd[t][j] = half_bits_to_float(buf_u16(rx, off, 0));
+      const int off = (r < N && b < nb) ? (r * nb + b) * kQ80Bytes : kOutOfRange;
+      const uint4 w0 = buf_u128(rw, off, 2), w1 = buf_u128(rw, off, 18);
+      wq[it][j][0] = w0.x; wq[it][j][1] = w0.y; wq[it][j][2] = w0.z; wq[it][j][3] = w0.w;
+      wq[it][j][4] = w1.x; wq[it][j][5] = w1.y; wq[it][j][6] = w1.z; wq[it][j][7] = w1.w;
+      wd[it][j] = half_bits_to_float(buf_u16(rw, off, 0));
     }
+  }
+
+  // The activation rows ([T][K/32] q8_1 blocks, contiguous) into LDS once, in
+  // consecutive 16-byte chunks.
+  {
+    const int xbytes = T * nb * kQ81Bytes;  // a multiple of 4
+    const int full = xbytes / 16, tail = (xbytes - 16 * full) / 4;
+    for (int c = tid; c < full; c += kSmallThreads) reinterpret_cast<uint4*>(xraw)[c] = buf_u128(rx, 16 * c, 0);
+    if (tid < tail) reinterpret_cast<uint32_t*>(xraw)[4 * full + tid] = buf_u32(rx, 16 * full + 4 * tid, 0);
+  }
+  __syncthreads();
+  uint32_t xq[kSmallTok][BPL][8];
+  float xd[kSmallTok][BPL];
+#pragma unroll
+  for (int t = 0; t < kSmallTok; ++t) {
+    if (t >= T) break;
+#pragma unroll
+    for (int j = 0; j < BPL; ++j) {
+      const int b = min(li + LPR * j, nb - 1);  // lanes past the row's last block compute unused values
+      const uint8_t* src = xraw + (t * nb + b) * kQ81Bytes;
+      xd[t][j] = half_bits_to_float(*reinterpret_cast<const uint16_t*>(src));
+      const uint32_t* cw = reinterpret_cast<const uint32_t*>(src + 4);  // 4-byte aligned
+#pragma unroll
+      for (int k = 0; k < 8; ++k) xq[t][j][k] = cw[k];
+    }
+  }
 
 #pragma unroll
-  for (int it = 0; it < kRowsPerWave / kRowsPerIter; ++it) {
+  for (int it = 0; it < kIters; ++it) {
     const int rl = kRowsPerWave * wave + kRowsPerIter * it + sub;  // row within the workgroup
     const int r = row0 + rl;
     float part[kSmallTok];
@@ -361,17 +415,20 @@ __global__ __launch_bounds__(kSmallThreads) void k_dense_small(const uint8_t* __
 #pragma unroll
     for (int j = 0; j < BPL; ++j) {
       const int b = li + LPR * j;
-      const int off = (r < N && b < nb) ? (r * nb + b) * kQ80Bytes : kOutOfRange;
-      const uint4 w0 = buf_u128(rw, off, 2), w1 = buf_u128(rw, off, 18);
-      const float dw = half_bits_to_float(buf_u16(rw, off, 0));
-      const uint32_t wq[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+      // activation block (t, b) from LDS; lanes past the row's last block read
+      // block nb - 1 and multiply it by zeros
+      const uint8_t* xb = xraw + min(b, nb - 1) * kQ81Bytes;
 #pragma unroll
       for (int t = 0; t < kSmallTok; ++t) {
         if (t >= T) break;
+        const uint8_t* src = xb + t * nb * kQ81Bytes;
+        const uint4 c0 = lds_u128_a4(src + 4), c1 = lds_u128_a4(src + 20);
+        const float xdv = half_bits_to_float(*reinterpret_cast<const uint16_t*>(src));
+        const uint32_t xw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
         int dot = 0;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) dot = __builtin_amdgcn_sdot4((int)wq[k], (int)xq[t][j][k], dot, false);
-        part[t] = __builtin_fmaf(dw, xd[t][j] * (float)dot, part[t]);
+        for (int k = 0; k < 8; ++k) dot = __builtin_amdgcn_sdot4((int)wq[it][j][k], (int)xw[k], dot, false);
+        part[t] = __builtin_fmaf(wd[it][j], xdv * (float)dot, part[t]);
         if (PROBE && r < N && b < nb) {
           const int pr = r - probe.row0;
           if (pr >= 0 && pr < probe.rows) probe.out[((int64_t)t * probe.rows + pr) * nb + b] = dot;
@@ -421,13 +478,14 @@ template <int BPL, int LPR>
 void launch_small(const uint8_t* x, const uint8_t* w, int T, int N, int K, float* y_f32, uint8_t* y_q8,
                   const ProbeRows* probe, hipStream_t st) {
   const dim3 grid(N / kSmallRows);
+  const size_t lds = (size_t)T * (K / 32) * kQ81Bytes + 16;
   const ProbeRows none = {nullptr, 0, 0};
   if (probe)
-    hipLaunchKernelGGL((k_dense_small<BPL, LPR, true>), grid, dim3(kSmallThreads), 0, st, x, w, T, N, K, y_f32, y_q8,
-                       *probe);
+    hipLaunchKernelGGL((k_dense_small<BPL, LPR, true>), grid, dim3(64 * small_waves(LPR)), lds, st, x, w, T, N, K,
+                       y_f32, y_q8, *probe);
   else
-    hipLaunchKernelGGL((k_dense_small<BPL, LPR, false>), grid, dim3(kSmallThreads), 0, st, x, w, T, N, K, y_f32,
-                       y_q8, none);
+    hipLaunchKernelGGL((k_dense_small<BPL, LPR, false>), grid, dim3(64 * small_waves(LPR)), lds, st, x, w, T, N, K,
+                       y_f32, y_q8, none);
 }
 
 // The GEMV-shaped kernel's configuration for K/32 blocks, or false when the
@@ -466,11 +524,11 @@ hipError_t launch_dense_q8_0(const uint8_t* x, const uint8_t* w, int64_t T, int 
   const dim3 grid(per_xcd * kXcds);
   const ProbeRows none = {nullptr, 0, 0};
   if (probe)
-    hipLaunchKernelGGL(k_dense_q8_0<true>, grid, dim3(kThreads), 0, st, x, w, (int)T, N, K, n_rt, items, per_xcd,
-                       y_f32, y_q8, *probe);
+    hipLaunchKernelGGL(k_dense_q8_0<true>, grid, dim3(kThreads), 0, st, x, w, (int)T, N, K, n_rt, n_tt, items,
+                       per_xcd, y_f32, y_q8, *probe);
   else
-    hipLaunchKernelGGL(k_dense_q8_0<false>, grid, dim3(kThreads), 0, st, x, w, (int)T, N, K, n_rt, items, per_xcd,
-                       y_f32, y_q8, none);
+    hipLaunchKernelGGL(k_dense_q8_0<false>, grid, dim3(kThreads), 0, st, x, w, (int)T, N, K, n_rt, n_tt, items,
+                       per_xcd, y_f32, y_q8, none);
   return hipGetLastError();
 }
 
