@@ -42,10 +42,10 @@
 //
 // Work items are dealt XCD-major: workgroup w runs on XCD w % 8 and takes
 // item (w % 8) * ceil(items / 8) + w / 8 of an order that sweeps groups of
-// kGroupRows row tiles over every token tile, so an XCD works through a
-// contiguous stretch of that order and its L2 keeps the group's weight rows
-// (when all of W exceeds an XCD's 4 MiB L2, the plain token-major order
-// streams W from memory again for every token tile).
+// row tiles (about kGroupBytes of weights) over every token tile, so an XCD
+// works through a contiguous stretch of that order and its L2 keeps the
+// group's weight rows (when all of W exceeds an XCD's 4 MiB L2, the plain
+// token-major order streams W from memory again for every token tile).
 #include <type_traits>
 
 #include "lat_moe_internal.h"
@@ -60,7 +60,7 @@ constexpr int kLogKB = 2;
 constexpr int kKB = 1 << kLogKB;  // 32-value blocks per K step
 constexpr int kQ80Bytes = 34;
 constexpr int kXcds = 8;
-constexpr int kGroupRows = 16;  // row tiles of one sweep over the token tiles (their weights stay in L2)
+constexpr int kGroupBytes = 2 << 20;  // weight bytes of the row tiles of one sweep over the token tiles
 // LDS slots of 16 bytes: (block, half) planes of rows/tokens, each plane
 // padded by 16 bytes so that the lanes of a load instruction, which walk the
 // (block, half) planes of one row, write to different banks.
@@ -80,19 +80,19 @@ static_assert(kRowsWG == 64 && kTokWG == 128 && kThreads == 256 && kKB >= 2,
 
 template <bool PROBE>
 __global__ __launch_bounds__(kThreads) void k_dense_q8_0(const uint8_t* __restrict__ x, const uint8_t* __restrict__ w,
-                                                         int T, int N, int K, int n_rt, int n_tt, int items,
-                                                         int per_xcd,
+                                                         int T, int N, int K, int n_rt, int n_tt, int group_rows,
+                                                         int items, int per_xcd,
                                                          float* __restrict__ y_f32, uint8_t* __restrict__ y_q8,
                                                          ProbeRows probe) {
   __shared__ __align__(16) Smem sm;
   const int wg = blockIdx.x;
   const int item = (wg % kXcds) * per_xcd + wg / kXcds;
   if (item >= items) return;
-  // grouped order: kGroupRows row tiles at a time, swept over every token tile
-  const int group = item / (kGroupRows * n_tt);
-  const int within = item - group * kGroupRows * n_tt;
-  const int g_rows = min(kGroupRows, n_rt - group * kGroupRows);
-  const int tt = within / g_rows, rt = group * kGroupRows + (within - (within / g_rows) * g_rows);
+  // grouped order: group_rows row tiles at a time, swept over every token tile
+  const int group = item / (group_rows * n_tt);
+  const int within = item - group * group_rows * n_tt;
+  const int g_rows = min(group_rows, n_rt - group * group_rows);
+  const int tt = within / g_rows, rt = group * group_rows + (within - (within / g_rows) * g_rows);
   const int row0 = rt * kRowsWG, tok0 = tt * kTokWG;
   const int nb = K / 32;
   const int n_steps = (nb + kKB - 1) / kKB;
@@ -520,15 +520,16 @@ hipError_t launch_dense_q8_0(const uint8_t* x, const uint8_t* w, int64_t T, int 
   const int n_rt = (N + kRowsWG - 1) / kRowsWG;
   const int n_tt = (int)((T + kTokWG - 1) / kTokWG);
   const int items = n_rt * n_tt;
+  const int group_rows = max(1, min(n_rt, (int)(kGroupBytes / ((int64_t)kRowsWG * (K / 32) * kQ80Bytes))));
   const int per_xcd = (items + kXcds - 1) / kXcds;
   const dim3 grid(per_xcd * kXcds);
   const ProbeRows none = {nullptr, 0, 0};
   if (probe)
-    hipLaunchKernelGGL(k_dense_q8_0<true>, grid, dim3(kThreads), 0, st, x, w, (int)T, N, K, n_rt, n_tt, items,
-                       per_xcd, y_f32, y_q8, *probe);
+    hipLaunchKernelGGL(k_dense_q8_0<true>, grid, dim3(kThreads), 0, st, x, w, (int)T, N, K, n_rt, n_tt, group_rows,
+                       items, per_xcd, y_f32, y_q8, *probe);
   else
-    hipLaunchKernelGGL(k_dense_q8_0<false>, grid, dim3(kThreads), 0, st, x, w, (int)T, N, K, n_rt, n_tt, items,
-                       per_xcd, y_f32, y_q8, none);
+    hipLaunchKernelGGL(k_dense_q8_0<false>, grid, dim3(kThreads), 0, st, x, w, (int)T, N, K, n_rt, n_tt, group_rows,
+                       items, per_xcd, y_f32, y_q8, none);
   return hipGetLastError();
 }
 
