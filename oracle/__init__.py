@@ -59,6 +59,7 @@ def lib() -> ctypes.CDLL:
         c.orc_dequant_q8_0.argtypes = [P, i64, P]
         c.orc_dense_q8_0.argtypes = [P, i64, P, i32, i32, P, i64, P]
         c.orc_probe_dense.argtypes = [P, i64, P, i32, i32, i64, P, P, P]
+        c.orc_router_topk.argtypes = [P, i64, i32, i32, P, P]
         c.orc_num_threads.restype = ctypes.c_int
         c.orc_set_num_threads.argtypes = [ctypes.c_int]
     return _lib
@@ -239,3 +240,14 @@ def probe_dense(x_q8, w_q8_0, N, K, tokens, rows):
     out = np.zeros((tok.size, K // 32), np.int32)
     lib().orc_probe_dense(_p(x), T, _p(_c(w_q8_0, np.uint8)), N, K, tok.size, _p(tok), _p(rows), _p(out))
     return out
+
+
+def router_topk(logits: np.ndarray, k: int):
+    """fp32 logits [T, E] -> (ids int32 [T, k], weights fp32 [T, k]): softmax,
+    top-k (ties to the lower expert), weights renormalised over the picks."""
+    l = _c(logits, np.float32)
+    T, E = l.shape
+    idx = np.zeros((T, k), np.int32)
+    w = np.zeros((T, k), np.float32)
+    lib().orc_router_topk(_p(l), T, E, k, _p(idx), _p(w))
+    return idx, w

@@ -553,6 +553,55 @@ void orc_probe_dense(const uint8_t* x_q8, int64_t T, const uint8_t* w, int N, in
   }
 }
 
+/* ------------------------------------------------------------------------ */
+/* Router: softmax over the experts, top-k, renormalised weights             */
+/* ------------------------------------------------------------------------ */
+
+/* Source: page "Run Edge0-145B Q3_K on AMD HIP (Linux, gfx1100) #1", section
+ * "Contents" and the HIP backend page (the MoE router picks the top experts of
+ * each token and the stage combines their outputs with the router's weights);
+ * the task's workloads state the rule: softmax over E, top-k, renormalised.
+ *
+ * For each token t:  p_e = exp(l_e - max l) / sum_e' exp(l_e' - max l)  (fp64);
+ * the k experts of largest p, taken in descending order, equal probabilities
+ * (equal logits) in ascending expert order; w_j = p_(j) / sum_i p_(i) over the
+ * k picks (fp64), stored as fp32.  The ranking is made on the logits: softmax
+ * is strictly increasing in the logit, and ranking the logits keeps that order
+ * where fp64 exp would round distinct tiny probabilities to the same value.
+ * A row needs at least one finite logit; -inf logits (masked experts) have
+ * p = 0 and are picked only when fewer than k logits are finite. */
+void orc_router_topk(const float* logits, int64_t T, int E, int k, int32_t* idx, float* w) {
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) {
+    const float* l = logits + t * E;
+    double mx = -INFINITY;
+    for (int e = 0; e < E; ++e)
+      if ((double)l[e] > mx) mx = (double)l[e];
+    double* p = (double*)malloc(sizeof(double) * E);
+    unsigned char* taken = (unsigned char*)calloc(E, 1);
+    double den = 0.0;
+    for (int e = 0; e < E; ++e) {
+      p[e] = exp((double)l[e] - mx);
+      den += p[e];
+    }
+    for (int e = 0; e < E; ++e) p[e] /= den;
+    double sel = 0.0;
+    for (int j = 0; j < k; ++j) {
+      int best = -1;
+      for (int e = 0; e < E; ++e) {
+        if (taken[e]) continue;
+        if (best < 0 || l[e] > l[best]) best = e; /* strict: ties keep the lower index */
+      }
+      taken[best] = 1;
+      idx[t * k + j] = best;
+      sel += p[best];
+    }
+    for (int j = 0; j < k; ++j) w[t * k + j] = (float)(p[idx[t * k + j]] / sel);
+    free(p);
+    free(taken);
+  }
+}
+
 int orc_num_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();
