@@ -98,6 +98,56 @@ class Stage:
         wall = (time.perf_counter() - t0) * 1e3 / steps
         return e0.elapsed_time(e1) / steps, wall
 
+    def router_and_graph(self, steps):
+        """µs of the router alone, and µs per step of router + stage replayed
+        from one captured graph (each replay checked against the eager step)."""
+        torch, lm, wl = self.torch, self.lm, self.wl
+        logits = torch.from_numpy(self.inputs.router_logits).cuda()
+        idx = torch.empty((wl.T, wl.k), dtype=torch.int32, device="cuda")
+        w = torch.empty((wl.T, wl.k), dtype=torch.float32, device="cuda")
+        route = lambda: lm.router_topk(logits, wl.k, idx, w)
+
+        def step():
+            route()
+            lm.expert_forward(self.x, idx, w, self.gu, self.dn, self.s, self.y, self.ws)
+
+        for _ in range(3):
+            step()
+        torch.cuda.synchronize()
+        ref = self.y.clone()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g_route, g_step = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_route):
+            for _ in range(10):
+                route()
+        with torch.cuda.graph(g_step):
+            step()
+        for _ in range(2):
+            self.y.zero_()
+            g_step.replay()
+            torch.cuda.synchronize()
+            if not torch.equal(self.y, ref):
+                raise RuntimeError("graph replay of router + stage differs from the eager step")
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = max(steps // 10, 2)
+        e0.record()
+        for _ in range(reps):
+            g_route.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        router_us = e0.elapsed_time(e1) * 1e3 / (10 * reps)
+        e0.record()
+        for _ in range(steps):
+            g_step.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return router_us, e0.elapsed_time(e1) * 1e3 / steps
+
     def stage_times(self, steps):
         """Mean ms of route / gate-up / down / combine over `steps` calls."""
         torch = self.torch
@@ -380,6 +430,7 @@ def main():
     ms, wall_ms = st.time_steps(args.steps, args.warmup)
     print(f"[bench] {ms:.4f} ms/step (events), {wall_ms:.4f} ms/step (host clock)", file=sys.stderr, flush=True)
     stages = st.stage_times(args.steps)
+    router_us, _ = st.router_and_graph(args.steps)
     names = ["route", "gateup", "down", "combine"]
     print("[bench] stage ms: " + ", ".join(f"{n}={v:.4f}" for n, v in zip(names, stages)), file=sys.stderr,
           flush=True)
@@ -416,6 +467,7 @@ def main():
                    "active_experts": alg["active"]},
         "roofline": roofline,
         "stage_ms": {n: round(v, 5) for n, v in zip(names, stages)},
+        "router_us": round(router_us, 2),
         "stage_int8_frac": round(total_ops / (ms * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4),
         "stage_hbm_gbs": round(alg["bytes"] / (ms * 1e-3) / 1e9, 1),
     }
@@ -428,10 +480,15 @@ def main():
         dms, _ = ds.time_steps(max(args.steps, 50), args.warmup)
         dstage = ds.stage_times(max(args.steps, 50))
         gbs = dalg["bytes"] / (dms * 1e-3) / 1e9
+        r_us, g_us = ds.router_and_graph(max(args.steps, 50))
         out["decode"] = {"workload": dwl.name, "us_per_step": round(dms * 1e3, 2),
                          "alg_bytes": dalg["bytes"], "hbm_gbs": round(gbs, 1),
                          "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
-                         "stage_us": {n: round(v * 1e3, 2) for n, v in zip(names, dstage)}}
+                         "stage_us": {n: round(v * 1e3, 2) for n, v in zip(names, dstage)},
+                         "router_us": round(r_us, 2),
+                         "router_and_stage_graph_us_per_step": round(g_us, 2)}
+        print(f"[bench] decode router {r_us:.2f} us, router + stage from one graph {g_us:.2f} us/step",
+              file=sys.stderr, flush=True)
         print(f"[bench] decode {dms * 1e3:.2f} us/step, {gbs:.0f} GB/s", file=sys.stderr, flush=True)
         del ds
     if not args.no_du:

@@ -51,6 +51,8 @@ extern "C" {
 #define LAT_MOE_ELAUNCH 4    /* a kernel launch failed (hipGetLastError after enqueue) */
 
 #define LAT_MOE_MAX_E 1024
+#define LAT_MOE_ROUTER_MAX_E 1024 /* experts the router takes */
+#define LAT_MOE_ROUTER_MAX_K 64   /* picks per token the router takes */
 
 /* Shapes of one call.  Supported: T >= 0, T * k < 2^31, L % 256 == 0
  * (256 <= L <= 65536), F % 32 == 0 (32 <= F <= 65536), 1 <= E <= 1024,
@@ -148,6 +150,23 @@ int lat_moe_dense_q8_0(const void* x_q8_1, const void* w_q8_0, int64_t T, int32_
 int lat_moe_dense_q8_0_debug(const void* x_q8_1, const void* w_q8_0, int64_t T, int32_t N, int32_t K,
                              float* y_f32, void* y_q8_1, void* stream, int32_t* dots_i32, int32_t row0,
                              int32_t rows);
+
+/* Router (page "Run Edge0-145B Q3_K on AMD HIP (Linux, gfx1100) #1", section
+ * "Contents", and the HIP backend page: each token's top experts and the
+ * weights the stage combines their outputs with): softmax of each token's
+ * logits over the E experts, the k largest probabilities in descending order
+ * (equal logits: ascending expert id), the k probabilities renormalised to
+ * sum to one.  Computed as the softmax of the k picked logits (the full
+ * denominator cancels; softmax ranks as the logits do), in fp32.
+ *   logits      [T][E] fp32; every row needs a finite maximum; -inf marks an
+ *               expert no token may prefer (picked only when fewer than k
+ *               logits of the row are finite, then with weight 0); NaN is
+ *               not supported
+ *   router_idx  [T][k] int32 out, router_w [T][k] fp32 out: the stage's inputs
+ * Supported: T >= 0, 1 <= E <= LAT_MOE_ROUTER_MAX_E, 1 <= k <= min(E,
+ * LAT_MOE_ROUTER_MAX_K); pointers 16-byte aligned.  T = 0 enqueues nothing. */
+int lat_moe_router_topk(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* router_idx, float* router_w,
+                        void* stream);
 
 /* Static description of an error code. */
 const char* lat_moe_strerror(int code);

@@ -24,6 +24,7 @@ EXPORTED = (
     "lat_moe_quantize_q8_1",
     "lat_moe_dense_q8_0",
     "lat_moe_dense_q8_0_debug",
+    "lat_moe_router_topk",
     "lat_moe_strerror",
     "lat_moe_version",
 )
@@ -80,6 +81,8 @@ def lib() -> ctypes.CDLL:
         c.lat_moe_dense_q8_0.restype = ctypes.c_int
         c.lat_moe_dense_q8_0_debug.argtypes = [P, P, i64, i32, i32, P, P, P, P, i32, i32]
         c.lat_moe_dense_q8_0_debug.restype = ctypes.c_int
+        c.lat_moe_router_topk.argtypes = [P, i64, i32, i32, P, P, P]
+        c.lat_moe_router_topk.restype = ctypes.c_int
         c.lat_moe_strerror.argtypes = [ctypes.c_int]
         c.lat_moe_strerror.restype = ctypes.c_char_p
         c.lat_moe_version.restype = ctypes.c_int
@@ -162,6 +165,14 @@ def dense_q8_0(x_q8_1, w_q8_0, T: int, N: int, K: int, y_f32=None, y_q8_1=None, 
     rows = 0 if dots_i32 is None else int(dots_i32.shape[1])
     _check(lib().lat_moe_dense_q8_0_debug(_ptr(x_q8_1), _ptr(w_q8_0), int(T), int(N), int(K), _ptr(y_f32),
                                           _ptr(y_q8_1), _stream(stream), _ptr(dots_i32), int(row0), rows))
+
+
+def router_topk(logits, k: int, router_idx, router_w, stream=None) -> None:
+    """fp32 logits [T, E] -> top-k expert ids (int32 [T, k]) and renormalised
+    softmax weights (fp32 [T, k]), the expert stage's routing inputs."""
+    T, E = logits.shape
+    _check(lib().lat_moe_router_topk(_ptr(logits), int(T), int(E), int(k), _ptr(router_idx), _ptr(router_w),
+                                     _stream(stream)))
 
 
 def version() -> int:

@@ -220,6 +220,20 @@ int lat_moe_dense_q8_0(const void* x_q8_1, const void* w_q8_0, int64_t T, int32_
   return lat_moe_dense_q8_0_debug(x_q8_1, w_q8_0, T, N, K, y_f32, y_q8_1, stream, nullptr, 0, 0);
 }
 
+int lat_moe_router_topk(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* router_idx, float* router_w,
+                        void* stream) {
+  if (T < 0 || E < 1 || E > LAT_MOE_ROUTER_MAX_E || k < 1 || k > E || k > LAT_MOE_ROUTER_MAX_K) return LAT_MOE_EINVAL;
+  if (T == 0) return LAT_MOE_OK;
+  const void* ptrs[] = {logits, router_idx, router_w};
+  for (const void* p : ptrs)
+    if (!p || !aligned16(p)) return LAT_MOE_EINVAL;
+  int rc = check_device(nullptr);
+  if (rc != LAT_MOE_OK) return rc;
+  if (launch_router_topk(logits, T, E, k, router_idx, router_w, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return LAT_MOE_ELAUNCH;
+  return LAT_MOE_OK;
+}
+
 const char* lat_moe_strerror(int code) {
   switch (code) {
     case LAT_MOE_OK: return "ok";

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/lat_moe.h"
+
 namespace latmoe {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -175,6 +177,8 @@ hipError_t launch_combine(const int32_t* idx, const Shapes& s, const Work& w, fl
 hipError_t launch_quantize_q8_1(const float* x, int64_t rows, int cols, uint8_t* out, hipStream_t st);
 hipError_t launch_export_h(const Shapes& s, const Work& w, uint8_t* h_out, hipStream_t st);
 hipError_t launch_copy_i32(const int32_t* src, int32_t* dst, int64_t n, hipStream_t st);
+// Router: fp32 logits [T][E] -> top-k ids and renormalised softmax weights.
+hipError_t launch_router_topk(const float* logits, int64_t T, int E, int k, int32_t* idx, float* w, hipStream_t st);
 // Latent D / U dense projection, Q8_0 weights [N][K/32] x q8_1 rows [T][K/32]
 // -> fp32 [T][N] and/or q8_1 [T][N/32] (either output may be null).
 hipError_t launch_dense_q8_0(const uint8_t* x, const uint8_t* w, int64_t T, int N, int K, float* y_f32,

@@ -94,6 +94,7 @@ class Inputs:
     router_w: np.ndarray     # float32 [T, k]
     gateup_q3k: np.ndarray   # uint8 [E, 2F, L/256, 110]
     down_iq4nl: np.ndarray   # uint8 [E, L, F/32, 18]
+    router_logits: Optional[np.ndarray] = None  # float32 [T, E]: the logits of step 3, before the softmax
 
 
 def _route(rng: np.random.Generator, wl: Workload) -> tuple:
@@ -106,6 +107,7 @@ def _route(rng: np.random.Generator, wl: Workload) -> tuple:
         if wl.n_masked > 0:
             masked = np.argsort(pop, kind="stable")[: wl.n_masked]
             logits[:, masked] = -np.inf
+    raw = logits.astype(np.float32)
     logits = logits - logits.max(axis=1, keepdims=True)
     p = np.exp(logits)
     p /= p.sum(axis=1, keepdims=True)
@@ -113,7 +115,7 @@ def _route(rng: np.random.Generator, wl: Workload) -> tuple:
     order = np.argsort(-p, axis=1, kind="stable")[:, : wl.k]
     top = np.take_along_axis(p, order, axis=1)
     top = top / top.sum(axis=1, keepdims=True)
-    return order.astype(np.int32), top.astype(np.float32)
+    return order.astype(np.int32), top.astype(np.float32), raw
 
 
 def random_q3k(rng: np.random.Generator, shape: tuple) -> np.ndarray:
@@ -137,10 +139,10 @@ def make_inputs(wl: Workload) -> Inputs:
         raise ValueError(f"unsupported workload shape {wl}")
     rng = np.random.default_rng(wl.seed)
     x = rng.standard_normal((wl.T, wl.L), dtype=np.float32)
-    idx, w = _route(rng, wl)
+    idx, w, logits = _route(rng, wl)
     gu = random_q3k(rng, (wl.E, 2 * wl.F, wl.L // 256))
     dn = random_iq4nl(rng, (wl.E, wl.L, wl.F // 32))
-    return Inputs(wl, x, idx, w, gu, dn)
+    return Inputs(wl, x, idx, w, gu, dn, logits)
 
 
 def group_sizes(router_idx: np.ndarray, E: int) -> np.ndarray:

@@ -91,3 +91,13 @@ def test_dense_argument_errors_before_any_hip_call():
     assert fd(x, w, 4, 64, 64, y, None, None, 0x50000, 0, 0) == 1
     # T = 0 is a no-op that touches nothing
     assert f(None, None, 0, 64, 64, y, None, None) == 0
+
+
+def test_router_argument_errors_before_any_hip_call():
+    f = lm.lib().lat_moe_router_topk
+    l, i, w = 0x10000, 0x20000, 0x30000
+    for T, E, k in [(-1, 8, 2), (4, 0, 1), (4, 1025, 2), (4, 8, 0), (4, 8, 9), (4, 128, 65)]:
+        assert f(l, T, E, k, i, w, None) == 1, (T, E, k)
+    assert f(l + 4, 4, 8, 2, i, w, None) == 1
+    assert f(l, 4, 8, 2, None, w, None) == 1
+    assert f(None, 0, 8, 2, None, None, None) == 0   # T = 0: no-op
