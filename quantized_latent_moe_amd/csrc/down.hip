@@ -228,10 +228,12 @@ __global__ __launch_bounds__(kThreads) void k_down_generic(const uint8_t* __rest
 // 16-byte-aligned bytes): a persistent, warp-specialized kernel.
 //
 // One workgroup of 12 waves per CU walks the items (expert, tile of up to 128
-// sorted pairs, 128 output rows) round-robin: item i = tile * nlt + row tile,
-// workgroup w takes w, w + G, ...; with G a multiple of nlt = L/128 it keeps
-// one row tile, and the 8 XCDs each serve a fixed eighth of every expert's
-// rows from L2.
+// sorted pairs, 128 output rows): each XCD takes a contiguous range of token
+// tiles with all their row tiles, so the H tile of an item is fetched from
+// memory once and shared in that XCD's L2 by the workgroups working on its
+// row tiles, and an expert's rows stay there across its consecutive tiles
+// (dealing a fixed row tile to each XCD instead made every XCD read every H
+// tile: 0.97 GB per launch at 5268 tokens).
 //   8 consumer waves: wave c owns rows 32*(c&3) .. +31 against tokens
 //     64*(c>>2) .. +63 (two 32x32 tiles sharing the weight fragment).  Per
 //     block: J = v_mfma_i32_32x32x32_i8 with the accumulator initialised to
@@ -249,6 +251,7 @@ __global__ __launch_bounds__(kThreads) void k_down_generic(const uint8_t* __rest
 // Operand rows are 256 bytes with their 16-byte chunks XOR-swizzled by the
 // row's low 4 bits (conflict-free 16-byte reads without padding); operands
 // and scales are double-buffered, one barrier per step.
+constexpr int kXcds = 8;  // workgroups are dealt to the XCDs round-robin
 constexpr int kWsConsumers = 8, kWsProducers = 4;
 constexpr int kWsThreads = 64 * (kWsConsumers + kWsProducers);  // 768
 constexpr int kWsLT = 128;                                      // output rows per item
@@ -295,10 +298,20 @@ __global__ __launch_bounds__(kWsThreads) void k_down(const uint8_t* __restrict__
   __shared__ __align__(16) float dhs[2][kWsNT][8];      // d_H per token and block
 
   const int nlt = L / kWsLT;
-  const int n_items = misc[kMiscTiles] * nlt;
-  const int G = gridDim.x;
-  if ((int)blockIdx.x >= n_items) return;
-  const int my_items = (n_items - 1 - (int)blockIdx.x) / G + 1;
+  // XCD x (workgroups w with w % 8 == x) takes token tiles [t0, t1), all their
+  // row tiles; its workgroup l = w / 8 takes items l, l + G/8, ... of that
+  // list (tile major), so the XCD's workgroups share each H tile in L2 and
+  // an expert's consecutive tiles reuse its rows there.
+  const int n_tiles = misc[kMiscTiles];
+  const int xcd = (int)blockIdx.x % kXcds, G8 = gridDim.x / kXcds, wl = (int)blockIdx.x / kXcds;
+  const int t0 = (int)((int64_t)n_tiles * xcd / kXcds), t1 = (int)((int64_t)n_tiles * (xcd + 1) / kXcds);
+  const int x_items = (t1 - t0) * nlt;
+  if (wl >= x_items) return;
+  const int my_items = (x_items - 1 - wl) / G8 + 1;
+  auto item_of = [&](int j) {
+    const int q = wl + j * G8;
+    return (t0 + q / nlt) * nlt + q % nlt;  // global item index: tile * nlt + row tile
+  };
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: role branches stay scalar
   const int nfb = F / 32, nsb = F / 256;
@@ -318,7 +331,7 @@ __global__ __launch_bounds__(kWsThreads) void k_down(const uint8_t* __restrict__
     int lj = 0, lsb = 0, ql0 = -1;
     bool need_setup = true;
     auto setup = [&](int j) {
-      const DItem it = ditem((int)blockIdx.x + j * G, nlt, tiles, offsets);
+      const DItem it = ditem(item_of(j), nlt, tiles, offsets);
       const int e = __builtin_amdgcn_readfirstlane(it.e);
       rw_src = make_rsrc(dn + (int64_t)e * L * row_bytes, (uint32_t)(L * row_bytes));
       if (it.l0 != ql0) {  // once per workgroup when the grid is a multiple of nlt
@@ -439,7 +452,7 @@ __global__ __launch_bounds__(kWsThreads) void k_down(const uint8_t* __restrict__
   for (int i = 0; i < 16; ++i) magic[i] = kMagicBits;
   float acc0[16], acc1[16];
   int cj = 0, csb = 0;
-  DItem cur = ditem((int)blockIdx.x, nlt, tiles, offsets);
+  DItem cur = ditem(item_of(0), nlt, tiles, offsets);
   int pair0 = -1, pair1 = -1;
   float w0 = 0.f, w1 = 0.f;
   // one K step over both halves (TWO) or the first only
@@ -544,7 +557,7 @@ __global__ __launch_bounds__(kWsThreads) void k_down(const uint8_t* __restrict__
           }
         }
         csb = 0;
-        if (++cj < my_items) cur = ditem((int)blockIdx.x + cj * G, nlt, tiles, offsets);
+        if (++cj < my_items) cur = ditem(item_of(cj), nlt, tiles, offsets);
       }
       __syncthreads();
     }
@@ -570,10 +583,9 @@ hipError_t launch_down(const uint8_t* dn, const float* router_w, const Shapes& s
                        const ProbeRows* probe, hipStream_t st) {
   const ProbeRows none = {nullptr, 0, 0};
   if (s.F % 256 == 0 && ((uintptr_t)dn & 15u) == 0) {
-    // one persistent workgroup per CU, a multiple of the row-tile count when possible
-    const int nlt = s.L / kWsLT;
-    int grid = w.num_cus;
-    if (grid >= nlt) grid -= grid % nlt;
+    // one persistent workgroup per CU, a multiple of the XCD count
+    int grid = w.num_cus - w.num_cus % kXcds;
+    if (grid < kXcds) grid = kXcds;
     const int pairs = (int)s.pairs();
     if (probe)
       hipLaunchKernelGGL(k_down<true>, dim3(grid), dim3(kWsThreads), 0, st, dn, router_w, w.perm, w.tiles, w.offsets,

@@ -7,11 +7,10 @@
 // (lat_q3k_w11.cu commit message).
 //
 // Persistent kernel: one workgroup per CU walks the work items (token tile of
-// up to kTileN = 128 sorted pairs, 64 features) round-robin: item
-// i = tile * nft + feature tile, workgroup w takes w, w + G, w + 2G, ...  With
-// G a multiple of the feature-tile count a workgroup keeps one feature tile,
-// and since workgroups are dealt to the 8 XCDs round-robin, each XCD's L2
-// serves a fixed subset of every expert's rows.
+// up to kTileN = 128 sorted pairs, 64 features): each XCD takes a contiguous
+// range of token tiles with all their feature tiles, so a tile's gathered
+// activation rows are fetched from memory once and shared in that XCD's L2,
+// and an expert's rows stay there across its consecutive tiles.
 //
 // The workgroup's 12 waves have two roles (3 waves per SIMD):
 //   8 consumer waves: wave c owns the gate and the up 32x32 tile of features
@@ -48,6 +47,7 @@
 namespace latmoe {
 namespace {
 
+constexpr int kXcds = 8;  // workgroups are dealt to the XCDs round-robin
 constexpr int kConsumers = 8, kProducers = 4;
 constexpr int kThreads = 64 * (kConsumers + kProducers);  // 768
 constexpr int kFT = 64;              // features per work item
@@ -92,10 +92,20 @@ __global__ __launch_bounds__(kThreads) void k_gateup(const int8_t* __restrict__ 
   __shared__ int32_t ids[2][kNT];  // token ids (or -1) of the producers' next items
 
   const int nft = (F + kFT - 1) / kFT;
-  const int n_items = misc[kMiscTiles] * nft;
-  const int G = gridDim.x;
-  if ((int)blockIdx.x >= n_items) return;
-  const int my_items = (n_items - 1 - (int)blockIdx.x) / G + 1;
+  // XCD x (workgroups w with w % 8 == x) takes token tiles [t0, t1), all their
+  // feature tiles; its workgroup l = w / 8 takes items l, l + G/8, ... of that
+  // list (tile major), so the XCD's workgroups share each tile's activation
+  // rows in L2 and an expert's rows stay there across its consecutive tiles.
+  const int n_tiles = misc[kMiscTiles];
+  const int xcd = (int)blockIdx.x % kXcds, G8 = gridDim.x / kXcds, wl = (int)blockIdx.x / kXcds;
+  const int t0 = (int)((int64_t)n_tiles * xcd / kXcds), t1 = (int)((int64_t)n_tiles * (xcd + 1) / kXcds);
+  const int x_items = (t1 - t0) * nft;
+  if (wl >= x_items) return;
+  const int my_items = (x_items - 1 - wl) / G8 + 1;
+  auto item_of = [&](int j) {
+    const int q = wl + j * G8;
+    return (t0 + q / nft) * nft + q % nft;  // global item index: tile * nft + feature tile
+  };
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: role branches stay scalar
@@ -120,12 +130,12 @@ __global__ __launch_bounds__(kThreads) void k_gateup(const int8_t* __restrict__ 
   bool need_setup = true;
   auto fetch_ids = [&](int j) {
     if (j < my_items) {
-      const Item it = item_info((int)blockIdx.x + j * G, nft, tiles, offsets);
+      const Item it = item_info(item_of(j), nft, tiles, offsets);
       if (ptid < kNT) ids[j & 1][ptid] = ptid < it.cnt ? perm[it.pos0 + ptid] / k : -1;
     }
   };
   auto setup = [&](int j) {
-    const Item it = item_info((int)blockIdx.x + j * G, nft, tiles, offsets);
+    const Item it = item_info(item_of(j), nft, tiles, offsets);
     const int e = __builtin_amdgcn_readfirstlane(it.e);  // uniform: the descriptor lives in SGPRs
     rw_src = make_rsrc(gu + (int64_t)e * 2 * F * row_bytes, (uint32_t)(2 * F * row_bytes));
     if (it.f0 != qf0) {  // once per workgroup when the grid is a multiple of nft
@@ -244,7 +254,7 @@ __global__ __launch_bounds__(kThreads) void k_gateup(const int8_t* __restrict__ 
   const v16i zero = {};
   float accg[16], accu[16];
   int cj = 0, csb = 0;  // item index and super-block of the MFMA step
-  Item cur = item_info((int)blockIdx.x, nft, tiles, offsets);
+  Item cur = item_info(item_of(0), nft, tiles, offsets);
 
   auto mfma_step = [&](auto grp_tag, int b) {
     constexpr int GRP = decltype(grp_tag)::value;
@@ -392,7 +402,7 @@ __global__ __launch_bounds__(kThreads) void k_gateup(const int8_t* __restrict__ 
         if (++csb == nsb) {
           epilogue();
           csb = 0;
-          if (++cj < my_items) cur = item_info((int)blockIdx.x + cj * G, nft, tiles, offsets);
+          if (++cj < my_items) cur = item_info(item_of(cj), nft, tiles, offsets);
         }
         __syncthreads();
       }
@@ -408,8 +418,8 @@ hipError_t launch_gateup(const Shapes& s, const Work& w, const uint8_t* gu, cons
   // One persistent workgroup per CU, rounded down to a multiple of the feature
   // tile count (so each workgroup keeps one feature tile) when that is possible.
   const int nft = (s.F + kFT - 1) / kFT;
-  int grid = w.num_cus;
-  if (grid >= nft) grid -= grid % nft;
+  int grid = w.num_cus - w.num_cus % kXcds;
+  if (grid < kXcds) grid = kXcds;
   const ProbeRows none = {nullptr, 0, 0};
   if (probe)
     hipLaunchKernelGGL(k_gateup<true>, dim3(grid), dim3(kThreads), 0, st, w.xc, w.xd, gu, w.perm, w.tiles, w.offsets,
