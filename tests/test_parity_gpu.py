@@ -93,6 +93,13 @@ SMALL = [
     Workload("wide_k", T=48, L=512, F=256, E=12, k=10, zipf_s=1.1, seed=11),
     # more than 512 experts (the chunked route passes at a small batch)
     Workload("many_experts", T=64, L=256, F=128, E=600, k=4, seed=12),
+    # the largest expert count, one expert per token
+    Workload("max_experts_k1", T=300, L=256, F=256, E=1024, k=1, seed=13),
+    # one token
+    Workload("one_token", T=1, L=1024, F=2048, E=16, k=4, seed=14),
+    # wide latent and FFN dimensions (past the small-batch limits: L > 1024, F > 2048)
+    Workload("wide_dims", T=40, L=2048, F=4096, E=4, k=2, seed=15),
+    Workload("wide_dims_prefill", T=700, L=2048, F=1024, E=6, k=2, zipf_s=1.1, seed=16),
 ]
 
 
