@@ -415,9 +415,7 @@ __global__ __launch_bounds__(kThreads) void k_gateup(const int8_t* __restrict__ 
 }  // namespace
 
 hipError_t launch_gateup(const Shapes& s, const Work& w, const uint8_t* gu, const ProbeRows* probe, hipStream_t st) {
-  // One persistent workgroup per CU, rounded down to a multiple of the feature
-  // tile count (so each workgroup keeps one feature tile) when that is possible.
-  const int nft = (s.F + kFT - 1) / kFT;
+  // One persistent workgroup per CU, rounded down to a multiple of the XCD count.
   int grid = w.num_cus - w.num_cus % kXcds;
   if (grid < kXcds) grid = kXcds;
   const ProbeRows none = {nullptr, 0, 0};
