@@ -275,6 +275,76 @@ class DenseStage:
         return res
 
 
+# Cold-call repetitions per workload (one call between two events, caches
+# evicted before each): tiny, decode, mid_prefill 50; prefill_5k 20; prefill_21k 10.
+COLD_REPS = {"tiny": 50, "decode": 50, "mid_prefill": 50, "prefill_5k": 20, "prefill_21k": 10}
+
+
+def device_info():
+    """CU count from the device properties, and a measured plain streaming
+    copy (1 GiB read and 1 GiB written per call, bytes of both counted) next
+    to the nominal 8 TB/s."""
+    import torch
+    p = torch.cuda.get_device_properties(0)
+    src = torch.ones((1 << 30) // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = 2 * (1 << 30) * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", None), "cus": p.multi_processor_count,
+            "stream_copy_gbs": round(gbs, 1), "hbm_peak_gbs": PEAK_HBM_GBS}
+
+
+def per_config(names):
+    """Every workload timed one call at a time, with the L2s and the 256 MB
+    last-level cache evicted before each call (a 1 GiB buffer written), as the
+    median, p10 and p90 of the call time; and the back-to-back rate."""
+    import numpy as np
+    import torch
+    from quantized_latent_moe_amd.inputs import WORKLOADS
+    evict = torch.empty((1 << 30) // 4, dtype=torch.float32, device="cuda")
+    out = {}
+    for name in names:
+        wl = WORKLOADS[name]
+        st = Stage(wl)
+        st.prime(0.05)
+        alg = algorithmic(wl, st.inputs.router_idx)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        times = []
+        for _ in range(COLD_REPS[name]):
+            evict.fill_(1.0)
+            e0.record()
+            st.step()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e3)
+        warm_ms, _ = st.time_steps(COLD_REPS[name], 3)
+        med = float(np.median(times))
+        ops = alg["ops_gateup"] + alg["ops_down"]
+        out[name] = {"T": wl.T, "cold_us": {"median": round(med, 2), "p10": round(float(np.percentile(times, 10)), 2),
+                                            "p90": round(float(np.percentile(times, 90)), 2), "calls": len(times)},
+                     "warm_us": round(warm_ms * 1e3, 2),
+                     "tokens_per_s_cold": round(wl.T / (med * 1e-6), 1),
+                     "int8_frac_cold": round(ops / (med * 1e-6) / 1e12 / PEAK_INT8_TOPS, 4),
+                     "alg_gbs_cold": round(alg["bytes"] / (med * 1e-6) / 1e9, 1)}
+        print(f"[bench] {name}: cold median {med:.1f} us (p10 {out[name]['cold_us']['p10']}, "
+              f"p90 {out[name]['cold_us']['p90']}), back-to-back {warm_ms * 1e3:.1f} us", file=sys.stderr, flush=True)
+        del st
+        torch.cuda.empty_cache()
+    del evict
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline_dense(dwl, target_s):
     """The oracle's D and U projections, as they stand, on the first n tokens."""
     import oracle
@@ -397,6 +467,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-du", action="store_true", help="skip the latent D / U projection timings")
     ap.add_argument("--du-only", action="store_true", help="time only the latent D / U projections")
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="skip the cold-cache timing of every workload (per_config)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="first run a plain device copy of MIB MiB (three times), the reference for counter scaling")
@@ -504,6 +576,9 @@ def main():
               file=sys.stderr, flush=True)
         print(f"[bench] decode {dms * 1e3:.2f} us/step, {gbs:.0f} GB/s", file=sys.stderr, flush=True)
         del ds
+    if not args.no_per_config:
+        out["device"] = device_info()
+        out["per_config"] = per_config(["tiny", "decode", "mid_prefill", "prefill_5k", "prefill_21k"])
     if not args.no_du:
         from quantized_latent_moe_amd.inputs import DENSE_WORKLOADS
         du = {}
