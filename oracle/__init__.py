@@ -47,13 +47,17 @@ def lib() -> ctypes.CDLL:
         c.orc_float_to_half.argtypes = [ctypes.c_float]
         c.orc_float_to_half.restype = ctypes.c_uint16
         c.orc_quantize_q8_1.argtypes = [P, i64, i32, P]
-        for f in (c.orc_dequant_q3k, c.orc_dequant_iq4nl, c.orc_dequant_q8_1):
+        for f in (c.orc_dequant_q3k, c.orc_dequant_iq4nl, c.orc_dequant_q4_0, c.orc_dequant_q8_1):
             f.argtypes = [P, i64, P]
         c.orc_q3k_fields.argtypes = [P, i64, P, P, P]
         c.orc_iq4nl_fields.argtypes = [P, i64, P, P]
         c.orc_forward.argtypes = [P, P, P, P, P, i64, i32, i32, i32, i32, P, i64, P, P, P]
         c.orc_forward.restype = i64
+        c.orc_forward_fmt.argtypes = [P, P, P, P, P, i32, i64, i32, i32, i32, i32, P, i64, P, P, P]
+        c.orc_forward_fmt.restype = i64
         c.orc_down_combine.argtypes = [P, P, P, P, i64, i32, i32, i32, i32, P, i64, P]
+        c.orc_down_combine_fmt.argtypes = [P, P, P, P, i32, i64, i32, i32, i32, i32, P, i64, P]
+        c.orc_probe_down_fmt.argtypes = [P, P, P, i32, i64, i32, i32, i32, i32, i64, P, P, P]
         c.orc_probe_gateup.argtypes = [P, P, P, i64, i32, i32, i32, i32, i64, P, P, P, P]
         c.orc_probe_down.argtypes = [P, P, P, i64, i32, i32, i32, i32, i64, P, P, P]
         c.orc_dequant_q8_0.argtypes = [P, i64, P]
@@ -114,6 +118,19 @@ def dequant_iq4nl(blocks: np.ndarray) -> np.ndarray:
     return out.reshape(b.shape[:-1] + (32,))
 
 
+def dequant_q4_0(blocks: np.ndarray) -> np.ndarray:
+    """Q4_0 blocks (18 B: fp16 d | 16 nibble bytes) -> d * (nibble - 8)."""
+    b = _c(blocks, np.uint8)
+    n = b.size // 18
+    out = np.empty(n * 32, np.float64)
+    lib().orc_dequant_q4_0(_p(b), n, _p(out))
+    return out.reshape(b.shape[:-1] + (32,))
+
+
+# Formats of the down weights (both 18 bytes per 32 weights, the same layout).
+DOWN_FORMATS = {"iq4_nl": 0, "q4_0": 1}
+
+
 def dequant_q8_1(blocks: np.ndarray) -> np.ndarray:
     b = _c(blocks, np.uint8)
     n = b.size // 36
@@ -150,9 +167,10 @@ class Result:
 
 def forward(x_q8: np.ndarray, router_idx: np.ndarray, router_w: np.ndarray, gateup: np.ndarray,
             down: np.ndarray, L: int, F: int, E: int, tokens: Optional[Sequence[int]] = None,
-            want_h: bool = True, want_gu: bool = False) -> Result:
+            want_h: bool = True, want_gu: bool = False, down_format: str = "iq4_nl") -> Result:
     """Whole stage.  y is fp64 [n_tok, L]; h is q8_1 [n_tok*k, F/32, 36] in
-    pair order of the evaluated tokens; gu is fp64 [n_tok*k, 2F]."""
+    pair order of the evaluated tokens; gu is fp64 [n_tok*k, 2F].  The down
+    weights are IQ4_NL or (down_format "q4_0") Q4_0 blocks."""
     x_q8 = _c(x_q8, np.uint8)
     idx = _c(router_idx, np.int32)
     w = _c(router_w, np.float32)
@@ -164,13 +182,13 @@ def forward(x_q8: np.ndarray, router_idx: np.ndarray, router_w: np.ndarray, gate
     y = np.zeros((n_tok, L), np.float64)
     h = np.zeros((n_tok * k, F // 32, 36), np.uint8) if want_h else None
     gu = np.zeros((n_tok * k, 2 * F), np.float64) if want_gu else None
-    dropped = lib().orc_forward(_p(x_q8), _p(idx), _p(w), _p(gateup), _p(down), T, L, F, E, k, _p(tok), n_tok,
-                                _p(y), _p(h), _p(gu))
+    dropped = lib().orc_forward_fmt(_p(x_q8), _p(idx), _p(w), _p(gateup), _p(down), DOWN_FORMATS[down_format], T, L,
+                                    F, E, k, _p(tok), n_tok, _p(y), _p(h), _p(gu))
     return Result(y, h, gu, int(dropped))
 
 
 def down_combine(h_q8: np.ndarray, router_idx: np.ndarray, router_w: np.ndarray, down: np.ndarray, L: int, F: int,
-                 E: int, tokens: Optional[Sequence[int]] = None) -> np.ndarray:
+                 E: int, tokens: Optional[Sequence[int]] = None, down_format: str = "iq4_nl") -> np.ndarray:
     """y from given H (q8_1 [T*k, F/32, 36], pair order over ALL T tokens)."""
     h = _c(h_q8, np.uint8)
     idx = _c(router_idx, np.int32)
@@ -179,7 +197,8 @@ def down_combine(h_q8: np.ndarray, router_idx: np.ndarray, router_w: np.ndarray,
     tok = None if tokens is None else _c(tokens, np.int64)
     n_tok = T if tok is None else tok.size
     y = np.zeros((n_tok, L), np.float64)
-    lib().orc_down_combine(_p(h), _p(idx), _p(w), _p(_c(down, np.uint8)), T, L, F, E, k, _p(tok), n_tok, _p(y))
+    lib().orc_down_combine_fmt(_p(h), _p(idx), _p(w), _p(_c(down, np.uint8)), DOWN_FORMATS[down_format], T, L, F, E,
+                               k, _p(tok), n_tok, _p(y))
     return y
 
 
@@ -196,15 +215,15 @@ def probe_gateup(x_q8, router_idx, gateup, L, F, E, pairs, rows, want_i16=False)
     return (o32, o16) if want_i16 else o32
 
 
-def probe_down(h_q8, router_idx, down, L, F, E, pairs, rows):
+def probe_down(h_q8, router_idx, down, L, F, E, pairs, rows, down_format="iq4_nl"):
     idx = _c(router_idx, np.int32)
     T, k = idx.shape
     pairs = _c(pairs, np.int64)
     rows = _c(rows, np.int32)
     n = pairs.size
     out = np.zeros((n, F // 32), np.int32)
-    lib().orc_probe_down(_p(_c(h_q8, np.uint8)), _p(idx), _p(_c(down, np.uint8)), T, L, F, E, k, n, _p(pairs),
-                         _p(rows), _p(out))
+    lib().orc_probe_down_fmt(_p(_c(h_q8, np.uint8)), _p(idx), _p(_c(down, np.uint8)), DOWN_FORMATS[down_format], T, L,
+                             F, E, k, n, _p(pairs), _p(rows), _p(out))
     return out
 
 

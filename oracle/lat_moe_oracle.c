@@ -13,7 +13,9 @@
  *                folded in floating point,
  *     SwiGLU   : H = silu(G) * U,
  *     requant  : H re-rounded to q8_1 (32-value blocks),
- *     down     : IQ4_NL weights [L][F] against H, same block structure,
+ *     down     : IQ4_NL weights [L][F] against H, same block structure
+ *                (or Q4_0 weights, the same block layout with a linear
+ *                table: see orc_q4_0_decode),
  *     combine  : y[t] += w[t][j] * O, slots taken in order j = 0..k-1.
  * Source: "Run Edge0-145B Q3_K on AMD HIP (Linux, gfx1100) #1", section
  * "Contents" (gate/up reads Q3_K, applies SwiGLU and rounds H to q8_1; down
@@ -159,6 +161,30 @@ void orc_iq4nl_decode(const uint8_t* blk, int8_t* kv, double* d) {
   *d = orc_half_to_double(rd16(blk));
 }
 
+/* Q4_0: 32 weights in 18 bytes = d (fp16) | qs[16], the nibbles in the same
+ * places as IQ4_NL's; weight = d * (nibble - 8).  The format is one of the
+ * weight formats the PR page names ("Not done": a Q4_0 file was not tried);
+ * its layout is ggml's public GGUF definition.  Here it is an alternative
+ * format of the down weights. */
+void orc_q4_0_decode(const uint8_t* blk, int8_t* v, double* d) {
+  const uint8_t* qs = blk + 2;
+  for (int i = 0; i < IQ4NL_VALUES; ++i) {
+    int nib = i < 16 ? (qs[i] & 15) : (qs[i - 16] >> 4);
+    v[i] = (int8_t)(nib - 8);
+  }
+  *d = orc_half_to_double(rd16(blk));
+}
+
+/* Down weight formats (both 18 bytes per 32 weights). */
+#define DOWN_IQ4NL 0
+#define DOWN_Q4_0 1
+static void down_block_decode(int fmt, const uint8_t* blk, int8_t* kv, double* d) {
+  if (fmt == DOWN_Q4_0)
+    orc_q4_0_decode(blk, kv, d);
+  else
+    orc_iq4nl_decode(blk, kv, d);
+}
+
 /* q8_1: 32 values in 36 bytes = d (fp16) | s (fp16) | qs[32] (int8). */
 void orc_q8_1_decode(const uint8_t* blk, int8_t* q, double* d) {
   for (int i = 0; i < Q81_VALUES; ++i) q[i] = (int8_t)blk[4 + i];
@@ -213,6 +239,15 @@ void orc_dequant_iq4nl(const uint8_t* blocks, int64_t nblocks, double* out) {
     for (int i = 0; i < IQ4NL_VALUES; ++i) out[b * IQ4NL_VALUES + i] = d * (double)kv[i];
   }
 }
+void orc_dequant_q4_0(const uint8_t* blocks, int64_t nblocks, double* out) {
+  for (int64_t b = 0; b < nblocks; ++b) {
+    double d;
+    int8_t v[IQ4NL_VALUES];
+    orc_q4_0_decode(blocks + b * IQ4NL_BYTES, v, &d);
+    for (int i = 0; i < IQ4NL_VALUES; ++i) out[b * IQ4NL_VALUES + i] = d * (double)v[i];
+  }
+}
+
 void orc_dequant_q8_1(const uint8_t* blocks, int64_t nblocks, double* out) {
   for (int64_t b = 0; b < nblocks; ++b) {
     int8_t q[Q81_VALUES];
@@ -261,13 +296,14 @@ static void gateup_row_dots(const uint8_t* row, const uint8_t* act, int L, int32
   }
 }
 
-/* Down block dots of one IQ4_NL row (F/32 blocks) against H (F/32 q8_1
- * blocks): J32[b] = sum_i K(i) * qH(i); dd[b] gets each block's d. */
-static void down_row_dots(const uint8_t* row, const uint8_t* h, int F, int32_t* J32, double* dd) {
+/* Down block dots of one IQ4_NL (or Q4_0) row (F/32 blocks) against H (F/32
+ * q8_1 blocks): J32[b] = sum_i K(i) * qH(i), K the block's integer weight
+ * (table value, or nibble - 8); dd[b] gets each block's d. */
+static void down_row_dots(int fmt, const uint8_t* row, const uint8_t* h, int F, int32_t* J32, double* dd) {
   int nb = F / IQ4NL_VALUES;
   for (int b = 0; b < nb; ++b) {
     int8_t kv[IQ4NL_VALUES];
-    orc_iq4nl_decode(row + (int64_t)b * IQ4NL_BYTES, kv, &dd[b]);
+    down_block_decode(fmt, row + (int64_t)b * IQ4NL_BYTES, kv, &dd[b]);
     const int8_t* q = (const int8_t*)(h + (int64_t)b * Q81_BYTES + 4);
     int32_t acc = 0;
     for (int i = 0; i < IQ4NL_VALUES; ++i) acc += (int32_t)kv[i] * (int32_t)q[i];
@@ -314,7 +350,7 @@ static void pair_swiglu_q8_1(const double* G, const double* U, int F, uint8_t* h
 }
 
 /* Down of one pair: O[l] = sum_b dd[l][b] * dH[b] * J32[l][b], fp64. */
-static void pair_down(const uint8_t* hq, const uint8_t* dn_e, int L, int F, double* O) {
+static void pair_down(int fmt, const uint8_t* hq, const uint8_t* dn_e, int L, int F, double* O) {
   int nb = F / IQ4NL_VALUES;
   int64_t row_bytes = (int64_t)nb * IQ4NL_BYTES;
   int32_t* J32 = (int32_t*)malloc(sizeof(int32_t) * nb);
@@ -322,7 +358,7 @@ static void pair_down(const uint8_t* hq, const uint8_t* dn_e, int L, int F, doub
   double* dh = (double*)malloc(sizeof(double) * nb);
   for (int b = 0; b < nb; ++b) dh[b] = orc_half_to_double(rd16(hq + (int64_t)b * Q81_BYTES));
   for (int l = 0; l < L; ++l) {
-    down_row_dots(dn_e + l * row_bytes, hq, F, J32, dd);
+    down_row_dots(fmt, dn_e + l * row_bytes, hq, F, J32, dd);
     double acc = 0.0;
     for (int b = 0; b < nb; ++b) acc += dd[b] * dh[b] * (double)J32[b];
     O[l] = acc;
@@ -334,7 +370,8 @@ static void pair_down(const uint8_t* hq, const uint8_t* dn_e, int L, int F, doub
 
 /* Full stage for a list of tokens.
  *   x_q8     [T][L/32] q8_1         idx, w  [T][k]
- *   gateup   [E][2F][L/256] Q3_K    down    [E][L][F/32] IQ4_NL
+ *   gateup   [E][2F][L/256] Q3_K    down    [E][L][F/32] IQ4_NL (down_fmt 0)
+ *                                            or Q4_0 (down_fmt 1)
  *   tokens   the n_tok token ids to evaluate (NULL = all T, in order)
  *   y        [n_tok][L] fp64 (overwritten)
  *   h_out    [n_tok*k][F/32] q8_1 H per pair (NULL to skip); an invalid
@@ -342,9 +379,9 @@ static void pair_down(const uint8_t* hq, const uint8_t* dn_e, int L, int F, doub
  *   gu_out   [n_tok*k][2F] fp64 G then U per pair (NULL to skip)
  * Pairs with an expert id outside [0, E) contribute nothing.  Returns the
  * number of such pairs among the evaluated tokens. */
-int64_t orc_forward(const uint8_t* x_q8, const int32_t* idx, const float* w, const uint8_t* gateup,
-                    const uint8_t* down, int64_t T, int L, int F, int E, int k, const int64_t* tokens,
-                    int64_t n_tok, double* y, uint8_t* h_out, double* gu_out) {
+int64_t orc_forward_fmt(const uint8_t* x_q8, const int32_t* idx, const float* w, const uint8_t* gateup,
+                        const uint8_t* down, int down_fmt, int64_t T, int L, int F, int E, int k,
+                        const int64_t* tokens, int64_t n_tok, double* y, uint8_t* h_out, double* gu_out) {
   if (!tokens) n_tok = T;
   int64_t xrow_bytes = (int64_t)(L / Q81_VALUES) * Q81_BYTES;
   int64_t hrow_bytes = (int64_t)(F / Q81_VALUES) * Q81_BYTES;
@@ -372,7 +409,7 @@ int64_t orc_forward(const uint8_t* x_q8, const int32_t* idx, const float* w, con
       }
       pair_gateup(x_q8 + t * xrow_bytes, gateup + e * gu_e_bytes, L, F, G, U);
       pair_swiglu_q8_1(G, U, F, hq);
-      pair_down(hq, down + e * dn_e_bytes, L, F, O);
+      pair_down(down_fmt, hq, down + e * dn_e_bytes, L, F, O);
       double wj = (double)w[t * k + j];
       for (int l = 0; l < L; ++l) yt[l] += wj * O[l];
       if (h_out) memcpy(h_out + po * hrow_bytes, hq, hrow_bytes);
@@ -389,11 +426,18 @@ int64_t orc_forward(const uint8_t* x_q8, const int32_t* idx, const float* w, con
   return dropped;
 }
 
+int64_t orc_forward(const uint8_t* x_q8, const int32_t* idx, const float* w, const uint8_t* gateup,
+                    const uint8_t* down, int64_t T, int L, int F, int E, int k, const int64_t* tokens,
+                    int64_t n_tok, double* y, uint8_t* h_out, double* gu_out) {
+  return orc_forward_fmt(x_q8, idx, w, gateup, down, DOWN_IQ4NL, T, L, F, E, k, tokens, n_tok, y, h_out, gu_out);
+}
+
 /* Down projection and combine only, from given H (q8_1, [T*k][F/32] in pair
  * order): y[t] = sum_j w[t][j] * O(H[t*k+j]).  Used to check the second half
  * of the stage against a GPU's own H. */
-void orc_down_combine(const uint8_t* h_q8, const int32_t* idx, const float* w, const uint8_t* down, int64_t T,
-                      int L, int F, int E, int k, const int64_t* tokens, int64_t n_tok, double* y) {
+void orc_down_combine_fmt(const uint8_t* h_q8, const int32_t* idx, const float* w, const uint8_t* down,
+                          int down_fmt, int64_t T, int L, int F, int E, int k, const int64_t* tokens,
+                          int64_t n_tok, double* y) {
   if (!tokens) n_tok = T;
   int64_t hrow_bytes = (int64_t)(F / Q81_VALUES) * Q81_BYTES;
   int64_t dn_e_bytes = (int64_t)L * (F / IQ4NL_VALUES) * IQ4NL_BYTES;
@@ -406,12 +450,17 @@ void orc_down_combine(const uint8_t* h_q8, const int32_t* idx, const float* w, c
     for (int j = 0; j < k; ++j) {
       int e = idx[t * k + j];
       if (e < 0 || e >= E) continue;
-      pair_down(h_q8 + (t * k + j) * hrow_bytes, down + e * dn_e_bytes, L, F, O);
+      pair_down(down_fmt, h_q8 + (t * k + j) * hrow_bytes, down + e * dn_e_bytes, L, F, O);
       double wj = (double)w[t * k + j];
       for (int l = 0; l < L; ++l) yt[l] += wj * O[l];
     }
     free(O);
   }
+}
+
+void orc_down_combine(const uint8_t* h_q8, const int32_t* idx, const float* w, const uint8_t* down, int64_t T,
+                      int L, int F, int E, int k, const int64_t* tokens, int64_t n_tok, double* y) {
+  orc_down_combine_fmt(h_q8, idx, w, down, DOWN_IQ4NL, T, L, F, E, k, tokens, n_tok, y);
 }
 
 /* Integer block-dot probes.
@@ -445,8 +494,9 @@ void orc_probe_gateup(const uint8_t* x_q8, const int32_t* idx, const uint8_t* ga
   }
 }
 
-void orc_probe_down(const uint8_t* h_q8, const int32_t* idx, const uint8_t* down, int64_t T, int L, int F, int E,
-                    int k, int64_t n, const int64_t* pair, const int32_t* row, int32_t* out) {
+void orc_probe_down_fmt(const uint8_t* h_q8, const int32_t* idx, const uint8_t* down, int down_fmt, int64_t T,
+                        int L, int F, int E, int k, int64_t n, const int64_t* pair, const int32_t* row,
+                        int32_t* out) {
   int nb = F / IQ4NL_VALUES;
   int64_t hrow_bytes = (int64_t)nb * Q81_BYTES;
   int64_t row_bytes = (int64_t)nb * IQ4NL_BYTES;
@@ -462,8 +512,13 @@ void orc_probe_down(const uint8_t* h_q8, const int32_t* idx, const uint8_t* down
       continue;
     }
     const uint8_t* wrow = down + ((int64_t)e * L + row[i]) * row_bytes;
-    down_row_dots(wrow, h_q8 + p * hrow_bytes, F, out + i * nb, dd);
+    down_row_dots(down_fmt, wrow, h_q8 + p * hrow_bytes, F, out + i * nb, dd);
   }
+}
+
+void orc_probe_down(const uint8_t* h_q8, const int32_t* idx, const uint8_t* down, int64_t T, int L, int F, int E,
+                    int k, int64_t n, const int64_t* pair, const int32_t* row, int32_t* out) {
+  orc_probe_down_fmt(h_q8, idx, down, DOWN_IQ4NL, T, L, F, E, k, n, pair, row, out);
 }
 
 /* ------------------------------------------------------------------------ */
