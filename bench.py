@@ -53,14 +53,16 @@ def algorithmic(wl, idx):
 
 
 class Stage:
-    """One workload resident on the GPU."""
+    """One workload resident on the GPU (down weights IQ4_NL, or with
+    down_format = DOWN_Q4_0 the same bytes read as Q4_0 blocks)."""
 
-    def __init__(self, wl):
+    def __init__(self, wl, down_format=0):
         import numpy as np
         import torch
         import quantized_latent_moe_amd as lm
         from quantized_latent_moe_amd.inputs import make_inputs
         self.lm, self.torch, self.wl = lm, torch, wl
+        self.down_format = down_format
         I = make_inputs(wl)
         self.inputs = I
         dev = torch.device("cuda", 0)
@@ -77,7 +79,11 @@ class Stage:
         torch.cuda.synchronize()
 
     def step(self):
-        self.lm.expert_forward(self.x, self.idx, self.w, self.gu, self.dn, self.s, self.y, self.ws)
+        if self.down_format:
+            self.lm.expert_forward_ex(self.x, self.idx, self.w, self.gu, self.dn, self.down_format, self.s, self.y,
+                                      self.ws)
+        else:
+            self.lm.expert_forward(self.x, self.idx, self.w, self.gu, self.dn, self.s, self.y, self.ws)
 
     def prime(self, seconds=0.1):
         """Part of setup, before the counted warm-up: run the stage for about
@@ -91,8 +97,12 @@ class Stage:
             torch.cuda.synchronize()
 
     def step_timed(self, events):
-        self.lm.expert_forward_debug(self.x, self.idx, self.w, self.gu, self.dn, self.s, self.y, self.ws,
-                                     stage_events=events)
+        if self.down_format:
+            self.lm.expert_forward_ex(self.x, self.idx, self.w, self.gu, self.dn, self.down_format, self.s, self.y,
+                                      self.ws, debug=True, stage_events=events)
+        else:
+            self.lm.expert_forward_debug(self.x, self.idx, self.w, self.gu, self.dn, self.s, self.y, self.ws,
+                                         stage_events=events)
 
     def time_steps(self, steps, warmup):
         torch = self.torch
@@ -457,6 +467,41 @@ def pmc_summary(fetch_dir, write_dir, kernel, copy_mib):
     print(f"hbm_bytes_per_launch {fetch + write:.0f}")
 
 
+def down_q4_0_report(steps, warmup):
+    """The stage with Q4_0 down weights (each workload's random down blocks
+    read as Q4_0, the same bytes): time per step, stage times and the down
+    kernel against its fold roof, at prefill_5k and decode."""
+    import torch
+    import quantized_latent_moe_amd as lm
+    from quantized_latent_moe_amd.inputs import WORKLOADS
+    names = ["route", "gateup", "down", "combine"]
+    rep = {}
+    for name in ("prefill_5k", "decode"):
+        wl = WORKLOADS[name]
+        st = Stage(wl, down_format=lm.DOWN_Q4_0)
+        st.prime()
+        n = steps if name == "prefill_5k" else max(steps, 50)
+        ms, _ = st.time_steps(n, warmup)
+        stages = st.stage_times(n)
+        alg = algorithmic(wl, st.inputs.router_idx)
+        r = {"workload": name, "ms_per_step": round(ms, 5), "tokens_per_s": round(wl.T / (ms * 1e-3), 1),
+             "stage_ms": {k: round(v, 5) for k, v in zip(names, stages)}}
+        if name == "prefill_5k":
+            fold = alg["fold_down"] / (stages[2] * 1e-3) / 1e12
+            r["down_roofline"] = {"bound": "alu", "kernel": "k_down (Q4_0)", "achieved": round(fold, 2),
+                                  "peak": round(PEAK_VALU_TOPS, 1), "unit": "T lane-op/s",
+                                  "frac": round(fold / PEAK_VALU_TOPS, 4)}
+        else:
+            gbs = alg["bytes"] / (ms * 1e-3) / 1e9
+            r.update(hbm_gbs=round(gbs, 1), hbm_frac=round(gbs / PEAK_HBM_GBS, 4))
+        print(f"[bench] Q4_0 down, {name}: {ms * 1e3:.1f} us/step, down {stages[2] * 1e3:.1f} us", file=sys.stderr,
+              flush=True)
+        rep[name] = r
+        del st
+        torch.cuda.empty_cache()
+    return rep
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -469,6 +514,7 @@ def main():
     ap.add_argument("--du-only", action="store_true", help="time only the latent D / U projections")
     ap.add_argument("--no-per-config", action="store_true",
                     help="skip the cold-cache timing of every workload (per_config)")
+    ap.add_argument("--no-formats", action="store_true", help="skip the Q4_0 down-weight timings")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="first run a plain device copy of MIB MiB (three times), the reference for counter scaling")
@@ -578,6 +624,8 @@ def main():
               file=sys.stderr, flush=True)
         print(f"[bench] decode {dms * 1e3:.2f} us/step, {gbs:.0f} GB/s", file=sys.stderr, flush=True)
         del ds
+    if not args.no_formats:
+        out["down_q4_0"] = down_q4_0_report(args.steps, args.warmup)
     if not args.no_per_config:
         out["device"] = device_info()
         out["per_config"] = per_config(["tiny", "decode", "mid_prefill", "prefill_5k", "prefill_21k"])

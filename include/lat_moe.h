@@ -117,6 +117,30 @@ int lat_moe_expert_forward_debug(const void* x_q8_1, const int32_t* router_idx, 
                                  float* y, void* workspace, size_t workspace_bytes, void* stream,
                                  const lat_moe_debug* dbg);
 
+/* Formats of the down weights for lat_moe_expert_forward_ex.  Both are
+ * 18-byte blocks of 32 weights, fp16 d then 16 bytes of 4-bit indices
+ * (element i < 16 in the low nibble of byte i, element i >= 16 in the high
+ * nibble of byte i - 16); a weight is d * K(index) with
+ *   IQ4_NL: K = {-127, -104, -83, -65, -49, -35, -22, -10, 1, 13, 25, 38, 53, 69, 89, 113}
+ *   Q4_0:   K(index) = index - 8
+ * (ggml's block formats; Q4_0 is among the weight formats named in section
+ * "Not done" of the page "Run Edge0-145B Q3_K on AMD HIP (Linux, gfx1100) #1",
+ * here read as a format of the expert's down weights). */
+#define LAT_MOE_DOWN_IQ4_NL 0
+#define LAT_MOE_DOWN_Q4_0 1
+
+/* The expert stage with a choice of down-weight format: down is
+ * [E][L][F/32] blocks of down_format (LAT_MOE_DOWN_IQ4_NL or
+ * LAT_MOE_DOWN_Q4_0; any other value returns LAT_MOE_EINVAL).  Every other
+ * argument, rule and result is that of lat_moe_expert_forward; dbg may be NULL
+ * (then nothing more is written) or as for lat_moe_expert_forward_debug, whose
+ * down_i32 dots are then sum K(index) * qH with the format's K.  With
+ * LAT_MOE_DOWN_IQ4_NL the call is lat_moe_expert_forward(_debug). */
+int lat_moe_expert_forward_ex(const void* x_q8_1, const int32_t* router_idx, const float* router_w,
+                              const void* gateup_q3k, const void* down, int32_t down_format,
+                              const lat_moe_shapes* shapes, float* y, void* workspace, size_t workspace_bytes,
+                              void* stream, const lat_moe_debug* dbg);
+
 /* Round fp32 rows to q8_1 with the rule above: x [rows][cols] -> out
  * [rows][cols/32] q8_1 blocks (cols % 32 == 0, rows >= 0).  This is the rounding
  * the stage's producer applies to the latent rows (the D projection's q8_1

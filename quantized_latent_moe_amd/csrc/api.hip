@@ -93,10 +93,11 @@ int check_device(int* num_cus) {
   return state[dev] == 1 ? LAT_MOE_OK : LAT_MOE_EDEVICE;
 }
 
-int forward_impl(const void* x, const int32_t* idx, const float* w, const void* gu, const void* dn,
+int forward_impl(const void* x, const int32_t* idx, const float* w, const void* gu, const void* dn, int down_fmt,
                  const lat_moe_shapes* s, float* y, void* ws, size_t ws_bytes, void* stream,
                  const lat_moe_debug* dbg) {
   if (!shapes_ok(s)) return LAT_MOE_EINVAL;
+  if (down_fmt != LAT_MOE_DOWN_IQ4_NL && down_fmt != LAT_MOE_DOWN_Q4_0) return LAT_MOE_EINVAL;
   if (s->T > 0) {
     const void* ptrs[] = {x, idx, w, gu, dn, y, ws};
     for (const void* p : ptrs)
@@ -138,8 +139,9 @@ int forward_impl(const void* x, const int32_t* idx, const float* w, const void* 
              : launch_gateup(sh, wk, gub, pg.out ? &pg : nullptr, st)) != hipSuccess)
     return LAT_MOE_ELAUNCH;
   if (mark(2) != hipSuccess) return LAT_MOE_ELAUNCH;
-  if ((small ? launch_down_small(dnb, w, sh, wk, pd.out ? &pd : nullptr, st)
-             : launch_down(dnb, w, sh, wk, pd.out ? &pd : nullptr, st)) != hipSuccess)
+  const int fmt = down_fmt == LAT_MOE_DOWN_Q4_0 ? kDownQ40 : kDownIq4Nl;
+  if ((small ? launch_down_small(dnb, fmt, w, sh, wk, pd.out ? &pd : nullptr, st)
+             : launch_down(dnb, fmt, w, sh, wk, pd.out ? &pd : nullptr, st)) != hipSuccess)
     return LAT_MOE_ELAUNCH;
   if (mark(3) != hipSuccess) return LAT_MOE_ELAUNCH;
   if (launch_combine(idx, sh, wk, y, st) != hipSuccess) return LAT_MOE_ELAUNCH;
@@ -167,8 +169,8 @@ size_t lat_moe_workspace_size(const lat_moe_shapes* shapes) {
 int lat_moe_expert_forward(const void* x_q8_1, const int32_t* router_idx, const float* router_w,
                            const void* gateup_q3k, const void* down_iq4nl, const lat_moe_shapes* shapes, float* y,
                            void* workspace, size_t workspace_bytes, void* stream) {
-  return forward_impl(x_q8_1, router_idx, router_w, gateup_q3k, down_iq4nl, shapes, y, workspace, workspace_bytes,
-                      stream, nullptr);
+  return forward_impl(x_q8_1, router_idx, router_w, gateup_q3k, down_iq4nl, LAT_MOE_DOWN_IQ4_NL, shapes, y, workspace,
+                      workspace_bytes, stream, nullptr);
 }
 
 int lat_moe_expert_forward_debug(const void* x_q8_1, const int32_t* router_idx, const float* router_w,
@@ -176,8 +178,16 @@ int lat_moe_expert_forward_debug(const void* x_q8_1, const int32_t* router_idx, 
                                  float* y, void* workspace, size_t workspace_bytes, void* stream,
                                  const lat_moe_debug* dbg) {
   if (!dbg) return LAT_MOE_EINVAL;
-  return forward_impl(x_q8_1, router_idx, router_w, gateup_q3k, down_iq4nl, shapes, y, workspace, workspace_bytes,
-                      stream, dbg);
+  return forward_impl(x_q8_1, router_idx, router_w, gateup_q3k, down_iq4nl, LAT_MOE_DOWN_IQ4_NL, shapes, y, workspace,
+                      workspace_bytes, stream, dbg);
+}
+
+int lat_moe_expert_forward_ex(const void* x_q8_1, const int32_t* router_idx, const float* router_w,
+                              const void* gateup_q3k, const void* down, int32_t down_format,
+                              const lat_moe_shapes* shapes, float* y, void* workspace, size_t workspace_bytes,
+                              void* stream, const lat_moe_debug* dbg) {
+  return forward_impl(x_q8_1, router_idx, router_w, gateup_q3k, down, down_format, shapes, y, workspace,
+                      workspace_bytes, stream, dbg);
 }
 
 int lat_moe_quantize_q8_1(const float* x, int64_t rows, int32_t cols, void* out_q8_1, void* stream) {

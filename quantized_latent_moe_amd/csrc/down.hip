@@ -35,7 +35,7 @@ constexpr int kRawHalfPer = kRawHalf / kThreads;               // 9
 static_assert(kRawHalf % kThreads == 0, "staging split");
 static_assert(kNT * 16 == 2 * kThreads && kNT * 8 == kThreads && kLT * 8 == kThreads, "staging split");
 
-template <bool PROBE, bool ALIGNED16>
+template <bool PROBE, bool ALIGNED16, int FMT>
 __global__ __launch_bounds__(kThreads) void k_down_generic(const uint8_t* __restrict__ dn, const float* __restrict__ router_w,
                                                    const int32_t* __restrict__ perm,
                                                    const int32_t* __restrict__ tiles,
@@ -152,8 +152,8 @@ __global__ __launch_bounds__(kThreads) void k_down_generic(const uint8_t* __rest
         uint32_t o[8];
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          o[w] = iq4_lookup(qw[w] & 0x0f0f0f0fu);             // values 4w .. 4w+3
-          o[4 + w] = iq4_lookup((qw[w] >> 4) & 0x0f0f0f0fu);  // values 16+4w ..
+          o[w] = down_lookup<FMT>(qw[w] & 0x0f0f0f0fu);             // values 4w .. 4w+3
+          o[4 + w] = down_lookup<FMT>((qw[w] >> 4) & 0x0f0f0f0fu);  // values 16+4w ..
         }
         dst[0] = uint4{o[0], o[1], o[2], o[3]};
         dst[1] = uint4{o[4], o[5], o[6], o[7]};
@@ -282,7 +282,7 @@ __device__ __forceinline__ DItem ditem(int i, int nlt, const int32_t* tiles, con
   return it;
 }
 
-template <bool PROBE>
+template <bool PROBE, int FMT>
 __global__ __launch_bounds__(kWsThreads) void k_down(const uint8_t* __restrict__ dn, const float* __restrict__ router_w,
                                                      const int32_t* __restrict__ perm,
                                                      const int32_t* __restrict__ tiles,
@@ -414,10 +414,10 @@ __global__ __launch_bounds__(kWsThreads) void k_down(const uint8_t* __restrict__
           nib[jj] = (ob & 3) ? __builtin_amdgcn_alignbyte(w[(ob >> 2) + 1], w[ob >> 2], ob & 3) : w[ob >> 2];
         }
         // element l < 16: low nibble of byte l; element l + 16: high nibble
-        const uint4 lo = {iq4_lookup(nib[0] & 0x0f0f0f0fu), iq4_lookup(nib[1] & 0x0f0f0f0fu),
-                          iq4_lookup(nib[2] & 0x0f0f0f0fu), iq4_lookup(nib[3] & 0x0f0f0f0fu)};
-        const uint4 hi = {iq4_lookup((nib[0] >> 4) & 0x0f0f0f0fu), iq4_lookup((nib[1] >> 4) & 0x0f0f0f0fu),
-                          iq4_lookup((nib[2] >> 4) & 0x0f0f0f0fu), iq4_lookup((nib[3] >> 4) & 0x0f0f0f0fu)};
+        const uint4 lo = {down_lookup<FMT>(nib[0] & 0x0f0f0f0fu), down_lookup<FMT>(nib[1] & 0x0f0f0f0fu),
+                          down_lookup<FMT>(nib[2] & 0x0f0f0f0fu), down_lookup<FMT>(nib[3] & 0x0f0f0f0fu)};
+        const uint4 hi = {down_lookup<FMT>((nib[0] >> 4) & 0x0f0f0f0fu), down_lookup<FMT>((nib[1] >> 4) & 0x0f0f0f0fu),
+                          down_lookup<FMT>((nib[2] >> 4) & 0x0f0f0f0fu), down_lookup<FMT>((nib[3] >> 4) & 0x0f0f0f0fu)};
         const int kg = 4 * hb + kk;
         *reinterpret_cast<uint4*>(As[b] + swz(r, 2 * kg)) = lo;
         *reinterpret_cast<uint4*>(As[b] + swz(r, 2 * kg + 1)) = hi;
@@ -566,21 +566,20 @@ __global__ __launch_bounds__(kWsThreads) void k_down(const uint8_t* __restrict__
   else consumer_loop(std::integral_constant<int, 0>{});
 }
 
-template <bool PROBE>
+template <bool PROBE, int FMT>
 void launch_variant(bool aligned, dim3 grid, hipStream_t st, const uint8_t* dn, const float* router_w,
                     const Shapes& s, const Work& w, ProbeRows probe) {
   if (aligned)
-    hipLaunchKernelGGL((k_down_generic<PROBE, true>), grid, dim3(kThreads), 0, st, dn, router_w, w.perm, w.tiles, w.offsets,
-                       w.misc, s.L, s.F, w.h_codes, w.h_ds, w.slots, probe);
+    hipLaunchKernelGGL((k_down_generic<PROBE, true, FMT>), grid, dim3(kThreads), 0, st, dn, router_w, w.perm, w.tiles,
+                       w.offsets, w.misc, s.L, s.F, w.h_codes, w.h_ds, w.slots, probe);
   else
-    hipLaunchKernelGGL((k_down_generic<PROBE, false>), grid, dim3(kThreads), 0, st, dn, router_w, w.perm, w.tiles, w.offsets,
-                       w.misc, s.L, s.F, w.h_codes, w.h_ds, w.slots, probe);
+    hipLaunchKernelGGL((k_down_generic<PROBE, false, FMT>), grid, dim3(kThreads), 0, st, dn, router_w, w.perm, w.tiles,
+                       w.offsets, w.misc, s.L, s.F, w.h_codes, w.h_ds, w.slots, probe);
 }
 
-}  // namespace
-
-hipError_t launch_down(const uint8_t* dn, const float* router_w, const Shapes& s, const Work& w,
-                       const ProbeRows* probe, hipStream_t st) {
+template <int FMT>
+void launch_fmt(const uint8_t* dn, const float* router_w, const Shapes& s, const Work& w, const ProbeRows* probe,
+                hipStream_t st) {
   const ProbeRows none = {nullptr, 0, 0};
   if (s.F % 256 == 0 && ((uintptr_t)dn & 15u) == 0) {
     // one persistent workgroup per CU, a multiple of the XCD count
@@ -588,21 +587,31 @@ hipError_t launch_down(const uint8_t* dn, const float* router_w, const Shapes& s
     if (grid < kXcds) grid = kXcds;
     const int pairs = (int)s.pairs();
     if (probe)
-      hipLaunchKernelGGL(k_down<true>, dim3(grid), dim3(kWsThreads), 0, st, dn, router_w, w.perm, w.tiles, w.offsets,
-                         w.misc, pairs, s.L, s.F, w.h_codes, w.h_ds, w.slots, *probe);
+      hipLaunchKernelGGL((k_down<true, FMT>), dim3(grid), dim3(kWsThreads), 0, st, dn, router_w, w.perm, w.tiles,
+                         w.offsets, w.misc, pairs, s.L, s.F, w.h_codes, w.h_ds, w.slots, *probe);
     else
-      hipLaunchKernelGGL(k_down<false>, dim3(grid), dim3(kWsThreads), 0, st, dn, router_w, w.perm, w.tiles,
+      hipLaunchKernelGGL((k_down<false, FMT>), dim3(grid), dim3(kWsThreads), 0, st, dn, router_w, w.perm, w.tiles,
                          w.offsets, w.misc, pairs, s.L, s.F, w.h_codes, w.h_ds, w.slots, none);
-    return hipGetLastError();
+    return;
   }
   const dim3 grid(w.max_tiles, s.L / kLT);
   // 16-byte staging needs every row (and so every 8-block step) 16-byte aligned;
   // that also means F is a multiple of 256, so every step is a full 144-byte chunk.
   const bool aligned = ((int64_t)(s.F / 32) * kIq4Bytes) % 16 == 0 && ((uintptr_t)dn & 15u) == 0;
   if (probe)
-    launch_variant<true>(aligned, grid, st, dn, router_w, s, w, *probe);
+    launch_variant<true, FMT>(aligned, grid, st, dn, router_w, s, w, *probe);
   else
-    launch_variant<false>(aligned, grid, st, dn, router_w, s, w, none);
+    launch_variant<false, FMT>(aligned, grid, st, dn, router_w, s, w, none);
+}
+
+}  // namespace
+
+hipError_t launch_down(const uint8_t* dn, int fmt, const float* router_w, const Shapes& s, const Work& w,
+                       const ProbeRows* probe, hipStream_t st) {
+  if (fmt == kDownQ40)
+    launch_fmt<kDownQ40>(dn, router_w, s, w, probe, st);
+  else
+    launch_fmt<kDownIq4Nl>(dn, router_w, s, w, probe, st);
   return hipGetLastError();
 }
 

@@ -140,6 +140,22 @@ __device__ __forceinline__ uint32_t iq4_lookup(uint32_t nib) {
   return __builtin_amdgcn_perm(hi, lo, pick);
 }
 
+// Down weight formats.  Both are 18-byte blocks of 32 weights: fp16 d, then 16
+// bytes of 4-bit indices (element i < 16 in the low nibble of byte i, element
+// i >= 16 in the high nibble of byte i - 16); they differ in what an index is
+// worth: IQ4_NL's non-linear table, or Q4_0's index - 8 (ggml's block
+// formats; Q4_0 is one of the weight formats named in section "Not done" of
+// the PR page "Run Edge0-145B Q3_K on AMD HIP (Linux, gfx1100) #1").
+enum DownFormat : int { kDownIq4Nl = 0, kDownQ40 = 1 };
+// 4 indices (one per byte, each 0..15) -> their 4 int8 weights.
+template <int FMT>
+__device__ __forceinline__ uint32_t down_lookup(uint32_t nib) {
+  if constexpr (FMT == kDownQ40)
+    return (nib + 0x78787878u) ^ 0x80808080u;  // index - 8 per byte (index + 0x78 <= 0x87: no carry out)
+  else
+    return iq4_lookup(nib);
+}
+
 // Raw buffer loads (gfx9 buffer resource, stride 0).  A load whose 32-bit
 // offset is at or past num_records returns zero without touching memory, so
 // padding lanes load from kOutOfRange instead of branching around the load.
@@ -163,7 +179,7 @@ __device__ __forceinline__ uint4 buf_u128(rsrc_t r, int voff, int soff) {
 // Sorts pairs by expert and splits the q8_1 activations x into codes and scales.
 hipError_t launch_route(const int32_t* idx, const uint8_t* x, const Shapes& s, const Work& w, hipStream_t st);
 hipError_t launch_gateup(const Shapes& s, const Work& w, const uint8_t* gu, const ProbeRows* probe, hipStream_t st);
-hipError_t launch_down(const uint8_t* dn, const float* router_w, const Shapes& s, const Work& w,
+hipError_t launch_down(const uint8_t* dn, int fmt, const float* router_w, const Shapes& s, const Work& w,
                        const ProbeRows* probe, hipStream_t st);
 // Batches of at most kSmallMaxPairs pairs (L <= 1024, F <= 2048) take the
 // GEMV-shaped gate/up and down kernels.
@@ -171,7 +187,7 @@ constexpr int kSmallMaxPairs = 64;
 bool small_path(const Shapes& s);
 hipError_t launch_gateup_small(const Shapes& s, const Work& w, const uint8_t* gu, const ProbeRows* probe,
                                hipStream_t st);
-hipError_t launch_down_small(const uint8_t* dn, const float* router_w, const Shapes& s, const Work& w,
+hipError_t launch_down_small(const uint8_t* dn, int fmt, const float* router_w, const Shapes& s, const Work& w,
                              const ProbeRows* probe, hipStream_t st);
 hipError_t launch_combine(const int32_t* idx, const Shapes& s, const Work& w, float* y, hipStream_t st);
 hipError_t launch_quantize_q8_1(const float* x, int64_t rows, int cols, uint8_t* out, hipStream_t st);

@@ -208,7 +208,7 @@ __global__ __launch_bounds__(kSmallThreads) void k_gateup_small(
 // ---------------------------------------------------------------------------
 // Down: workgroup (tile j -> expert, 32 output rows l0).  Threads: row r = t
 // >> 3, K slice q = t & 7 (blocks q, q + 8, ...).
-template <bool PROBE>
+template <bool PROBE, int FMT>
 __global__ __launch_bounds__(kSmallThreads) void k_down_small(
     const uint8_t* __restrict__ dn, const float* __restrict__ router_w, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ tiles, const int32_t* __restrict__ offsets, const int32_t* __restrict__ misc,
@@ -285,8 +285,8 @@ __global__ __launch_bounds__(kSmallThreads) void k_down_small(
       uint32_t op[8];
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        op[w] = iq4_lookup(nibs[w] & 0x0f0f0f0fu);             // elements 4w .. 4w+3
-        op[4 + w] = iq4_lookup((nibs[w] >> 4) & 0x0f0f0f0fu);  // elements 16+4w ..
+        op[w] = down_lookup<FMT>(nibs[w] & 0x0f0f0f0fu);             // elements 4w .. 4w+3
+        op[4 + w] = down_lookup<FMT>((nibs[w] >> 4) & 0x0f0f0f0fu);  // elements 16+4w ..
       }
 #pragma unroll
       for (int tk = 0; tk < kSmallTok; ++tk) {
@@ -344,18 +344,31 @@ hipError_t launch_gateup_small(const Shapes& s, const Work& w, const uint8_t* gu
   return hipGetLastError();
 }
 
-hipError_t launch_down_small(const uint8_t* dn, const float* router_w, const Shapes& s, const Work& w,
-                             const ProbeRows* probe, hipStream_t st) {
+namespace {
+
+template <int FMT>
+void launch_down_small_fmt(const uint8_t* dn, const float* router_w, const Shapes& s, const Work& w,
+                           const ProbeRows* probe, hipStream_t st) {
   const int nfb = s.F / 32;
   const size_t lds = kSmallTok * s.F + 4 * kSmallTok * nfb;
   const dim3 grid((unsigned)(s.pairs() < s.E ? s.pairs() : s.E), s.L / 32);
   const ProbeRows none = {nullptr, 0, 0};
   if (probe)
-    hipLaunchKernelGGL(k_down_small<true>, grid, dim3(kSmallThreads), lds, st, dn, router_w, w.perm, w.tiles,
+    hipLaunchKernelGGL((k_down_small<true, FMT>), grid, dim3(kSmallThreads), lds, st, dn, router_w, w.perm, w.tiles,
                        w.offsets, w.misc, (int)s.pairs(), s.L, s.F, w.h_codes, w.h_ds, w.slots, *probe);
   else
-    hipLaunchKernelGGL(k_down_small<false>, grid, dim3(kSmallThreads), lds, st, dn, router_w, w.perm, w.tiles,
+    hipLaunchKernelGGL((k_down_small<false, FMT>), grid, dim3(kSmallThreads), lds, st, dn, router_w, w.perm, w.tiles,
                        w.offsets, w.misc, (int)s.pairs(), s.L, s.F, w.h_codes, w.h_ds, w.slots, none);
+}
+
+}  // namespace
+
+hipError_t launch_down_small(const uint8_t* dn, int fmt, const float* router_w, const Shapes& s, const Work& w,
+                             const ProbeRows* probe, hipStream_t st) {
+  if (fmt == kDownQ40)
+    launch_down_small_fmt<kDownQ40>(dn, router_w, s, w, probe, st);
+  else
+    launch_down_small_fmt<kDownIq4Nl>(dn, router_w, s, w, probe, st);
   return hipGetLastError();
 }
 
