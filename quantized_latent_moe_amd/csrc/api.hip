@@ -30,7 +30,7 @@ bool shapes_ok(const lat_moe_shapes* s) {
 }
 
 struct Layout {
-  size_t chunk_hist, chunk_bad, offsets, misc, tiles, perm, h_codes, h_ds, slots, xc, xd, total;
+  size_t chunk_hist, chunk_bad, offsets, misc, tiles, perm, h_codes, h_ds, slots, xc, xd, xg, xgd, total;
   int nchunk, max_tiles;
 };
 
@@ -44,13 +44,15 @@ Layout layout(const lat_moe_shapes* s) {
   L.chunk_bad = o;  o = align_up(o + sizeof(int32_t) * (size_t)L.nchunk);
   L.offsets = o;    o = align_up(o + sizeof(int32_t) * (size_t)(s->E + 1));
   L.misc = o;       o = align_up(o + sizeof(int32_t) * kMiscWords);
-  L.tiles = o;      o = align_up(o + sizeof(int32_t) * 2 * (size_t)L.max_tiles);
+  L.tiles = o;      o = align_up(o + sizeof(int32_t) * kTileWords * (size_t)L.max_tiles);
   L.perm = o;       o = align_up(o + sizeof(int32_t) * (size_t)P);
   L.h_codes = o;    o = align_up(o + (size_t)P * s->F);
   L.h_ds = o;       o = align_up(o + sizeof(uint32_t) * (size_t)P * (s->F / 32));
   L.slots = o;      o = align_up(o + sizeof(float) * (size_t)P * s->L);
   L.xc = o;         o = align_up(o + (size_t)s->T * s->L);
   L.xd = o;         o = align_up(o + sizeof(float) * (size_t)s->T * (s->L / 32));
+  L.xg = o;         o = align_up(o + (size_t)kGatherRows * s->L);
+  L.xgd = o;        o = align_up(o + sizeof(float) * (size_t)kGatherRows * (s->L / 32));
   L.total = o;
   return L;
 }
@@ -69,6 +71,8 @@ Work carve(const Layout& L, void* ws) {
   w.slots = reinterpret_cast<float*>(b + L.slots);
   w.xc = reinterpret_cast<int8_t*>(b + L.xc);
   w.xd = reinterpret_cast<float*>(b + L.xd);
+  w.xg = reinterpret_cast<int8_t*>(b + L.xg);
+  w.xgd = reinterpret_cast<float*>(b + L.xgd);
   w.nchunk = L.nchunk;
   w.max_tiles = L.max_tiles;
   w.num_cus = 1;

@@ -53,9 +53,9 @@ __global__ __launch_bounds__(kThreads) void k_down_generic(const uint8_t* __rest
 
   const int tile = blockIdx.x;
   if (tile >= misc[kMiscTiles]) return;
-  const int e = tiles[2 * tile];
-  const int pos0 = tiles[2 * tile + 1];
-  const int cnt = min(kNT, offsets[e + 1] - pos0);
+  const int e = tiles[kTileWords * tile];
+  const int pos0 = tiles[kTileWords * tile + 1];
+  const int cnt = tiles[kTileWords * tile + 2];  // at most kTileN == kNT
   const int l0 = blockIdx.y * kLT;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lsub = wave & 3, tsub = wave >> 2;
@@ -272,13 +272,13 @@ struct DItem {
   int e, pos0, cnt, l0;
 };
 
-__device__ __forceinline__ DItem ditem(int i, int nlt, const int32_t* tiles, const int32_t* offsets) {
+__device__ __forceinline__ DItem ditem(int i, int nlt, const int32_t* tiles) {
   DItem it;
   const int tile = i / nlt;
   it.l0 = (i - tile * nlt) * kWsLT;
-  it.e = tiles[2 * tile];
-  it.pos0 = tiles[2 * tile + 1];
-  it.cnt = min(kWsNT, offsets[it.e + 1] - it.pos0);
+  it.e = tiles[kTileWords * tile];
+  it.pos0 = tiles[kTileWords * tile + 1];
+  it.cnt = tiles[kTileWords * tile + 2];  // at most kTileN == kWsNT
   return it;
 }
 
@@ -331,7 +331,7 @@ __global__ __launch_bounds__(kWsThreads) void k_down(const uint8_t* __restrict__
     int lj = 0, lsb = 0, ql0 = -1;
     bool need_setup = true;
     auto setup = [&](int j) {
-      const DItem it = ditem(item_of(j), nlt, tiles, offsets);
+      const DItem it = ditem(item_of(j), nlt, tiles);
       const int e = __builtin_amdgcn_readfirstlane(it.e);
       rw_src = make_rsrc(dn + (int64_t)e * L * row_bytes, (uint32_t)(L * row_bytes));
       if (it.l0 != ql0) {  // once per workgroup when the grid is a multiple of nlt
@@ -452,7 +452,7 @@ __global__ __launch_bounds__(kWsThreads) void k_down(const uint8_t* __restrict__
   for (int i = 0; i < 16; ++i) magic[i] = kMagicBits;
   float acc0[16], acc1[16];
   int cj = 0, csb = 0;
-  DItem cur = ditem(item_of(0), nlt, tiles, offsets);
+  DItem cur = ditem(item_of(0), nlt, tiles);
   int pair0 = -1, pair1 = -1;
   float w0 = 0.f, w1 = 0.f;
   // one K step over both halves (TWO) or the first only
@@ -557,7 +557,7 @@ __global__ __launch_bounds__(kWsThreads) void k_down(const uint8_t* __restrict__
           }
         }
         csb = 0;
-        if (++cj < my_items) cur = ditem(item_of(cj), nlt, tiles, offsets);
+        if (++cj < my_items) cur = ditem(item_of(cj), nlt, tiles);
       }
       __syncthreads();
     }

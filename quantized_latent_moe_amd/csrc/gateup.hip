@@ -66,13 +66,13 @@ struct Item {
   int e, pos0, cnt, f0;
 };
 
-__device__ __forceinline__ Item item_info(int i, int nft, const int32_t* tiles, const int32_t* offsets) {
+__device__ __forceinline__ Item item_info(int i, int nft, const int32_t* tiles) {
   Item it;
   const int tile = i / nft;
   it.f0 = (i - tile * nft) * kFT;
-  it.e = tiles[2 * tile];
-  it.pos0 = tiles[2 * tile + 1];
-  it.cnt = min(kNT, offsets[it.e + 1] - it.pos0);
+  it.e = tiles[kTileWords * tile];
+  it.pos0 = tiles[kTileWords * tile + 1];
+  it.cnt = tiles[kTileWords * tile + 2];  // at most kTileN == kNT
   return it;
 }
 
@@ -130,12 +130,12 @@ __global__ __launch_bounds__(kThreads) void k_gateup(const int8_t* __restrict__ 
   bool need_setup = true;
   auto fetch_ids = [&](int j) {
     if (j < my_items) {
-      const Item it = item_info(item_of(j), nft, tiles, offsets);
+      const Item it = item_info(item_of(j), nft, tiles);
       if (ptid < kNT) ids[j & 1][ptid] = ptid < it.cnt ? perm[it.pos0 + ptid] / k : -1;
     }
   };
   auto setup = [&](int j) {
-    const Item it = item_info(item_of(j), nft, tiles, offsets);
+    const Item it = item_info(item_of(j), nft, tiles);
     const int e = __builtin_amdgcn_readfirstlane(it.e);  // uniform: the descriptor lives in SGPRs
     rw_src = make_rsrc(gu + (int64_t)e * 2 * F * row_bytes, (uint32_t)(2 * F * row_bytes));
     if (it.f0 != qf0) {  // once per workgroup when the grid is a multiple of nft
@@ -254,7 +254,7 @@ __global__ __launch_bounds__(kThreads) void k_gateup(const int8_t* __restrict__ 
   const v16i zero = {};
   float accg[16], accu[16];
   int cj = 0, csb = 0;  // item index and super-block of the MFMA step
-  Item cur = item_info(item_of(0), nft, tiles, offsets);
+  Item cur = item_info(item_of(0), nft, tiles);
 
   auto mfma_step = [&](auto grp_tag, int b) {
     constexpr int GRP = decltype(grp_tag)::value;
@@ -402,7 +402,7 @@ __global__ __launch_bounds__(kThreads) void k_gateup(const int8_t* __restrict__ 
         if (++csb == nsb) {
           epilogue();
           csb = 0;
-          if (++cj < my_items) cur = item_info(item_of(cj), nft, tiles, offsets);
+          if (++cj < my_items) cur = item_info(item_of(cj), nft, tiles);
         }
         __syncthreads();
       }

@@ -20,6 +20,11 @@ constexpr int kQ81Bytes = 36;    // 32 values
 constexpr int kRouteChunk = 1024;
 // Token (sorted pair) tile of the grouped GEMMs.
 constexpr int kTileN = 128;
+// Tile table entry: (expert, first sorted position, pairs in the tile, 0).
+constexpr int kTileWords = 4;
+// Batches of at most this many pairs also get their activation rows gathered
+// in sorted order by the route pass (the small-batch kernels read them there).
+constexpr int kGatherRows = 64;
 
 // Slots of the small device status array written by the route scan.
 constexpr int kMiscTiles = 0;    // number of (expert, token tile) work items
@@ -39,13 +44,15 @@ struct Work {
   int32_t* chunk_bad;   // [nchunk]
   int32_t* offsets;     // [E+1]
   int32_t* misc;        // [kMiscWords]
-  int32_t* tiles;       // [max_tiles][2] (expert, first sorted position)
+  int32_t* tiles;       // [max_tiles][kTileWords] (expert, first sorted position, pairs, 0)
   int32_t* perm;        // [T*k] pair ids grouped by expert
   int8_t* h_codes;      // [T*k][F] H codes in sorted order
   uint32_t* h_ds;       // [T*k][F/32] fp16 d | fp16 s << 16
   float* slots;         // [T*k][L] weighted expert outputs in pair order
   int8_t* xc;           // [T][L] activation codes (q8_1 blocks split into codes ...)
   float* xd;            // [T][L/32] ... and fp32 block scales)
+  int8_t* xg;           // [kGatherRows][L] codes of the valid pairs' rows in sorted order (small batches)
+  float* xgd;           // [kGatherRows][L/32] their fp32 block scales
   int nchunk, max_tiles;
   int num_cus;          // compute units of the current device (persistent grids)
 };
@@ -183,7 +190,7 @@ hipError_t launch_down(const uint8_t* dn, int fmt, const float* router_w, const 
                        const ProbeRows* probe, hipStream_t st);
 // Batches of at most kSmallMaxPairs pairs (L <= 1024, F <= 2048) take the
 // GEMV-shaped gate/up and down kernels.
-constexpr int kSmallMaxPairs = 64;
+constexpr int kSmallMaxPairs = kGatherRows;
 bool small_path(const Shapes& s);
 hipError_t launch_gateup_small(const Shapes& s, const Work& w, const uint8_t* gu, const ProbeRows* probe,
                                hipStream_t st);

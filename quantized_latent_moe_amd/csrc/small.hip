@@ -7,8 +7,9 @@
 // streams the active experts' weights once.  One workgroup per (active
 // expert, 32 features) for gate/up and per (active expert, 32 output rows)
 // for down: it issues the loads of its rows (contiguous in memory, 16-byte
-// coalesced buffer loads) and of its tokens' rows together, stages them in
-// LDS, then each thread takes a K slice of one row and forms the 32-value
+// coalesced buffer loads) and of its tokens' rows together (gate/up reads the
+// rows the route pass gathered in sorted order, down the H rows, both found
+// from the tile entry alone), stages them in LDS, then each thread takes a K slice of one row and forms the 32-value
 // block dots with v_dot4 against up to kSmallTok tokens at a time; lane
 // shuffles sum the row's slices.  2-byte-aligned blocks are realigned with
 // v_alignbyte.
@@ -36,15 +37,13 @@ constexpr int kSmallThreads = 256;
 // slice q = t & 3 (super-blocks q, q + 4, ...).
 template <bool PROBE>
 __global__ __launch_bounds__(kSmallThreads) void k_gateup_small(
-    const int8_t* __restrict__ xc, const float* __restrict__ xd, const uint8_t* __restrict__ gu,
-    const int32_t* __restrict__ perm, const int32_t* __restrict__ tiles, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ misc, int T, int k, int L, int F, int8_t* __restrict__ h_codes,
-    uint32_t* __restrict__ h_ds, ProbeRows probe) {
+    const int8_t* __restrict__ xg, const float* __restrict__ xgd, const uint8_t* __restrict__ gu,
+    const int32_t* __restrict__ perm, const int32_t* __restrict__ tiles, const int32_t* __restrict__ misc, int L,
+    int F, int8_t* __restrict__ h_codes, uint32_t* __restrict__ h_ds, ProbeRows probe) {
   extern __shared__ __align__(16) uint8_t smem[];
   if ((int)blockIdx.x >= misc[kMiscTiles]) return;
-  const int e = tiles[2 * blockIdx.x];
-  const int pos0 = tiles[2 * blockIdx.x + 1];
-  const int cnt = min(kTileN, offsets[e + 1] - pos0);
+  const int4 te = *reinterpret_cast<const int4*>(tiles + kTileWords * blockIdx.x);
+  const int e = te.x, pos0 = te.y, cnt = te.z;  // cnt <= kGatherRows
   const int f0 = blockIdx.y * 32;
   const int tid = threadIdx.x, lane = tid & 63;
   const int nsb = L / 256, nxb = L / 32, nsub = L / 16, row_bytes = nsb * kQ3kBytes;
@@ -55,8 +54,9 @@ __global__ __launch_bounds__(kSmallThreads) void k_gateup_small(
   float* gus = reinterpret_cast<float*>(xsum + kSmallTok * nsub);
 
   const rsrc_t rw = make_rsrc(gu + (int64_t)e * 2 * F * row_bytes, (uint32_t)(2 * F * row_bytes));
-  const rsrc_t rx = make_rsrc(xc, (uint32_t)(T * L));
-  const rsrc_t rd = make_rsrc(xd, (uint32_t)(T * nxb * 4));
+  // the gathered rows: sorted position pos at xg + pos * L, xgd + pos * nxb
+  const rsrc_t rx = make_rsrc(xg, (uint32_t)(kGatherRows * L));
+  const rsrc_t rd = make_rsrc(xgd, (uint32_t)(kGatherRows * nxb * 4));
   constexpr int kXPer = kSmallTok * 1024 / 16 / kSmallThreads;  // 2
   const int r = tid >> 2, q = tid & 3;
   const int wrow = r < 32 ? f0 + r : F + f0 + r - 32;  // weight row of the expert
@@ -78,7 +78,7 @@ __global__ __launch_bounds__(kSmallThreads) void k_gateup_small(
   }
   for (int g0 = 0; g0 < cnt; g0 += kSmallTok) {
     const int nt = min(kSmallTok, cnt - g0);
-    // ---- the group's token rows (pair ids read straight from perm)
+    // ---- the group's token rows, at their sorted positions
     uint4 xv[kXPer];
     uint32_t dv;
 #pragma unroll
@@ -86,14 +86,12 @@ __global__ __launch_bounds__(kSmallThreads) void k_gateup_small(
       const int i = tid + kSmallThreads * m;
       const int tk = i / (L / 16), c = i - tk * (L / 16);
       const bool ok = tk < nt && i < kSmallTok * (L / 16);
-      const int p = ok ? perm[pos0 + g0 + tk] : 0;
-      xv[m] = buf_u128(rx, ok ? (p / k) * L + 16 * c : kOutOfRange, 0);
+      xv[m] = buf_u128(rx, ok ? (pos0 + g0 + tk) * L + 16 * c : kOutOfRange, 0);
     }
     {
       const int tk = tid / nxb, b = tid - tk * nxb;
       const bool ok = tk < nt && tid < kSmallTok * nxb;
-      const int p = ok ? perm[pos0 + g0 + tk] : 0;
-      dv = buf_u32(rd, ok ? ((p / k) * nxb + b) * 4 : kOutOfRange, 0);
+      dv = buf_u32(rd, ok ? ((pos0 + g0 + tk) * nxb + b) * 4 : kOutOfRange, 0);
     }
     if (g0 > 0) __syncthreads();  // the previous group's reads of xs / gus are done
 #pragma unroll
@@ -211,14 +209,13 @@ __global__ __launch_bounds__(kSmallThreads) void k_gateup_small(
 template <bool PROBE, int FMT>
 __global__ __launch_bounds__(kSmallThreads) void k_down_small(
     const uint8_t* __restrict__ dn, const float* __restrict__ router_w, const int32_t* __restrict__ perm,
-    const int32_t* __restrict__ tiles, const int32_t* __restrict__ offsets, const int32_t* __restrict__ misc,
+    const int32_t* __restrict__ tiles, const int32_t* __restrict__ misc,
     int pairs, int L, int F, const int8_t* __restrict__ h_codes, const uint32_t* __restrict__ h_ds,
     float* __restrict__ slots, ProbeRows probe) {
   extern __shared__ __align__(16) uint8_t smem[];
   if ((int)blockIdx.x >= misc[kMiscTiles]) return;
-  const int e = tiles[2 * blockIdx.x];
-  const int pos0 = tiles[2 * blockIdx.x + 1];
-  const int cnt = min(kTileN, offsets[e + 1] - pos0);
+  const int4 te = *reinterpret_cast<const int4*>(tiles + kTileWords * blockIdx.x);
+  const int e = te.x, pos0 = te.y, cnt = te.z;  // cnt <= kSmallMaxPairs
   const int l0 = blockIdx.y * 32;
   const int tid = threadIdx.x;
   const int nfb = F / 32, row_bytes = nfb * kIq4Bytes;
@@ -336,11 +333,11 @@ hipError_t launch_gateup_small(const Shapes& s, const Work& w, const uint8_t* gu
   const dim3 grid((unsigned)(s.pairs() < s.E ? s.pairs() : s.E), s.F / 32);
   const ProbeRows none = {nullptr, 0, 0};
   if (probe)
-    hipLaunchKernelGGL(k_gateup_small<true>, grid, dim3(kSmallThreads), lds, st, w.xc, w.xd, gu, w.perm, w.tiles,
-                       w.offsets, w.misc, (int)s.T, s.k, s.L, s.F, w.h_codes, w.h_ds, *probe);
+    hipLaunchKernelGGL(k_gateup_small<true>, grid, dim3(kSmallThreads), lds, st, w.xg, w.xgd, gu, w.perm, w.tiles,
+                       w.misc, s.L, s.F, w.h_codes, w.h_ds, *probe);
   else
-    hipLaunchKernelGGL(k_gateup_small<false>, grid, dim3(kSmallThreads), lds, st, w.xc, w.xd, gu, w.perm, w.tiles,
-                       w.offsets, w.misc, (int)s.T, s.k, s.L, s.F, w.h_codes, w.h_ds, none);
+    hipLaunchKernelGGL(k_gateup_small<false>, grid, dim3(kSmallThreads), lds, st, w.xg, w.xgd, gu, w.perm, w.tiles,
+                       w.misc, s.L, s.F, w.h_codes, w.h_ds, none);
   return hipGetLastError();
 }
 
@@ -355,10 +352,10 @@ void launch_down_small_fmt(const uint8_t* dn, const float* router_w, const Shape
   const ProbeRows none = {nullptr, 0, 0};
   if (probe)
     hipLaunchKernelGGL((k_down_small<true, FMT>), grid, dim3(kSmallThreads), lds, st, dn, router_w, w.perm, w.tiles,
-                       w.offsets, w.misc, (int)s.pairs(), s.L, s.F, w.h_codes, w.h_ds, w.slots, *probe);
+                       w.misc, (int)s.pairs(), s.L, s.F, w.h_codes, w.h_ds, w.slots, *probe);
   else
     hipLaunchKernelGGL((k_down_small<false, FMT>), grid, dim3(kSmallThreads), lds, st, dn, router_w, w.perm, w.tiles,
-                       w.offsets, w.misc, (int)s.pairs(), s.L, s.F, w.h_codes, w.h_ds, w.slots, none);
+                       w.misc, (int)s.pairs(), s.L, s.F, w.h_codes, w.h_ds, w.slots, none);
 }
 
 }  // namespace

@@ -93,6 +93,9 @@ SMALL = [
     Workload("wide_k", T=48, L=512, F=256, E=12, k=10, zipf_s=1.1, seed=11),
     # more than 512 experts (the chunked route passes at a small batch)
     Workload("many_experts", T=64, L=256, F=128, E=600, k=4, seed=12),
+    # a small batch with more than 512 experts (routed by the chunked passes,
+    # rows gathered by their own kernel)
+    Workload("small_batch_many_experts", T=6, L=512, F=256, E=700, k=8, seed=17),
     # the largest expert count, one expert per token
     Workload("max_experts_k1", T=300, L=256, F=256, E=1024, k=1, seed=13),
     # one token
@@ -176,6 +179,30 @@ def test_invalid_and_duplicate_ids():
     _check_probes(out, I, xq, (0, 2 * wl.F), (0, wl.L))
     check_h(out["h"], ref.h, label="edge")
     check_y(out["y"], stagewise_y(out, I), label="edge stage-wise")
+
+
+def test_small_batch_invalid_and_duplicate_ids():
+    """The small-batch kernels (at most 64 pairs) with dropped and repeated ids:
+    only the valid pairs' rows are gathered, in sorted order."""
+    wl = Workload("edge_small", T=9, L=256, F=96, E=5, k=3, seed=18)
+    I, xq = _case(wl)
+    idx = I.router_idx.copy()
+    idx[0, :] = [-1, 5, 1 << 20]
+    idx[1, :] = [2, 2, 2]
+    idx[4, 2] = -3
+    I.router_idx[...] = idx
+    ref = oracle.forward(xq, idx, I.router_w, I.gateup_q3k, I.down_iq4nl, wl.L, wl.F, wl.E)
+    g = Gpu(I, xq)
+    out = g.forward_debug(gu_rows=(0, 2 * wl.F), dn_rows=(0, wl.L))
+    _check_routing(out, I)
+    assert out["dropped"] == ref.dropped == 4
+    assert (out["y"][0] == 0).all()
+    _check_probes(out, I, xq, (0, 2 * wl.F), (0, wl.L))
+    check_h(out["h"], ref.h, label="edge_small")
+    check_y(out["y"], stagewise_y(out, I), label="edge_small stage-wise")
+    # every id invalid: no tile, nothing gathered, y = 0
+    g.set_routing(np.full((wl.T, wl.k), 7, np.int32), I.router_w)
+    assert (g.forward() == 0).all()
 
 
 def test_all_invalid_and_zero_weights():
