@@ -219,11 +219,12 @@ int lat_moe_dense_q8_0_debug(const void* x_q8_1, const void* w_q8_0, int64_t T, 
     if (!p || !aligned16(p)) return LAT_MOE_EINVAL;
   if ((y_f32 && !aligned16(y_f32)) || (y_q8_1 && !aligned16(y_q8_1)) || (dots_i32 && !aligned16(dots_i32)))
     return LAT_MOE_EINVAL;
-  int rc = check_device(nullptr);
+  int num_cus = 1;
+  int rc = check_device(&num_cus);
   if (rc != LAT_MOE_OK) return rc;
   const ProbeRows probe{dots_i32, row0, rows};
   if (launch_dense_q8_0(static_cast<const uint8_t*>(x_q8_1), static_cast<const uint8_t*>(w_q8_0), T, N, K, y_f32,
-                        static_cast<uint8_t*>(y_q8_1), dots_i32 ? &probe : nullptr,
+                        static_cast<uint8_t*>(y_q8_1), dots_i32 ? &probe : nullptr, num_cus,
                         static_cast<hipStream_t>(stream)) != hipSuccess)
     return LAT_MOE_ELAUNCH;
   return LAT_MOE_OK;

@@ -505,7 +505,7 @@ bool small_config(int64_t T, int nb, int* bpl, int* lpr) {
 }  // namespace
 
 hipError_t launch_dense_q8_0(const uint8_t* x, const uint8_t* w, int64_t T, int N, int K, float* y_f32,
-                             uint8_t* y_q8, const ProbeRows* probe, hipStream_t st) {
+                             uint8_t* y_q8, const ProbeRows* probe, int num_cus, hipStream_t st) {
   int bpl = 0, lpr = 0;
   if (small_config(T, K / 32, &bpl, &lpr)) {
     const int t = (int)T;
@@ -517,6 +517,7 @@ hipError_t launch_dense_q8_0(const uint8_t* x, const uint8_t* w, int64_t T, int 
     else launch_small<4, 64>(x, w, t, N, K, y_f32, y_q8, probe, st);
     return hipGetLastError();
   }
+  if (dense_ws_fits(T, N, K)) return launch_dense_ws(x, w, T, N, K, y_f32, y_q8, probe, num_cus, st);
   const int n_rt = (N + kRowsWG - 1) / kRowsWG;
   const int n_tt = (int)((T + kTokWG - 1) / kTokWG);
   const int items = n_rt * n_tt;

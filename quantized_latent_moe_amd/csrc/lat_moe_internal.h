@@ -205,6 +205,10 @@ hipError_t launch_router_topk(const float* logits, int64_t T, int E, int k, int3
 // Latent D / U dense projection, Q8_0 weights [N][K/32] x q8_1 rows [T][K/32]
 // -> fp32 [T][N] and/or q8_1 [T][N/32] (either output may be null).
 hipError_t launch_dense_q8_0(const uint8_t* x, const uint8_t* w, int64_t T, int N, int K, float* y_f32,
-                             uint8_t* y_q8, const ProbeRows* probe, hipStream_t st);
+                             uint8_t* y_q8, const ProbeRows* probe, int num_cus, hipStream_t st);
+// The persistent warp-specialized form, for T >= 128, N % 128 == 0, K % 256 == 0.
+bool dense_ws_fits(int64_t T, int N, int K);
+hipError_t launch_dense_ws(const uint8_t* x, const uint8_t* w, int64_t T, int N, int K, float* y_f32, uint8_t* y_q8,
+                           const ProbeRows* probe, int num_cus, hipStream_t st);
 
 }  // namespace latmoe

@@ -113,6 +113,11 @@ SMALL = [
     (4, 64, 8192, 12),     # 256 blocks: four a lane (batches of at most 4)
     (7, 32, 1056, 13),     # 33 blocks, a partly idle lane group
     (9, 64, 256, 14),      # one token more: the MFMA kernel
+    # the persistent warp-specialized kernel (T >= 128, N % 128 == 0, K % 256 == 0)
+    (300, 256, 512, 15),   # two full token tiles and a 44-token tail (one 32-token half)
+    (129, 128, 256, 16),   # a one-token tail tile, one K step
+    (200, 384, 768, 17),   # three K steps, a 72-token tail (both halves, the second partial)
+    (640, 1024, 4096, 18), # D-shaped, five full token tiles
 ]
 
 
