@@ -63,6 +63,8 @@ def lib() -> ctypes.CDLL:
         c.orc_dequant_q8_0.argtypes = [P, i64, P]
         c.orc_dense_q8_0.argtypes = [P, i64, P, i32, i32, P, i64, P]
         c.orc_probe_dense.argtypes = [P, i64, P, i32, i32, i64, P, P, P]
+        c.orc_dense_fmt.argtypes = [P, i64, P, i32, i32, i32, P, i64, P]
+        c.orc_probe_dense_fmt.argtypes = [P, i64, P, i32, i32, i32, i64, P, P, P]
         c.orc_router_topk.argtypes = [P, i64, i32, i32, P, P]
         c.orc_num_threads.restype = ctypes.c_int
         c.orc_set_num_threads.argtypes = [ctypes.c_int]
@@ -235,20 +237,24 @@ def dequant_q8_0(blocks: np.ndarray) -> np.ndarray:
     return out.reshape(b.shape[:-1] + (32,))
 
 
+DENSE_FORMATS = {"q8_0": 0, "q4_0": 1}
+
+
 def dense_q8_0(x_q8: np.ndarray, w_q8_0: np.ndarray, N: int, K: int,
-               tokens: Optional[Sequence[int]] = None) -> np.ndarray:
+               tokens: Optional[Sequence[int]] = None, w_format: str = "q8_0") -> np.ndarray:
     """Latent D / U projection: x q8_1 [T, K/32, 36] against Q8_0 weights
-    [N, K/32, 34] -> fp64 [n_tok, N] (block dots folded in fp64)."""
+    [N, K/32, 34] (or, w_format "q4_0", Q4_0 weights [N, K/32, 18]) -> fp64
+    [n_tok, N] (block dots folded in fp64)."""
     x = _c(x_q8, np.uint8)
     T = x.size // ((K // 32) * 36)
     tok = None if tokens is None else _c(tokens, np.int64)
     n_tok = T if tok is None else tok.size
     y = np.zeros((n_tok, N), np.float64)
-    lib().orc_dense_q8_0(_p(x), T, _p(_c(w_q8_0, np.uint8)), N, K, _p(tok), n_tok, _p(y))
+    lib().orc_dense_fmt(_p(x), T, _p(_c(w_q8_0, np.uint8)), DENSE_FORMATS[w_format], N, K, _p(tok), n_tok, _p(y))
     return y
 
 
-def probe_dense(x_q8, w_q8_0, N, K, tokens, rows):
+def probe_dense(x_q8, w_q8_0, N, K, tokens, rows, w_format="q8_0"):
     """Integer block dots of (token, weight row) probes -> int32 [n, K/32]."""
     x = _c(x_q8, np.uint8)
     T = x.size // ((K // 32) * 36)
@@ -257,7 +263,8 @@ def probe_dense(x_q8, w_q8_0, N, K, tokens, rows):
     assert tok.size == rows.size and (tok.size == 0 or (tok.min() >= 0 and tok.max() < T))
     assert rows.size == 0 or (rows.min() >= 0 and rows.max() < N)
     out = np.zeros((tok.size, K // 32), np.int32)
-    lib().orc_probe_dense(_p(x), T, _p(_c(w_q8_0, np.uint8)), N, K, tok.size, _p(tok), _p(rows), _p(out))
+    lib().orc_probe_dense_fmt(_p(x), T, _p(_c(w_q8_0, np.uint8)), DENSE_FORMATS[w_format], N, K, tok.size, _p(tok),
+                              _p(rows), _p(out))
     return out
 
 

@@ -549,14 +549,25 @@ void orc_dequant_q8_0(const uint8_t* blocks, int64_t nblocks, double* out) {
   }
 }
 
-/* Block dots of weight row w (K/32 Q8_0 blocks) with activation row x
+/* Projection weight formats: Q8_0, or Q4_0 (the PR page's section "Not done"
+ * names a Q4_0 projection file; its block is the one orc_q4_0_decode reads,
+ * 18 bytes per 32 weights). */
+#define DENSE_Q8_0 0
+#define DENSE_Q4_0 1
+static int64_t dense_block_bytes(int fmt) { return fmt == DENSE_Q4_0 ? IQ4NL_BYTES : Q80_BYTES; }
+
+/* Block dots of weight row w (K/32 Q8_0 or Q4_0 blocks) with activation row x
  * (K/32 q8_1 blocks): D32[b] = sum_i qw(i) * qx(i); dw[b], dx[b] get the
  * two block scales. */
-static void dense_row_dots(const uint8_t* w, const uint8_t* x, int K, int32_t* D32, double* dw, double* dx) {
+static void dense_row_dots(int fmt, const uint8_t* w, const uint8_t* x, int K, int32_t* D32, double* dw,
+                           double* dx) {
   int nb = K / Q80_VALUES;
   for (int b = 0; b < nb; ++b) {
     int8_t qw[Q80_VALUES], qx[Q81_VALUES];
-    orc_q8_0_decode(w + (int64_t)b * Q80_BYTES, qw, &dw[b]);
+    if (fmt == DENSE_Q4_0)
+      orc_q4_0_decode(w + (int64_t)b * IQ4NL_BYTES, qw, &dw[b]);
+    else
+      orc_q8_0_decode(w + (int64_t)b * Q80_BYTES, qw, &dw[b]);
     orc_q8_1_decode(x + (int64_t)b * Q81_BYTES, qx, &dx[b]);
     int32_t acc = 0;
     for (int i = 0; i < Q80_VALUES; ++i) acc += (int32_t)qw[i] * (int32_t)qx[i];
@@ -566,11 +577,11 @@ static void dense_row_dots(const uint8_t* w, const uint8_t* x, int K, int32_t* D
 
 /* y[t][n] = sum over blocks b (ascending) of dw[n][b] * dx[t][b] * D32[t][n][b]
  * in fp64, for the tokens tok[0..n_tok) (all T tokens when tok is NULL).
- * x [T][K/32] q8_1, w [N][K/32] Q8_0, y [n_tok][N]. */
-void orc_dense_q8_0(const uint8_t* x_q8, int64_t T, const uint8_t* w, int N, int K, const int64_t* tok,
-                    int64_t n_tok, double* y) {
+ * x [T][K/32] q8_1, w [N][K/32] Q8_0 (fmt 0) or Q4_0 (fmt 1), y [n_tok][N]. */
+void orc_dense_fmt(const uint8_t* x_q8, int64_t T, const uint8_t* w, int fmt, int N, int K, const int64_t* tok,
+                   int64_t n_tok, double* y) {
   int nb = K / Q80_VALUES;
-  int64_t xrow = (int64_t)nb * Q81_BYTES, wrow = (int64_t)nb * Q80_BYTES;
+  int64_t xrow = (int64_t)nb * Q81_BYTES, wrow = (int64_t)nb * dense_block_bytes(fmt);
   (void)T;
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t i = 0; i < n_tok; ++i) {
@@ -579,7 +590,7 @@ void orc_dense_q8_0(const uint8_t* x_q8, int64_t T, const uint8_t* w, int N, int
     double* dw = (double*)malloc(sizeof(double) * nb);
     double* dx = (double*)malloc(sizeof(double) * nb);
     for (int n = 0; n < N; ++n) {
-      dense_row_dots(w + n * wrow, x_q8 + t * xrow, K, D32, dw, dx);
+      dense_row_dots(fmt, w + n * wrow, x_q8 + t * xrow, K, D32, dw, dx);
       double acc = 0.0;
       for (int b = 0; b < nb; ++b) acc += dw[b] * dx[b] * (double)D32[b];
       y[i * N + n] = acc;
@@ -590,22 +601,32 @@ void orc_dense_q8_0(const uint8_t* x_q8, int64_t T, const uint8_t* w, int N, int
   }
 }
 
+void orc_dense_q8_0(const uint8_t* x_q8, int64_t T, const uint8_t* w, int N, int K, const int64_t* tok,
+                    int64_t n_tok, double* y) {
+  orc_dense_fmt(x_q8, T, w, DENSE_Q8_0, N, K, tok, n_tok, y);
+}
+
 /* Dense block-dot probes: for probe i = (token tok[i], weight row row[i]),
  * out[i][K/32] = D32. */
-void orc_probe_dense(const uint8_t* x_q8, int64_t T, const uint8_t* w, int N, int K, int64_t n, const int64_t* tok,
-                     const int32_t* row, int32_t* out) {
+void orc_probe_dense_fmt(const uint8_t* x_q8, int64_t T, const uint8_t* w, int fmt, int N, int K, int64_t n,
+                         const int64_t* tok, const int32_t* row, int32_t* out) {
   int nb = K / Q80_VALUES;
-  int64_t xrow = (int64_t)nb * Q81_BYTES, wrow = (int64_t)nb * Q80_BYTES;
+  int64_t xrow = (int64_t)nb * Q81_BYTES, wrow = (int64_t)nb * dense_block_bytes(fmt);
   (void)T;
   (void)N;
 #pragma omp parallel for schedule(static)
   for (int64_t i = 0; i < n; ++i) {
     double* dw = (double*)malloc(sizeof(double) * nb);
     double* dx = (double*)malloc(sizeof(double) * nb);
-    dense_row_dots(w + row[i] * wrow, x_q8 + tok[i] * xrow, K, out + i * nb, dw, dx);
+    dense_row_dots(fmt, w + row[i] * wrow, x_q8 + tok[i] * xrow, K, out + i * nb, dw, dx);
     free(dw);
     free(dx);
   }
+}
+
+void orc_probe_dense(const uint8_t* x_q8, int64_t T, const uint8_t* w, int N, int K, int64_t n, const int64_t* tok,
+                     const int32_t* row, int32_t* out) {
+  orc_probe_dense_fmt(x_q8, T, w, DENSE_Q8_0, N, K, n, tok, row, out);
 }
 
 /* ------------------------------------------------------------------------ */

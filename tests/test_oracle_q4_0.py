@@ -104,3 +104,45 @@ def test_down_format_leaves_h_and_scales_linearly():
     # and the down-only path agrees with the full stage
     y = oracle.down_combine(b.h, I.router_idx, I.router_w, I.down_iq4nl, L, F, E, down_format="q4_0")
     assert np.array_equal(y, b.y)
+
+
+# ---- Q4_0 as the weight format of the latent D / U projections -------------
+
+def _dense_case(T, N, K, seed):
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal((T, K)) * np.exp(rng.uniform(-1, 1, (T, 1)))).astype(np.float32)
+    xq = oracle.quantize_q8_1(x)
+    nib = rng.integers(0, 16, (N, K // 32, 32))
+    d = rng.uniform(0.5, 1.5, (N, K // 32)).astype(np.float16) * np.float16(2.0 ** -8)
+    w = pack_iq4nl(nib.reshape(-1, 32), d.reshape(-1)).reshape(N, K // 32, 18)
+    return xq, w, nib, d
+
+
+@pytest.mark.parametrize("T,N,K", [(5, 96, 256), (3, 64, 1024)])
+def test_dense_q4_0_bruteforce(T, N, K):
+    """fp64 matmul of the exactly dequantized operands (non-square: a
+    transposed operand or a wrong block index fails)."""
+    xq, w, nib, d = _dense_case(T, N, K, seed=T + N)
+    y = oracle.dense_q8_0(xq, w, N, K, w_format="q4_0")
+    W = (d.astype(np.float64)[..., None] * (nib - 8)).reshape(N, K)
+    X = oracle.dequant_q8_1(xq).reshape(T, K)
+    ref = X @ W.T
+    assert np.abs(y - ref).max() <= 1e-12 * np.abs(ref).max()
+
+
+def test_dense_q4_0_block_dots_and_q8_0_equivalence():
+    T, N, K = 4, 64, 512
+    xq, w, nib, d = _dense_case(T, N, K, seed=7)
+    rng = np.random.default_rng(2)
+    toks = rng.integers(0, T, 40)
+    rows = rng.integers(0, N, 40).astype(np.int32)
+    dots = oracle.probe_dense(xq, w, N, K, toks, rows, w_format="q4_0")
+    qx = xq[..., 4:].view(np.int8).reshape(T, K // 32, 32).astype(np.int64)
+    for i, (t, r) in enumerate(zip(toks, rows)):
+        assert np.array_equal(dots[i], ((nib[r] - 8) * qx[t]).sum(-1))
+    # the same weights written as Q8_0 blocks (codes nibble - 8, the same d)
+    # give the same projection, bit for bit
+    w8 = np.zeros((N, K // 32, 34), np.uint8)
+    w8[..., 0:2] = d.reshape(N, K // 32, 1).view(np.uint8)
+    w8[..., 2:] = (nib - 8).astype(np.int8).view(np.uint8)
+    assert np.array_equal(oracle.dense_q8_0(xq, w8, N, K), oracle.dense_q8_0(xq, w, N, K, w_format="q4_0"))
