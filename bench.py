@@ -208,6 +208,7 @@ class DenseStage:
         lm.quantize_q8_1(t(I.x), self.xh)
         lm.quantize_q8_1(t(I.z), self.zl)
         self.dw, self.uw = t(I.d_q8_0), t(I.u_q8_0)
+        self.dw4, self.uw4 = t(I.d_q4_0), t(I.u_q4_0)  # the same projections with Q4_0 weights
         self.xl = torch.empty((dwl.T, dwl.L // 32, 36), dtype=torch.uint8, device=dev)
         self.out = torch.empty((dwl.T, dwl.H), dtype=torch.float32, device=dev)
         torch.cuda.synchronize()
@@ -219,6 +220,14 @@ class DenseStage:
     def run_u(self):
         w = self.wl
         self.lm.dense_q8_0(self.zl, self.uw, w.T, w.H, w.L, self.out, None)
+
+    def run_d4(self):
+        w = self.wl
+        self.lm.dense_q4_0(self.xh, self.dw4, w.T, w.L, w.H, None, self.xl)
+
+    def run_u4(self):
+        w = self.wl
+        self.lm.dense_q4_0(self.zl, self.uw4, w.T, w.H, w.L, self.out, None)
 
     def time(self, fn, steps, warmup, out=None):
         """ms per call.  Decode-sized calls are replayed from a captured graph of
@@ -264,12 +273,15 @@ class DenseStage:
     def report(self, steps, warmup):
         w = self.wl
         res = {"workload": w.name, "T": w.T, "H": w.H, "L": w.L}
-        for name, fn, N, K, out_bytes, out in (("D", self.run_d, w.L, w.H, w.T * (w.L // 32) * 36, self.xl),
-                                               ("U", self.run_u, w.H, w.L, w.T * w.H * 4, self.out)):
+        for name, fn, N, K, out_bytes, out, wb in (
+                ("D", self.run_d, w.L, w.H, w.T * (w.L // 32) * 36, self.xl, 34),
+                ("U", self.run_u, w.H, w.L, w.T * w.H * 4, self.out, 34),
+                ("D_q4_0", self.run_d4, w.L, w.H, w.T * (w.L // 32) * 36, self.xl, 18),
+                ("U_q4_0", self.run_u4, w.H, w.L, w.T * w.H * 4, self.out, 18)):
             ms = self.time(fn, steps, warmup, out)
             ops = 2 * w.T * N * K
             folds = 2 * w.T * N * (K // 32)
-            nbytes = N * (K // 32) * 34 + w.T * (K // 32) * 36 + out_bytes
+            nbytes = N * (K // 32) * wb + w.T * (K // 32) * 36 + out_bytes
             fold_t = folds / (ms * 1e-3) / 1e12
             gbs = nbytes / (ms * 1e-3) / 1e9
             # prefill: bound by the per-block fp32 fold on the VALU (2 lane-ops per

@@ -175,6 +175,24 @@ int lat_moe_dense_q8_0_debug(const void* x_q8_1, const void* w_q8_0, int64_t T, 
                              float* y_f32, void* y_q8_1, void* stream, int32_t* dots_i32, int32_t row0,
                              int32_t rows);
 
+/* The same projection with Q4_0 weights: w_q4_0 [N][K/32] blocks of 18 B,
+ * d (fp16) | qs[16], element i < 16 the low nibble of qs[i], element i >= 16
+ * the high nibble of qs[i - 16], weight = d * (nibble - 8) (ggml's Q4_0; the
+ * page "Run Edge0-145B Q3_K on AMD HIP (Linux, gfx1100) #1", section "Not
+ * done", names a Q4_0 projection file).  I is then the int32 dot of the
+ * nibble - 8 values with the activation codes.  Rules, outputs and errors as
+ * for lat_moe_dense_q8_0, with N * K/32 * 18 < 2^31 bytes of weights and one
+ * more shape rule: T <= 8 (and K <= 4096, or K <= 8192 with T <= 4), or
+ * N % 128 == 0 and K % 256 == 0; other shapes return LAT_MOE_EINVAL. */
+int lat_moe_dense_q4_0(const void* x_q8_1, const void* w_q4_0, int64_t T, int32_t N, int32_t K, float* y_f32,
+                       void* y_q8_1, void* stream);
+
+/* As lat_moe_dense_q4_0, plus the integer block dots of weight rows
+ * row0 .. row0+rows-1, as for lat_moe_dense_q8_0_debug. */
+int lat_moe_dense_q4_0_debug(const void* x_q8_1, const void* w_q4_0, int64_t T, int32_t N, int32_t K,
+                             float* y_f32, void* y_q8_1, void* stream, int32_t* dots_i32, int32_t row0,
+                             int32_t rows);
+
 /* Router (page "Run Edge0-145B Q3_K on AMD HIP (Linux, gfx1100) #1", section
  * "Contents", and the HIP backend page: each token's top experts and the
  * weights the stage combines their outputs with): softmax of each token's

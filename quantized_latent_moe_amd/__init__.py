@@ -28,6 +28,8 @@ EXPORTED = (
     "lat_moe_quantize_q8_1",
     "lat_moe_dense_q8_0",
     "lat_moe_dense_q8_0_debug",
+    "lat_moe_dense_q4_0",
+    "lat_moe_dense_q4_0_debug",
     "lat_moe_router_topk",
     "lat_moe_strerror",
     "lat_moe_version",
@@ -88,6 +90,10 @@ def lib() -> ctypes.CDLL:
         c.lat_moe_dense_q8_0.restype = ctypes.c_int
         c.lat_moe_dense_q8_0_debug.argtypes = [P, P, i64, i32, i32, P, P, P, P, i32, i32]
         c.lat_moe_dense_q8_0_debug.restype = ctypes.c_int
+        c.lat_moe_dense_q4_0.argtypes = [P, P, i64, i32, i32, P, P, P]
+        c.lat_moe_dense_q4_0.restype = ctypes.c_int
+        c.lat_moe_dense_q4_0_debug.argtypes = [P, P, i64, i32, i32, P, P, P, P, i32, i32]
+        c.lat_moe_dense_q4_0_debug.restype = ctypes.c_int
         c.lat_moe_router_topk.argtypes = [P, i64, i32, i32, P, P, P]
         c.lat_moe_router_topk.restype = ctypes.c_int
         c.lat_moe_strerror.argtypes = [ctypes.c_int]
@@ -193,6 +199,14 @@ def dense_q8_0(x_q8_1, w_q8_0, T: int, N: int, K: int, y_f32=None, y_q8_1=None, 
     dots of weight rows row0 .. row0+rows-1."""
     rows = 0 if dots_i32 is None else int(dots_i32.shape[1])
     _check(lib().lat_moe_dense_q8_0_debug(_ptr(x_q8_1), _ptr(w_q8_0), int(T), int(N), int(K), _ptr(y_f32),
+                                          _ptr(y_q8_1), _stream(stream), _ptr(dots_i32), int(row0), rows))
+
+
+def dense_q4_0(x_q8_1, w_q4_0, T: int, N: int, K: int, y_f32=None, y_q8_1=None, *, dots_i32=None, row0: int = 0,
+               stream=None) -> None:
+    """As dense_q8_0 with Q4_0 weights (uint8 [N, K/32, 18])."""
+    rows = 0 if dots_i32 is None else int(dots_i32.shape[1])
+    _check(lib().lat_moe_dense_q4_0_debug(_ptr(x_q8_1), _ptr(w_q4_0), int(T), int(N), int(K), _ptr(y_f32),
                                           _ptr(y_q8_1), _stream(stream), _ptr(dots_i32), int(row0), rows))
 
 

@@ -161,6 +161,32 @@ int forward_impl(const void* x, const int32_t* idx, const float* w, const void* 
   return LAT_MOE_OK;
 }
 
+int dense_impl(int wfmt, const void* x_q8_1, const void* w, int64_t T, int32_t N, int32_t K, float* y_f32,
+               void* y_q8_1, void* stream, int32_t* dots_i32, int32_t row0, int32_t rows) {
+  if (T < 0 || K < 32 || K > 65536 || K % 32 || N < 32 || N > 65536 || N % 32) return LAT_MOE_EINVAL;
+  const int wb = wfmt == kDenseQ40 ? kQ40Bytes : kQ80Bytes;
+  if ((int64_t)N * (K / 32) * wb >= (int64_t)1 << 31 || T * (K / 32) * 36 >= (int64_t)1 << 31) return LAT_MOE_EINVAL;
+  if (!dense_shape_ok(wfmt, T, N, K)) return LAT_MOE_EINVAL;
+  if (!y_f32 && !y_q8_1) return LAT_MOE_EINVAL;
+  if (dots_i32 && (row0 < 0 || rows < 1 || (int64_t)row0 + rows > N)) return LAT_MOE_EINVAL;
+  if (T == 0) return LAT_MOE_OK;
+  const void* need[] = {x_q8_1, w};
+  for (const void* p : need)
+    if (!p || !aligned16(p)) return LAT_MOE_EINVAL;
+  if ((y_f32 && !aligned16(y_f32)) || (y_q8_1 && !aligned16(y_q8_1)) || (dots_i32 && !aligned16(dots_i32)))
+    return LAT_MOE_EINVAL;
+  int num_cus = 1;
+  int rc = check_device(&num_cus);
+  if (rc != LAT_MOE_OK) return rc;
+  const ProbeRows probe{dots_i32, row0, rows};
+  if (launch_dense(static_cast<const uint8_t*>(x_q8_1), static_cast<const uint8_t*>(w), wfmt, T, N, K, y_f32,
+                   static_cast<uint8_t*>(y_q8_1), dots_i32 ? &probe : nullptr, num_cus,
+                   static_cast<hipStream_t>(stream)) != hipSuccess)
+    return LAT_MOE_ELAUNCH;
+  return LAT_MOE_OK;
+}
+
+
 }  // namespace
 
 extern "C" {
@@ -206,33 +232,27 @@ int lat_moe_quantize_q8_1(const float* x, int64_t rows, int32_t cols, void* out_
   return LAT_MOE_OK;
 }
 
+
 int lat_moe_dense_q8_0_debug(const void* x_q8_1, const void* w_q8_0, int64_t T, int32_t N, int32_t K,
                              float* y_f32, void* y_q8_1, void* stream, int32_t* dots_i32, int32_t row0,
                              int32_t rows) {
-  if (T < 0 || K < 32 || K > 65536 || K % 32 || N < 32 || N > 65536 || N % 32) return LAT_MOE_EINVAL;
-  if ((int64_t)N * (K / 32) * 34 >= (int64_t)1 << 31 || T * (K / 32) * 36 >= (int64_t)1 << 31) return LAT_MOE_EINVAL;
-  if (!y_f32 && !y_q8_1) return LAT_MOE_EINVAL;
-  if (dots_i32 && (row0 < 0 || rows < 1 || (int64_t)row0 + rows > N)) return LAT_MOE_EINVAL;
-  if (T == 0) return LAT_MOE_OK;
-  const void* need[] = {x_q8_1, w_q8_0};
-  for (const void* p : need)
-    if (!p || !aligned16(p)) return LAT_MOE_EINVAL;
-  if ((y_f32 && !aligned16(y_f32)) || (y_q8_1 && !aligned16(y_q8_1)) || (dots_i32 && !aligned16(dots_i32)))
-    return LAT_MOE_EINVAL;
-  int num_cus = 1;
-  int rc = check_device(&num_cus);
-  if (rc != LAT_MOE_OK) return rc;
-  const ProbeRows probe{dots_i32, row0, rows};
-  if (launch_dense_q8_0(static_cast<const uint8_t*>(x_q8_1), static_cast<const uint8_t*>(w_q8_0), T, N, K, y_f32,
-                        static_cast<uint8_t*>(y_q8_1), dots_i32 ? &probe : nullptr, num_cus,
-                        static_cast<hipStream_t>(stream)) != hipSuccess)
-    return LAT_MOE_ELAUNCH;
-  return LAT_MOE_OK;
+  return dense_impl(kDenseQ80, x_q8_1, w_q8_0, T, N, K, y_f32, y_q8_1, stream, dots_i32, row0, rows);
 }
 
 int lat_moe_dense_q8_0(const void* x_q8_1, const void* w_q8_0, int64_t T, int32_t N, int32_t K, float* y_f32,
                        void* y_q8_1, void* stream) {
-  return lat_moe_dense_q8_0_debug(x_q8_1, w_q8_0, T, N, K, y_f32, y_q8_1, stream, nullptr, 0, 0);
+  return dense_impl(kDenseQ80, x_q8_1, w_q8_0, T, N, K, y_f32, y_q8_1, stream, nullptr, 0, 0);
+}
+
+int lat_moe_dense_q4_0_debug(const void* x_q8_1, const void* w_q4_0, int64_t T, int32_t N, int32_t K,
+                             float* y_f32, void* y_q8_1, void* stream, int32_t* dots_i32, int32_t row0,
+                             int32_t rows) {
+  return dense_impl(kDenseQ40, x_q8_1, w_q4_0, T, N, K, y_f32, y_q8_1, stream, dots_i32, row0, rows);
+}
+
+int lat_moe_dense_q4_0(const void* x_q8_1, const void* w_q4_0, int64_t T, int32_t N, int32_t K, float* y_f32,
+                       void* y_q8_1, void* stream) {
+  return dense_impl(kDenseQ40, x_q8_1, w_q4_0, T, N, K, y_f32, y_q8_1, stream, nullptr, 0, 0);
 }
 
 int lat_moe_router_topk(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* router_idx, float* router_w,

@@ -58,7 +58,6 @@ constexpr int kRowsWG = 64;   // weight rows per work item
 constexpr int kTokWG = 128;   // tokens per work item
 constexpr int kLogKB = 2;
 constexpr int kKB = 1 << kLogKB;  // 32-value blocks per K step
-constexpr int kQ80Bytes = 34;
 constexpr int kXcds = 8;
 constexpr int kGroupBytes = 2 << 20;  // weight bytes of the row tiles of one sweep over the token tiles
 // LDS slots of 16 bytes: (block, half) planes of rows/tokens, each plane
@@ -341,7 +340,7 @@ __device__ __forceinline__ float group_sum(float v) {
 
 // BPL: blocks per lane and row (the row's K/32 blocks are dealt to LPR lanes
 // round-robin); LPR: lanes per row.
-template <int BPL, int LPR, bool PROBE>
+template <int BPL, int LPR, bool PROBE, int WFMT>
 __global__ __launch_bounds__(64 * small_waves(LPR)) void k_dense_small(const uint8_t* __restrict__ x,
                                                                const uint8_t* __restrict__ w, int T, int N, int K,
                                                                float* __restrict__ y_f32, uint8_t* __restrict__ y_q8,
@@ -358,7 +357,8 @@ __global__ __launch_bounds__(64 * small_waves(LPR)) void k_dense_small(const uin
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int row0 = blockIdx.x * kSmallRows;
   const int li = lane & (LPR - 1), sub = lane / LPR;  // lane within its row group, row group
-  const rsrc_t rw = make_rsrc(w, (uint32_t)((int64_t)N * nb * kQ80Bytes));
+  constexpr int kWB = WFMT == kDenseQ40 ? kQ40Bytes : kQ80Bytes;  // weight block bytes
+  const rsrc_t rw = make_rsrc(w, (uint32_t)((int64_t)N * nb * kWB));
   const rsrc_t rx = make_rsrc(x, (uint32_t)((int64_t)T * nb * kQ81Bytes));
 
   // This wave's weight blocks (row of iteration it, block li + LPR j) into
@@ -372,10 +372,21 @@ __global__ __launch_bounds__(64 * small_waves(LPR)) void k_dense_small(const uin
 #pragma unroll
     for (int j = 0; j < BPL; ++j) {
       const int b = li + LPR * j;
-      const int off = (r < N && b < nb) ? (r * nb + b) * kQ80Bytes : kOutOfRange;
-      const uint4 w0 = buf_u128(rw, off, 2), w1 = buf_u128(rw, off, 18);
-      wq[it][j][0] = w0.x; wq[it][j][1] = w0.y; wq[it][j][2] = w0.z; wq[it][j][3] = w0.w;
-      wq[it][j][4] = w1.x; wq[it][j][5] = w1.y; wq[it][j][6] = w1.z; wq[it][j][7] = w1.w;
+      const int off = (r < N && b < nb) ? (r * nb + b) * kWB : kOutOfRange;
+      if constexpr (WFMT == kDenseQ40) {
+        // 16 bytes of nibbles: element i < 16 low nibble of byte i, i >= 16 high nibble of byte i - 16
+        const uint4 n = buf_u128(rw, off, 2);
+        const uint32_t nw[4] = {n.x, n.y, n.z, n.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          wq[it][j][k] = down_lookup<kDownQ40>(nw[k] & 0x0f0f0f0fu);
+          wq[it][j][4 + k] = down_lookup<kDownQ40>((nw[k] >> 4) & 0x0f0f0f0fu);
+        }
+      } else {
+        const uint4 w0 = buf_u128(rw, off, 2), w1 = buf_u128(rw, off, 18);
+        wq[it][j][0] = w0.x; wq[it][j][1] = w0.y; wq[it][j][2] = w0.z; wq[it][j][3] = w0.w;
+        wq[it][j][4] = w1.x; wq[it][j][5] = w1.y; wq[it][j][6] = w1.z; wq[it][j][7] = w1.w;
+      }
       wd[it][j] = half_bits_to_float(buf_u16(rw, off, 0));
     }
   }
@@ -474,18 +485,27 @@ __global__ __launch_bounds__(64 * small_waves(LPR)) void k_dense_small(const uin
   }
 }
 
-template <int BPL, int LPR>
-void launch_small(const uint8_t* x, const uint8_t* w, int T, int N, int K, float* y_f32, uint8_t* y_q8,
-                  const ProbeRows* probe, hipStream_t st) {
+template <int BPL, int LPR, int WFMT>
+void launch_small_fmt(const uint8_t* x, const uint8_t* w, int T, int N, int K, float* y_f32, uint8_t* y_q8,
+                      const ProbeRows* probe, hipStream_t st) {
   const dim3 grid(N / kSmallRows);
   const size_t lds = (size_t)T * (K / 32) * kQ81Bytes + 16;
   const ProbeRows none = {nullptr, 0, 0};
   if (probe)
-    hipLaunchKernelGGL((k_dense_small<BPL, LPR, true>), grid, dim3(64 * small_waves(LPR)), lds, st, x, w, T, N, K,
-                       y_f32, y_q8, *probe);
+    hipLaunchKernelGGL((k_dense_small<BPL, LPR, true, WFMT>), grid, dim3(64 * small_waves(LPR)), lds, st, x, w, T, N,
+                       K, y_f32, y_q8, *probe);
   else
-    hipLaunchKernelGGL((k_dense_small<BPL, LPR, false>), grid, dim3(64 * small_waves(LPR)), lds, st, x, w, T, N, K,
-                       y_f32, y_q8, none);
+    hipLaunchKernelGGL((k_dense_small<BPL, LPR, false, WFMT>), grid, dim3(64 * small_waves(LPR)), lds, st, x, w, T,
+                       N, K, y_f32, y_q8, none);
+}
+
+template <int BPL, int LPR>
+void launch_small(int wfmt, const uint8_t* x, const uint8_t* w, int T, int N, int K, float* y_f32, uint8_t* y_q8,
+                  const ProbeRows* probe, hipStream_t st) {
+  if (wfmt == kDenseQ40)
+    launch_small_fmt<BPL, LPR, kDenseQ40>(x, w, T, N, K, y_f32, y_q8, probe, st);
+  else
+    launch_small_fmt<BPL, LPR, kDenseQ80>(x, w, T, N, K, y_f32, y_q8, probe, st);
 }
 
 // The GEMV-shaped kernel's configuration for K/32 blocks, or false when the
@@ -504,20 +524,28 @@ bool small_config(int64_t T, int nb, int* bpl, int* lpr) {
 
 }  // namespace
 
-hipError_t launch_dense_q8_0(const uint8_t* x, const uint8_t* w, int64_t T, int N, int K, float* y_f32,
-                             uint8_t* y_q8, const ProbeRows* probe, int num_cus, hipStream_t st) {
+bool dense_shape_ok(int wfmt, int64_t T, int N, int K) {
+  int bpl = 0, lpr = 0;
+  return wfmt == kDenseQ80 || small_config(T, K / 32, &bpl, &lpr) || dense_ws_shape(N, K);
+}
+
+hipError_t launch_dense(const uint8_t* x, const uint8_t* w, int wfmt, int64_t T, int N, int K, float* y_f32,
+                        uint8_t* y_q8, const ProbeRows* probe, int num_cus, hipStream_t st) {
   int bpl = 0, lpr = 0;
   if (small_config(T, K / 32, &bpl, &lpr)) {
     const int t = (int)T;
-    if (lpr == 8) launch_small<1, 8>(x, w, t, N, K, y_f32, y_q8, probe, st);
-    else if (lpr == 16) launch_small<1, 16>(x, w, t, N, K, y_f32, y_q8, probe, st);
-    else if (lpr == 32) launch_small<1, 32>(x, w, t, N, K, y_f32, y_q8, probe, st);
-    else if (bpl == 1) launch_small<1, 64>(x, w, t, N, K, y_f32, y_q8, probe, st);
-    else if (bpl == 2) launch_small<2, 64>(x, w, t, N, K, y_f32, y_q8, probe, st);
-    else launch_small<4, 64>(x, w, t, N, K, y_f32, y_q8, probe, st);
+    if (lpr == 8) launch_small<1, 8>(wfmt, x, w, t, N, K, y_f32, y_q8, probe, st);
+    else if (lpr == 16) launch_small<1, 16>(wfmt, x, w, t, N, K, y_f32, y_q8, probe, st);
+    else if (lpr == 32) launch_small<1, 32>(wfmt, x, w, t, N, K, y_f32, y_q8, probe, st);
+    else if (bpl == 1) launch_small<1, 64>(wfmt, x, w, t, N, K, y_f32, y_q8, probe, st);
+    else if (bpl == 2) launch_small<2, 64>(wfmt, x, w, t, N, K, y_f32, y_q8, probe, st);
+    else launch_small<4, 64>(wfmt, x, w, t, N, K, y_f32, y_q8, probe, st);
     return hipGetLastError();
   }
-  if (dense_ws_fits(T, N, K)) return launch_dense_ws(x, w, T, N, K, y_f32, y_q8, probe, num_cus, st);
+  // Q4_0 weights above the GEMV sizes take the persistent kernel at any T
+  // (the entry point has checked its shape rule); Q8_0 weights from T = 128.
+  if (dense_ws_shape(N, K) && (wfmt == kDenseQ40 || T >= 128))
+    return launch_dense_ws(x, w, wfmt, T, N, K, y_f32, y_q8, probe, num_cus, st);
   const int n_rt = (N + kRowsWG - 1) / kRowsWG;
   const int n_tt = (int)((T + kTokWG - 1) / kTokWG);
   const int items = n_rt * n_tt;

@@ -23,7 +23,10 @@
 //     block halves (buffer loads at the blocks' unaligned code offsets: Q8_0
 //     blocks are 34 bytes, q8_1 blocks 36; the lanes of one load walk four
 //     contiguous row segments), the fp16 scales, and writes them to LDS.
-//     Q8_0 codes are the MFMA operand as they are: no expansion step.
+//     Q8_0 codes are the MFMA operand as they are: no expansion step.  Q4_0
+//     weights (18-byte blocks: fp16 d, 16 bytes of nibbles; weight = d *
+//     (nibble - 8)) are loaded a whole block per lane, four per lane and
+//     step, and expanded in registers into the same operand rows.
 // Operand rows are 256 bytes (8 blocks) with their 16-byte chunks XOR-swizzled
 // by the row's low 4 bits; operands and scales are double-buffered, one
 // barrier per step; step g + 2's loads are in flight during step g.
@@ -46,7 +49,6 @@ constexpr int kCons = 8, kProd = 4;
 constexpr int kThreads = 64 * (kCons + kProd);  // 768
 constexpr int kLT = 128;                        // weight rows per item
 constexpr int kNT = 128;                        // tokens per item
-constexpr int kQ80Bytes = 34;
 constexpr int kGroupBytes = 2 << 20;
 static_assert(kLT == 32 * kProd && kNT == 32 * kProd, "a producer owns 32 rows and 32 tokens");
 
@@ -68,7 +70,7 @@ __device__ __forceinline__ void item_tiles(int item, int n_rt, int n_tt, int gro
   rt = group * group_rows + (within - tt * g_rows);
 }
 
-template <bool PROBE>
+template <bool PROBE, int WFMT>
 __global__ __launch_bounds__(kThreads) void k_dense_ws(const uint8_t* __restrict__ x, const uint8_t* __restrict__ w,
                                                        int T, int N, int K, int n_rt, int n_tt, int group_rows,
                                                        int items, float* __restrict__ y_f32,
@@ -99,11 +101,14 @@ __global__ __launch_bounds__(kThreads) void k_dense_ws(const uint8_t* __restrict
   if (wave >= kCons) {
     // =============================== producer ===============================
     const int p = wave - kCons;
-    const rsrc_t rw = make_rsrc(w, (uint32_t)((int64_t)N * nb * kQ80Bytes));
+    constexpr int kWB = WFMT == kDenseQ40 ? kQ40Bytes : kQ80Bytes;  // weight block bytes
+    const rsrc_t rw = make_rsrc(w, (uint32_t)((int64_t)N * nb * kWB));
     const rsrc_t rx = make_rsrc(x, (uint32_t)((int64_t)T * nb * kQ81Bytes));
     // codes, load m < 8: row (token) 32p + 4m + (lane >> 4), chunk lane & 15 =
     // (block (lane & 15) >> 1, half lane & 1); scales, load c < 4: row (token)
-    // 32p + 8c + (lane >> 3), block lane & 7.  Step s adds 8 s blocks.
+    // 32p + 8c + (lane >> 3), block lane & 7.  Step s adds 8 s blocks.  Q4_0
+    // weights: load c < 4 takes the whole block (row 32p + 8c + (lane >> 3),
+    // block lane & 7): its d and its 16 bytes of nibbles.
     const int pc = lane & 15, pkb = pc >> 1, ph = pc & 1;
     int woff[8], xoff[8], wsoff[4], xsoff[4];
     int lj = 0, lsb = 0;
@@ -121,22 +126,27 @@ __global__ __launch_bounds__(kThreads) void k_dense_ws(const uint8_t* __restrict
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int r = l0 + 32 * p + 8 * c + (lane >> 3);
-        wsoff[c] = (r * nb + (lane & 7)) * kQ80Bytes;
+        wsoff[c] = (r * nb + (lane & 7)) * kWB;
         const int n = 32 * p + 8 * c + (lane >> 3);
         xsoff[c] = n < cnt ? ((n0 + n) * nb + (lane & 7)) * kQ81Bytes : kOutOfRange;
       }
     };
-    uint4 rq[8], rv[8];
+    uint4 rq[WFMT == kDenseQ40 ? 4 : 8], rv[8];
     uint32_t rwd[4], rxd[4];
     auto load_next = [&]() {
       if (need_setup) {
         setup(lj);
         need_setup = false;
       }
-      const int sw = __builtin_amdgcn_readfirstlane(lsb * 8 * kQ80Bytes);  // scalar offsets stay in SGPRs
+      const int sw = __builtin_amdgcn_readfirstlane(lsb * 8 * kWB);  // scalar offsets stay in SGPRs
       const int sx = __builtin_amdgcn_readfirstlane(lsb * 8 * kQ81Bytes);
+      if constexpr (WFMT == kDenseQ40) {
 #pragma unroll
-      for (int m = 0; m < 8; ++m) rq[m] = buf_u128(rw, woff[m], sw);
+        for (int c = 0; c < 4; ++c) rq[c] = buf_u128(rw, wsoff[c] + 2, sw);
+      } else {
+#pragma unroll
+        for (int m = 0; m < 8; ++m) rq[m] = buf_u128(rw, woff[m], sw);
+      }
 #pragma unroll
       for (int m = 0; m < 8; ++m) rv[m] = buf_u128(rx, xoff[m], sx);
 #pragma unroll
@@ -154,8 +164,24 @@ __global__ __launch_bounds__(kThreads) void k_dense_ws(const uint8_t* __restrict
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
         const int r = 32 * p + 4 * m + (lane >> 4);
-        *reinterpret_cast<uint4*>(As[b] + swz(r, pc)) = rq[m];
+        if constexpr (WFMT != kDenseQ40) *reinterpret_cast<uint4*>(As[b] + swz(r, pc)) = rq[m];
         *reinterpret_cast<uint4*>(Bs[b] + swz(r, pc)) = rv[m];  // token r of the item
+      }
+      if constexpr (WFMT == kDenseQ40) {
+        // element i < 16 of a block: low nibble of byte i; i >= 16: high nibble of byte i - 16
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int r = 32 * p + 8 * c + (lane >> 3), kb = lane & 7;
+          const uint4 n = rq[c];
+          const uint4 lo = {down_lookup<kDownQ40>(n.x & 0x0f0f0f0fu), down_lookup<kDownQ40>(n.y & 0x0f0f0f0fu),
+                            down_lookup<kDownQ40>(n.z & 0x0f0f0f0fu), down_lookup<kDownQ40>(n.w & 0x0f0f0f0fu)};
+          const uint4 hi = {down_lookup<kDownQ40>((n.x >> 4) & 0x0f0f0f0fu),
+                            down_lookup<kDownQ40>((n.y >> 4) & 0x0f0f0f0fu),
+                            down_lookup<kDownQ40>((n.z >> 4) & 0x0f0f0f0fu),
+                            down_lookup<kDownQ40>((n.w >> 4) & 0x0f0f0f0fu)};
+          *reinterpret_cast<uint4*>(As[b] + swz(r, 2 * kb)) = lo;
+          *reinterpret_cast<uint4*>(As[b] + swz(r, 2 * kb + 1)) = hi;
+        }
       }
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
@@ -318,24 +344,35 @@ __global__ __launch_bounds__(kThreads) void k_dense_ws(const uint8_t* __restrict
 
 }  // namespace
 
-bool dense_ws_fits(int64_t T, int N, int K) { return T >= kNT && N % kLT == 0 && K % 256 == 0; }
+bool dense_ws_shape(int N, int K) { return N % kLT == 0 && K % 256 == 0; }
 
-hipError_t launch_dense_ws(const uint8_t* x, const uint8_t* w, int64_t T, int N, int K, float* y_f32, uint8_t* y_q8,
-                           const ProbeRows* probe, int num_cus, hipStream_t st) {
+hipError_t launch_dense_ws(const uint8_t* x, const uint8_t* w, int wfmt, int64_t T, int N, int K, float* y_f32,
+                           uint8_t* y_q8, const ProbeRows* probe, int num_cus, hipStream_t st) {
   // one persistent workgroup per CU, a multiple of the XCD count
   int grid = num_cus - num_cus % kXcds;
   if (grid < kXcds) grid = kXcds;
   const int n_rt = N / kLT;
   const int n_tt = (int)((T + kNT - 1) / kNT);
   const int items = n_rt * n_tt;
-  const int group_rows = max(1, min(n_rt, (int)(kGroupBytes / ((int64_t)kLT * (K / 32) * kQ80Bytes))));
+  const int wb = wfmt == kDenseQ40 ? kQ40Bytes : kQ80Bytes;
+  const int group_rows = max(1, min(n_rt, (int)(kGroupBytes / ((int64_t)kLT * (K / 32) * wb))));
   const ProbeRows none = {nullptr, 0, 0};
-  if (probe)
-    hipLaunchKernelGGL(k_dense_ws<true>, dim3(grid), dim3(kThreads), 0, st, x, w, (int)T, N, K, n_rt, n_tt,
-                       group_rows, items, y_f32, y_q8, *probe);
-  else
-    hipLaunchKernelGGL(k_dense_ws<false>, dim3(grid), dim3(kThreads), 0, st, x, w, (int)T, N, K, n_rt, n_tt,
-                       group_rows, items, y_f32, y_q8, none);
+  const ProbeRows pr = probe ? *probe : none;
+  if (wfmt == kDenseQ40) {
+    if (probe)
+      hipLaunchKernelGGL((k_dense_ws<true, kDenseQ40>), dim3(grid), dim3(kThreads), 0, st, x, w, (int)T, N, K, n_rt,
+                         n_tt, group_rows, items, y_f32, y_q8, pr);
+    else
+      hipLaunchKernelGGL((k_dense_ws<false, kDenseQ40>), dim3(grid), dim3(kThreads), 0, st, x, w, (int)T, N, K, n_rt,
+                         n_tt, group_rows, items, y_f32, y_q8, pr);
+  } else {
+    if (probe)
+      hipLaunchKernelGGL((k_dense_ws<true, kDenseQ80>), dim3(grid), dim3(kThreads), 0, st, x, w, (int)T, N, K, n_rt,
+                         n_tt, group_rows, items, y_f32, y_q8, pr);
+    else
+      hipLaunchKernelGGL((k_dense_ws<false, kDenseQ80>), dim3(grid), dim3(kThreads), 0, st, x, w, (int)T, N, K, n_rt,
+                         n_tt, group_rows, items, y_f32, y_q8, pr);
+  }
   return hipGetLastError();
 }
 

@@ -204,11 +204,18 @@ hipError_t launch_copy_i32(const int32_t* src, int32_t* dst, int64_t n, hipStrea
 hipError_t launch_router_topk(const float* logits, int64_t T, int E, int k, int32_t* idx, float* w, hipStream_t st);
 // Latent D / U dense projection, Q8_0 weights [N][K/32] x q8_1 rows [T][K/32]
 // -> fp32 [T][N] and/or q8_1 [T][N/32] (either output may be null).
-hipError_t launch_dense_q8_0(const uint8_t* x, const uint8_t* w, int64_t T, int N, int K, float* y_f32,
-                             uint8_t* y_q8, const ProbeRows* probe, int num_cus, hipStream_t st);
-// The persistent warp-specialized form, for T >= 128, N % 128 == 0, K % 256 == 0.
-bool dense_ws_fits(int64_t T, int N, int K);
-hipError_t launch_dense_ws(const uint8_t* x, const uint8_t* w, int64_t T, int N, int K, float* y_f32, uint8_t* y_q8,
-                           const ProbeRows* probe, int num_cus, hipStream_t st);
+// Weight formats of the projections: Q8_0 (34-byte blocks) and Q4_0 (18-byte
+// blocks, the layout of IQ4_NL with weight = d * (nibble - 8)).
+enum DenseFormat : int { kDenseQ80 = 0, kDenseQ40 = 1 };
+constexpr int kQ80Bytes = 34, kQ40Bytes = 18;
+hipError_t launch_dense(const uint8_t* x, const uint8_t* w, int wfmt, int64_t T, int N, int K, float* y_f32,
+                        uint8_t* y_q8, const ProbeRows* probe, int num_cus, hipStream_t st);
+// Shapes a format's kernels take (Q8_0: all; Q4_0: the GEMV kernel's batches,
+// or N % 128 == 0 and K % 256 == 0).
+bool dense_shape_ok(int wfmt, int64_t T, int N, int K);
+// The persistent warp-specialized form (any T >= 1), for N % 128 == 0 and K % 256 == 0.
+bool dense_ws_shape(int N, int K);
+hipError_t launch_dense_ws(const uint8_t* x, const uint8_t* w, int wfmt, int64_t T, int N, int K, float* y_f32,
+                           uint8_t* y_q8, const ProbeRows* probe, int num_cus, hipStream_t st);
 
 }  // namespace latmoe

@@ -185,6 +185,8 @@ class DenseInputs:
     d_q8_0: np.ndarray   # uint8 [L, H/32, 34]
     z: np.ndarray        # float32 [T, L]
     u_q8_0: np.ndarray   # uint8 [H, L/32, 34]
+    d_q4_0: np.ndarray = None  # uint8 [L, H/32, 18]: D's weights as Q4_0 blocks (drawn after the rest)
+    u_q4_0: np.ndarray = None  # uint8 [H, L/32, 18]
 
 
 def random_q8_0(rng: np.random.Generator, shape: tuple) -> np.ndarray:
@@ -197,6 +199,16 @@ def random_q8_0(rng: np.random.Generator, shape: tuple) -> np.ndarray:
     return b
 
 
+def random_q4_0(rng: np.random.Generator, shape: tuple) -> np.ndarray:
+    """Q4_0 blocks (18 bytes: fp16 d, 16 bytes of nibbles) with the nibble
+    bytes uniform and d ~ U(0.5, 1.5) * 2^-8."""
+    b = np.empty(shape + (18,), np.uint8)
+    b[..., 2:] = rng.integers(0, 256, size=shape + (16,), dtype=np.uint8)
+    d = (rng.uniform(0.5, 1.5, size=shape) * 2.0 ** -8).astype(np.float16)
+    b[..., 0:2] = d.view(np.uint8).reshape(shape + (2,))
+    return b
+
+
 def make_dense_inputs(wl: DenseWorkload) -> DenseInputs:
     if wl.H % 32 or wl.L % 32 or wl.H <= 0 or wl.L <= 0 or wl.T < 0:
         raise ValueError(f"unsupported dense workload shape {wl}")
@@ -205,4 +217,6 @@ def make_dense_inputs(wl: DenseWorkload) -> DenseInputs:
     dw = random_q8_0(rng, (wl.L, wl.H // 32))
     z = rng.standard_normal((wl.T, wl.L), dtype=np.float32)
     uw = random_q8_0(rng, (wl.H, wl.L // 32))
-    return DenseInputs(wl, x, dw, z, uw)
+    dw4 = random_q4_0(rng, (wl.L, wl.H // 32))
+    uw4 = random_q4_0(rng, (wl.H, wl.L // 32))
+    return DenseInputs(wl, x, dw, z, uw, dw4, uw4)

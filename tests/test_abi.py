@@ -99,6 +99,14 @@ def test_dense_argument_errors_before_any_hip_call():
     assert fd(x, w, 4, 64, 64, y, None, None, 0x50000, 0, 0) == 1
     # T = 0 is a no-op that touches nothing
     assert f(None, None, 0, 64, 64, y, None, None) == 0
+    # Q4_0 weights: the same checks, plus the shape rule (T <= 8, or N % 128 == 0 and K % 256 == 0)
+    f4 = lm.lib().lat_moe_dense_q4_0
+    for T, N, K in [(4, 40, 64), (-1, 64, 64), (9, 96, 256), (200, 128, 288), (200, 160, 256), (8, 64, 8192),
+                    (1 << 30, 128, 256)]:
+        assert f4(x, w, T, N, K, y, q, None) == 1, (T, N, K)
+    assert f4(x, w, 4, 64, 64, None, None, None) == 1
+    assert f4(None, w, 200, 128, 256, y, None, None) == 1
+    assert f4(None, None, 0, 128, 256, y, None, None) == 0
 
 
 def test_router_argument_errors_before_any_hip_call():
