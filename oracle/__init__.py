@@ -53,7 +53,8 @@ def lib() -> ctypes.CDLL:
         c.orc_iq4nl_fields.argtypes = [P, i64, P, P]
         c.orc_forward.argtypes = [P, P, P, P, P, i64, i32, i32, i32, i32, P, i64, P, P, P]
         c.orc_forward.restype = i64
-        c.orc_forward_fmt.argtypes = [P, P, P, P, P, i32, i64, i32, i32, i32, i32, P, i64, P, P, P]
+        c.orc_forward_fmt.argtypes = [P, P, P, P, i32, P, i32, i64, i32, i32, i32, i32, P, i64, P, P, P]
+        c.orc_probe_gateup_fmt.argtypes = [P, P, P, i32, i64, i32, i32, i32, i32, i64, P, P, P, P]
         c.orc_forward_fmt.restype = i64
         c.orc_down_combine.argtypes = [P, P, P, P, i64, i32, i32, i32, i32, P, i64, P]
         c.orc_down_combine_fmt.argtypes = [P, P, P, P, i32, i64, i32, i32, i32, i32, P, i64, P]
@@ -129,8 +130,10 @@ def dequant_q4_0(blocks: np.ndarray) -> np.ndarray:
     return out.reshape(b.shape[:-1] + (32,))
 
 
-# Formats of the down weights (both 18 bytes per 32 weights, the same layout).
+# Formats of the down weights (both 18 bytes per 32 weights, the same layout)
+# and of the gate/up weights (Q3_K super-blocks, or Q4_0 blocks).
 DOWN_FORMATS = {"iq4_nl": 0, "q4_0": 1}
+GATEUP_FORMATS = {"q3_k": 0, "q4_0": 1}
 
 
 def dequant_q8_1(blocks: np.ndarray) -> np.ndarray:
@@ -169,10 +172,12 @@ class Result:
 
 def forward(x_q8: np.ndarray, router_idx: np.ndarray, router_w: np.ndarray, gateup: np.ndarray,
             down: np.ndarray, L: int, F: int, E: int, tokens: Optional[Sequence[int]] = None,
-            want_h: bool = True, want_gu: bool = False, down_format: str = "iq4_nl") -> Result:
+            want_h: bool = True, want_gu: bool = False, down_format: str = "iq4_nl",
+            gateup_format: str = "q3_k") -> Result:
     """Whole stage.  y is fp64 [n_tok, L]; h is q8_1 [n_tok*k, F/32, 36] in
     pair order of the evaluated tokens; gu is fp64 [n_tok*k, 2F].  The down
-    weights are IQ4_NL or (down_format "q4_0") Q4_0 blocks."""
+    weights are IQ4_NL or (down_format "q4_0") Q4_0 blocks; the gate/up
+    weights Q3_K or (gateup_format "q4_0") Q4_0 blocks [E, 2F, L/32, 18]."""
     x_q8 = _c(x_q8, np.uint8)
     idx = _c(router_idx, np.int32)
     w = _c(router_w, np.float32)
@@ -184,8 +189,8 @@ def forward(x_q8: np.ndarray, router_idx: np.ndarray, router_w: np.ndarray, gate
     y = np.zeros((n_tok, L), np.float64)
     h = np.zeros((n_tok * k, F // 32, 36), np.uint8) if want_h else None
     gu = np.zeros((n_tok * k, 2 * F), np.float64) if want_gu else None
-    dropped = lib().orc_forward_fmt(_p(x_q8), _p(idx), _p(w), _p(gateup), _p(down), DOWN_FORMATS[down_format], T, L,
-                                    F, E, k, _p(tok), n_tok, _p(y), _p(h), _p(gu))
+    dropped = lib().orc_forward_fmt(_p(x_q8), _p(idx), _p(w), _p(gateup), GATEUP_FORMATS[gateup_format], _p(down),
+                                    DOWN_FORMATS[down_format], T, L, F, E, k, _p(tok), n_tok, _p(y), _p(h), _p(gu))
     return Result(y, h, gu, int(dropped))
 
 
@@ -204,7 +209,7 @@ def down_combine(h_q8: np.ndarray, router_idx: np.ndarray, router_w: np.ndarray,
     return y
 
 
-def probe_gateup(x_q8, router_idx, gateup, L, F, E, pairs, rows, want_i16=False):
+def probe_gateup(x_q8, router_idx, gateup, L, F, E, pairs, rows, want_i16=False, gateup_format="q3_k"):
     idx = _c(router_idx, np.int32)
     T, k = idx.shape
     pairs = _c(pairs, np.int64)
@@ -212,8 +217,8 @@ def probe_gateup(x_q8, router_idx, gateup, L, F, E, pairs, rows, want_i16=False)
     n = pairs.size
     o32 = np.zeros((n, L // 32), np.int32)
     o16 = np.zeros((n, L // 16), np.int32) if want_i16 else None
-    lib().orc_probe_gateup(_p(_c(x_q8, np.uint8)), _p(idx), _p(_c(gateup, np.uint8)), T, L, F, E, k, n, _p(pairs),
-                           _p(rows), _p(o32), _p(o16))
+    lib().orc_probe_gateup_fmt(_p(_c(x_q8, np.uint8)), _p(idx), _p(_c(gateup, np.uint8)),
+                               GATEUP_FORMATS[gateup_format], T, L, F, E, k, n, _p(pairs), _p(rows), _p(o32), _p(o16))
     return (o32, o16) if want_i16 else o32
 
 

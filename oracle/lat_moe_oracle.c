@@ -274,6 +274,31 @@ void orc_iq4nl_fields(const uint8_t* blocks, int64_t nblocks, int8_t* kv, double
  *   I16[s] = sum over the 16 values i of sub-block s of v(i) * q(i)
  * Row = L/256 Q3_K blocks; act = L/32 q8_1 blocks.  dw[sb] gets each
  * super-block's d. */
+/* Gate/up weight formats: Q3_K (110-byte super-blocks of 256, one d per
+ * super-block) or Q4_0 (18-byte blocks of 32, one d per block: dw[b]). */
+#define GU_Q3K 0
+#define GU_Q4_0 1
+static int64_t gu_row_bytes(int fmt, int L) {
+  return fmt == GU_Q4_0 ? (int64_t)(L / 32) * IQ4NL_BYTES : (int64_t)(L / Q3K_VALUES) * Q3K_BYTES;
+}
+
+static void gateup_row_dots_q4_0(const uint8_t* row, const uint8_t* act, int L, int32_t* I32, int32_t* I16,
+                                 double* dw) {
+  for (int b = 0; b < L / 32; ++b) {
+    int8_t v[32];
+    orc_q4_0_decode(row + (int64_t)b * IQ4NL_BYTES, v, &dw[b]);
+    const int8_t* q = (const int8_t*)(act + (int64_t)b * Q81_BYTES + 4);
+    int32_t acc32 = 0;
+    for (int half = 0; half < 2; ++half) {
+      int32_t acc16 = 0;
+      for (int i = 0; i < 16; ++i) acc16 += (int32_t)v[half * 16 + i] * (int32_t)q[half * 16 + i];
+      if (I16) I16[b * 2 + half] = acc16;
+      acc32 += acc16;
+    }
+    I32[b] = acc32;
+  }
+}
+
 static void gateup_row_dots(const uint8_t* row, const uint8_t* act, int L, int32_t* I32, int32_t* I16,
                             double* dw) {
   int nsb = L / Q3K_VALUES;
@@ -317,17 +342,20 @@ static void down_row_dots(int fmt, const uint8_t* row, const uint8_t* h, int F, 
 
 /* Gate/up of one pair: G[F], U[F] in fp64.
  *   G/U[r] = sum over blocks b (ascending) of dw[r][b/8] * dx[b] * I32[r][b]. */
-static void pair_gateup(const uint8_t* xrow, const uint8_t* gu_e, int L, int F, double* G, double* U) {
-  int nb = L / Q81_VALUES, nsb = L / Q3K_VALUES;
-  int64_t row_bytes = (int64_t)nsb * Q3K_BYTES;
+static void pair_gateup(int fmt, const uint8_t* xrow, const uint8_t* gu_e, int L, int F, double* G, double* U) {
+  int nb = L / Q81_VALUES;
+  int64_t row_bytes = gu_row_bytes(fmt, L);
   int32_t* I32 = (int32_t*)malloc(sizeof(int32_t) * nb);
-  double* dw = (double*)malloc(sizeof(double) * nsb);
+  double* dw = (double*)malloc(sizeof(double) * nb);  /* per super-block (Q3_K) or per block (Q4_0) */
   double* dx = (double*)malloc(sizeof(double) * nb);
   for (int b = 0; b < nb; ++b) dx[b] = orc_half_to_double(rd16(xrow + (int64_t)b * Q81_BYTES));
   for (int r = 0; r < 2 * F; ++r) {
-    gateup_row_dots(gu_e + r * row_bytes, xrow, L, I32, NULL, dw);
+    if (fmt == GU_Q4_0)
+      gateup_row_dots_q4_0(gu_e + r * row_bytes, xrow, L, I32, NULL, dw);
+    else
+      gateup_row_dots(gu_e + r * row_bytes, xrow, L, I32, NULL, dw);
     double acc = 0.0;
-    for (int b = 0; b < nb; ++b) acc += dw[b / 8] * dx[b] * (double)I32[b];
+    for (int b = 0; b < nb; ++b) acc += dw[fmt == GU_Q4_0 ? b : b / 8] * dx[b] * (double)I32[b];
     if (r < F) G[r] = acc;
     else U[r - F] = acc;
   }
@@ -379,13 +407,13 @@ static void pair_down(int fmt, const uint8_t* hq, const uint8_t* dn_e, int L, in
  *   gu_out   [n_tok*k][2F] fp64 G then U per pair (NULL to skip)
  * Pairs with an expert id outside [0, E) contribute nothing.  Returns the
  * number of such pairs among the evaluated tokens. */
-int64_t orc_forward_fmt(const uint8_t* x_q8, const int32_t* idx, const float* w, const uint8_t* gateup,
+int64_t orc_forward_fmt(const uint8_t* x_q8, const int32_t* idx, const float* w, const uint8_t* gateup, int gu_fmt,
                         const uint8_t* down, int down_fmt, int64_t T, int L, int F, int E, int k,
                         const int64_t* tokens, int64_t n_tok, double* y, uint8_t* h_out, double* gu_out) {
   if (!tokens) n_tok = T;
   int64_t xrow_bytes = (int64_t)(L / Q81_VALUES) * Q81_BYTES;
   int64_t hrow_bytes = (int64_t)(F / Q81_VALUES) * Q81_BYTES;
-  int64_t gu_e_bytes = (int64_t)2 * F * (L / Q3K_VALUES) * Q3K_BYTES;
+  int64_t gu_e_bytes = (int64_t)2 * F * gu_row_bytes(gu_fmt, L);
   int64_t dn_e_bytes = (int64_t)L * (F / IQ4NL_VALUES) * IQ4NL_BYTES;
   int64_t dropped = 0;
 #pragma omp parallel for schedule(dynamic, 1) reduction(+ : dropped)
@@ -407,7 +435,7 @@ int64_t orc_forward_fmt(const uint8_t* x_q8, const int32_t* idx, const float* w,
           for (int f = 0; f < 2 * F; ++f) gu_out[po * 2 * F + f] = 0.0;
         continue;
       }
-      pair_gateup(x_q8 + t * xrow_bytes, gateup + e * gu_e_bytes, L, F, G, U);
+      pair_gateup(gu_fmt, x_q8 + t * xrow_bytes, gateup + e * gu_e_bytes, L, F, G, U);
       pair_swiglu_q8_1(G, U, F, hq);
       pair_down(down_fmt, hq, down + e * dn_e_bytes, L, F, O);
       double wj = (double)w[t * k + j];
@@ -429,7 +457,8 @@ int64_t orc_forward_fmt(const uint8_t* x_q8, const int32_t* idx, const float* w,
 int64_t orc_forward(const uint8_t* x_q8, const int32_t* idx, const float* w, const uint8_t* gateup,
                     const uint8_t* down, int64_t T, int L, int F, int E, int k, const int64_t* tokens,
                     int64_t n_tok, double* y, uint8_t* h_out, double* gu_out) {
-  return orc_forward_fmt(x_q8, idx, w, gateup, down, DOWN_IQ4NL, T, L, F, E, k, tokens, n_tok, y, h_out, gu_out);
+  return orc_forward_fmt(x_q8, idx, w, gateup, GU_Q3K, down, DOWN_IQ4NL, T, L, F, E, k, tokens, n_tok, y, h_out,
+                         gu_out);
 }
 
 /* Down projection and combine only, from given H (q8_1, [T*k][F/32] in pair
@@ -468,12 +497,12 @@ void orc_down_combine(const uint8_t* h_q8, const int32_t* idx, const float* w, c
  * out16[n][L/16] = I16 (either may be NULL).  Down: for probe n = (pair p,
  * row l < L) with H given in pair order: out[n][F/32] = J32.  Probes whose
  * pair has an invalid expert id are filled with zeros. */
-void orc_probe_gateup(const uint8_t* x_q8, const int32_t* idx, const uint8_t* gateup, int64_t T, int L, int F,
-                      int E, int k, int64_t n, const int64_t* pair, const int32_t* row, int32_t* out32,
-                      int32_t* out16) {
-  int nb = L / Q81_VALUES, nsb = L / Q3K_VALUES;
+void orc_probe_gateup_fmt(const uint8_t* x_q8, const int32_t* idx, const uint8_t* gateup, int gu_fmt, int64_t T,
+                          int L, int F, int E, int k, int64_t n, const int64_t* pair, const int32_t* row,
+                          int32_t* out32, int32_t* out16) {
+  int nb = L / Q81_VALUES;
   int64_t xrow_bytes = (int64_t)nb * Q81_BYTES;
-  int64_t row_bytes = (int64_t)nsb * Q3K_BYTES;
+  int64_t row_bytes = gu_row_bytes(gu_fmt, L);
   (void)T;
 #pragma omp parallel for schedule(static)
   for (int64_t i = 0; i < n; ++i) {
@@ -482,16 +511,25 @@ void orc_probe_gateup(const uint8_t* x_q8, const int32_t* idx, const uint8_t* ga
     int32_t* o32 = out32 ? out32 + i * nb : NULL;
     int32_t* o16 = out16 ? out16 + i * 2 * nb : NULL;
     int32_t tmp32[L / Q81_VALUES];
-    double dw[L / Q3K_VALUES];
+    double dw[L / Q81_VALUES];
     if (e < 0 || e >= E) {
       if (o32) memset(o32, 0, sizeof(int32_t) * nb);
       if (o16) memset(o16, 0, sizeof(int32_t) * 2 * nb);
       continue;
     }
     const uint8_t* wrow = gateup + ((int64_t)e * 2 * F + row[i]) * row_bytes;
-    gateup_row_dots(wrow, x_q8 + (p / k) * xrow_bytes, L, tmp32, o16, dw);
+    if (gu_fmt == GU_Q4_0)
+      gateup_row_dots_q4_0(wrow, x_q8 + (p / k) * xrow_bytes, L, tmp32, o16, dw);
+    else
+      gateup_row_dots(wrow, x_q8 + (p / k) * xrow_bytes, L, tmp32, o16, dw);
     if (o32) memcpy(o32, tmp32, sizeof(int32_t) * nb);
   }
+}
+
+void orc_probe_gateup(const uint8_t* x_q8, const int32_t* idx, const uint8_t* gateup, int64_t T, int L, int F,
+                      int E, int k, int64_t n, const int64_t* pair, const int32_t* row, int32_t* out32,
+                      int32_t* out16) {
+  orc_probe_gateup_fmt(x_q8, idx, gateup, GU_Q3K, T, L, F, E, k, n, pair, row, out32, out16);
 }
 
 void orc_probe_down_fmt(const uint8_t* h_q8, const int32_t* idx, const uint8_t* down, int down_fmt, int64_t T,

@@ -145,6 +145,14 @@ def make_inputs(wl: Workload) -> Inputs:
     return Inputs(wl, x, idx, w, gu, dn, logits)
 
 
+def make_gateup_q4_0(wl: Workload) -> np.ndarray:
+    """The workload's gate/up weights as Q4_0 blocks, uint8 [E, 2F, L/32, 18]
+    (nibble bytes uniform, d ~ U(0.5, 1.5) * 2^-8), from a stream of their own
+    (seed [seed, 4]), so make_inputs' draws are unchanged and nothing is drawn
+    unless they are asked for."""
+    return random_q4_0(np.random.default_rng([wl.seed, 4]), (wl.E, 2 * wl.F, wl.L // 32))
+
+
 def group_sizes(router_idx: np.ndarray, E: int) -> np.ndarray:
     """Tokens routed to each expert (ids outside [0, E) ignored)."""
     ids = router_idx.reshape(-1)
