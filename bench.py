@@ -31,14 +31,15 @@ PEAK_VALU_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12   # 39.3 T lane-ops/s
 METRIC = "expert-stage prefill tokens/s at T=5268; % int8 MFMA peak; HBM GB/s"
 
 
-def algorithmic(wl, idx):
-    """Valid pairs, int8 ops per stage and algorithmic HBM bytes of one call."""
+def algorithmic(wl, idx, gateup_q4_0=False):
+    """Valid pairs, int8 ops per stage and algorithmic HBM bytes of one call
+    (gate/up weights Q3_K, 110 B per 256 values, or Q4_0, 18 B per 32)."""
     import numpy as np
     ids = idx.reshape(-1)
     valid = (ids >= 0) & (ids < wl.E)
     pv = int(valid.sum())
     active = int(np.unique(ids[valid]).size)
-    gu_bytes = 2 * wl.F * (wl.L // 256) * 110
+    gu_bytes = 2 * wl.F * (wl.L // 32) * 18 if gateup_q4_0 else 2 * wl.F * (wl.L // 256) * 110
     dn_bytes = wl.L * (wl.F // 32) * 18
     ops_gateup = 2 * pv * 2 * wl.F * wl.L
     ops_down = 2 * pv * wl.L * wl.F
@@ -54,15 +55,18 @@ def algorithmic(wl, idx):
 
 class Stage:
     """One workload resident on the GPU (down weights IQ4_NL, or with
-    down_format = DOWN_Q4_0 the same bytes read as Q4_0 blocks)."""
+    down_format = DOWN_Q4_0 the same bytes read as Q4_0 blocks; gate/up
+    weights Q3_K, or with gateup_format = GATEUP_Q4_0 Q4_0 blocks drawn for
+    the workload)."""
 
-    def __init__(self, wl, down_format=0):
+    def __init__(self, wl, down_format=0, gateup_format=0):
         import numpy as np
         import torch
         import quantized_latent_moe_amd as lm
         from quantized_latent_moe_amd.inputs import make_inputs
         self.lm, self.torch, self.wl = lm, torch, wl
-        self.down_format = down_format
+        self.down_format, self.gateup_format = down_format, gateup_format
+        self.ex = bool(down_format or gateup_format)
         I = make_inputs(wl)
         self.inputs = I
         dev = torch.device("cuda", 0)
@@ -72,16 +76,21 @@ class Stage:
         lm.quantize_q8_1(x32, self.x)     # the producer's q8_1 rounding; not part of the stage
         del x32
         self.idx, self.w = t(I.router_idx), t(I.router_w)
-        self.gu, self.dn = t(I.gateup_q3k), t(I.down_iq4nl)
+        if gateup_format:
+            from quantized_latent_moe_amd.inputs import make_gateup_q4_0
+            self.gu = t(make_gateup_q4_0(wl))
+        else:
+            self.gu = t(I.gateup_q3k)
+        self.dn = t(I.down_iq4nl)
         self.s = lm.shapes(wl.T, wl.L, wl.F, wl.E, wl.k)
         self.ws = torch.empty(lm.workspace_size(self.s), dtype=torch.uint8, device=dev)
         self.y = torch.empty((wl.T, wl.L), dtype=torch.float32, device=dev)
         torch.cuda.synchronize()
 
     def step(self):
-        if self.down_format:
+        if self.ex:
             self.lm.expert_forward_ex(self.x, self.idx, self.w, self.gu, self.dn, self.down_format, self.s, self.y,
-                                      self.ws)
+                                      self.ws, gateup_format=self.gateup_format)
         else:
             self.lm.expert_forward(self.x, self.idx, self.w, self.gu, self.dn, self.s, self.y, self.ws)
 
@@ -97,9 +106,9 @@ class Stage:
             torch.cuda.synchronize()
 
     def step_timed(self, events):
-        if self.down_format:
+        if self.ex:
             self.lm.expert_forward_ex(self.x, self.idx, self.w, self.gu, self.dn, self.down_format, self.s, self.y,
-                                      self.ws, debug=True, stage_events=events)
+                                      self.ws, gateup_format=self.gateup_format, debug=True, stage_events=events)
         else:
             self.lm.expert_forward_debug(self.x, self.idx, self.w, self.gu, self.dn, self.s, self.y, self.ws,
                                          stage_events=events)
@@ -414,7 +423,7 @@ def cpu_baseline(wl, target_s):
             "sample": f"first {n} of {wl.T} tokens of {wl.name} ({n * wl.k} routed pairs), {dt:.1f} s"}
 
 
-KERNEL_SOURCES = {"k_gateup": "gateup.hip", "k_down": "down.hip"}
+KERNEL_SOURCES = {"k_gateup": "gateup.hip", "k_down": "down.hip", "k_gateup_q40": "gateup_q40.hip"}
 
 
 def kernel_source_hash(kernel):
@@ -479,23 +488,26 @@ def pmc_summary(fetch_dir, write_dir, kernel, copy_mib):
     print(f"hbm_bytes_per_launch {fetch + write:.0f}")
 
 
-def down_q4_0_report(steps, warmup):
-    """The stage with Q4_0 down weights (each workload's random down blocks
-    read as Q4_0, the same bytes): time per step, stage times and the down
-    kernel against its fold roof, at prefill_5k and decode."""
+def q4_0_report(steps, warmup, gateup_q4_0, workloads=("prefill_5k", "decode")):
+    """The stage with Q4_0 weights: down weights Q4_0 (each workload's random
+    down blocks read as Q4_0, the same bytes), and with gateup_q4_0 the
+    gate/up weights Q4_0 too (drawn for the workload).  Time per step, stage
+    times and the Q4_0 kernels against their fold roof, at prefill_5k and
+    decode (or the given workloads)."""
     import torch
     import quantized_latent_moe_amd as lm
     from quantized_latent_moe_amd.inputs import WORKLOADS
     names = ["route", "gateup", "down", "combine"]
+    label = "Q4_0 gate/up + down" if gateup_q4_0 else "Q4_0 down"
     rep = {}
-    for name in ("prefill_5k", "decode"):
+    for name in workloads:
         wl = WORKLOADS[name]
-        st = Stage(wl, down_format=lm.DOWN_Q4_0)
+        st = Stage(wl, down_format=lm.DOWN_Q4_0, gateup_format=lm.GATEUP_Q4_0 if gateup_q4_0 else 0)
         st.prime()
-        n = steps if name == "prefill_5k" else max(steps, 50)
+        n = steps if name != "decode" else max(steps, 50)
         ms, _ = st.time_steps(n, warmup)
         stages = st.stage_times(n)
-        alg = algorithmic(wl, st.inputs.router_idx)
+        alg = algorithmic(wl, st.inputs.router_idx, gateup_q4_0=gateup_q4_0)
         r = {"workload": name, "ms_per_step": round(ms, 5), "tokens_per_s": round(wl.T / (ms * 1e-3), 1),
              "stage_ms": {k: round(v, 5) for k, v in zip(names, stages)}}
         if name == "prefill_5k":
@@ -503,11 +515,17 @@ def down_q4_0_report(steps, warmup):
             r["down_roofline"] = {"bound": "alu", "kernel": "k_down (Q4_0)", "achieved": round(fold, 2),
                                   "peak": round(PEAK_VALU_TOPS, 1), "unit": "T lane-op/s",
                                   "frac": round(fold / PEAK_VALU_TOPS, 4)}
+            if gateup_q4_0:
+                fold = alg["fold_gateup"] / (stages[1] * 1e-3) / 1e12
+                r["gateup_roofline"] = {"bound": "alu", "kernel": "k_gateup_q40", "achieved": round(fold, 2),
+                                        "peak": round(PEAK_VALU_TOPS, 1), "unit": "T lane-op/s",
+                                        "frac": round(fold / PEAK_VALU_TOPS, 4),
+                                        "traffic": read_traffic("k_gateup_q40", name)}
         else:
             gbs = alg["bytes"] / (ms * 1e-3) / 1e9
-            r.update(hbm_gbs=round(gbs, 1), hbm_frac=round(gbs / PEAK_HBM_GBS, 4))
-        print(f"[bench] Q4_0 down, {name}: {ms * 1e3:.1f} us/step, down {stages[2] * 1e3:.1f} us", file=sys.stderr,
-              flush=True)
+            r.update(alg_bytes=alg["bytes"], hbm_gbs=round(gbs, 1), hbm_frac=round(gbs / PEAK_HBM_GBS, 4))
+        print(f"[bench] {label}, {name}: {ms * 1e3:.1f} us/step, gate/up {stages[1] * 1e3:.1f} us, "
+              f"down {stages[2] * 1e3:.1f} us", file=sys.stderr, flush=True)
         rep[name] = r
         del st
         torch.cuda.empty_cache()
@@ -526,7 +544,9 @@ def main():
     ap.add_argument("--du-only", action="store_true", help="time only the latent D / U projections")
     ap.add_argument("--no-per-config", action="store_true",
                     help="skip the cold-cache timing of every workload (per_config)")
-    ap.add_argument("--no-formats", action="store_true", help="skip the Q4_0 down-weight timings")
+    ap.add_argument("--no-formats", action="store_true", help="skip the Q4_0 weight timings")
+    ap.add_argument("--formats-only", action="store_true",
+                    help="time only the stage with Q4_0 gate/up and down weights, at --workload")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="first run a plain device copy of MIB MiB (three times), the reference for counter scaling")
@@ -565,6 +585,9 @@ def main():
             if name == "du_prefill_5k" and not args.no_cpu_baseline:
                 rep["cpu_baseline"] = cpu_baseline_dense(DENSE_WORKLOADS[name], 3.0)
             print(json.dumps(rep), flush=True)
+        return
+    if args.formats_only:
+        print(json.dumps(q4_0_report(args.steps, args.warmup, gateup_q4_0=True, workloads=(wl.name,))), flush=True)
         return
     st = Stage(wl)
     st.prime()
@@ -637,7 +660,8 @@ def main():
         print(f"[bench] decode {dms * 1e3:.2f} us/step, {gbs:.0f} GB/s", file=sys.stderr, flush=True)
         del ds
     if not args.no_formats:
-        out["down_q4_0"] = down_q4_0_report(args.steps, args.warmup)
+        out["down_q4_0"] = q4_0_report(args.steps, args.warmup, gateup_q4_0=False)
+        out["gateup_down_q4_0"] = q4_0_report(args.steps, args.warmup, gateup_q4_0=True)
     if not args.no_per_config:
         out["device"] = device_info()
         out["per_config"] = per_config(["tiny", "decode", "mid_prefill", "prefill_5k", "prefill_21k"])

@@ -129,15 +129,26 @@ int lat_moe_expert_forward_debug(const void* x_q8_1, const int32_t* router_idx, 
 #define LAT_MOE_DOWN_IQ4_NL 0
 #define LAT_MOE_DOWN_Q4_0 1
 
-/* The expert stage with a choice of down-weight format: down is
- * [E][L][F/32] blocks of down_format (LAT_MOE_DOWN_IQ4_NL or
- * LAT_MOE_DOWN_Q4_0; any other value returns LAT_MOE_EINVAL).  Every other
- * argument, rule and result is that of lat_moe_expert_forward; dbg may be NULL
- * (then nothing more is written) or as for lat_moe_expert_forward_debug, whose
- * down_i32 dots are then sum K(index) * qH with the format's K.  With
+/* Formats of the gate/up weights for lat_moe_expert_forward_ex:
+ *   LAT_MOE_GATEUP_Q3_K  [E][2F][L/256] Q3_K super-blocks (110 B), as above;
+ *   LAT_MOE_GATEUP_Q4_0  [E][2F][L/32] Q4_0 blocks (18 B, the layout above,
+ *                        weight = d * (nibble - 8)), one scale per 32 values:
+ *                        G/U = sum over blocks of d_w * d_x * I32, with I32
+ *                        the int32 dot of the nibble - 8 values and the
+ *                        activation codes (the gateup_i32 probe). */
+#define LAT_MOE_GATEUP_Q3_K 0
+#define LAT_MOE_GATEUP_Q4_0 1
+
+/* The expert stage with a choice of weight formats: gateup is [E][2F][...]
+ * blocks of gateup_format and down [E][L][F/32] blocks of down_format (any
+ * other value returns LAT_MOE_EINVAL).  Every other argument, rule and result
+ * is that of lat_moe_expert_forward (with Q4_0 gate/up weights one expert's
+ * 2F * L/32 * 18 bytes must stay below 2^31); dbg may be NULL (then nothing
+ * more is written) or as for lat_moe_expert_forward_debug, whose probes then
+ * hold the formats' integer dots.  With LAT_MOE_GATEUP_Q3_K and
  * LAT_MOE_DOWN_IQ4_NL the call is lat_moe_expert_forward(_debug). */
 int lat_moe_expert_forward_ex(const void* x_q8_1, const int32_t* router_idx, const float* router_w,
-                              const void* gateup_q3k, const void* down, int32_t down_format,
+                              const void* gateup, int32_t gateup_format, const void* down, int32_t down_format,
                               const lat_moe_shapes* shapes, float* y, void* workspace, size_t workspace_bytes,
                               void* stream, const lat_moe_debug* dbg);
 

@@ -18,6 +18,9 @@ LAT_MOE_MAX_E = 1024
 # down-weight formats of lat_moe_expert_forward_ex (both 18-byte blocks of 32)
 DOWN_IQ4_NL = 0
 DOWN_Q4_0 = 1
+# gate/up-weight formats of lat_moe_expert_forward_ex
+GATEUP_Q3_K = 0
+GATEUP_Q4_0 = 1
 
 # Symbols the C header declares (checked by the CPU test suite).
 EXPORTED = (
@@ -80,8 +83,8 @@ def lib() -> ctypes.CDLL:
         c.lat_moe_expert_forward_debug.argtypes = [P, P, P, P, P, ctypes.POINTER(Shapes), P, P, ctypes.c_size_t, P,
                                                    ctypes.POINTER(Debug)]
         c.lat_moe_expert_forward_debug.restype = ctypes.c_int
-        c.lat_moe_expert_forward_ex.argtypes = [P, P, P, P, P, ctypes.c_int32, ctypes.POINTER(Shapes), P, P,
-                                                ctypes.c_size_t, P, ctypes.POINTER(Debug)]
+        c.lat_moe_expert_forward_ex.argtypes = [P, P, P, P, ctypes.c_int32, P, ctypes.c_int32, ctypes.POINTER(Shapes),
+                                                P, P, ctypes.c_size_t, P, ctypes.POINTER(Debug)]
         c.lat_moe_expert_forward_ex.restype = ctypes.c_int
         c.lat_moe_quantize_q8_1.argtypes = [P, ctypes.c_int64, ctypes.c_int32, P, P]
         c.lat_moe_quantize_q8_1.restype = ctypes.c_int
@@ -168,18 +171,21 @@ def expert_forward_debug(x_q8_1, router_idx, router_w, gateup_q3k, down_iq4nl, s
     _check(rc)
 
 
-def expert_forward_ex(x_q8_1, router_idx, router_w, gateup_q3k, down, down_format: int, s: Shapes, y, workspace, *,
-                      debug: bool = False, h_q8_1=None, perm=None, offsets=None, dropped=None, gateup_i32=None,
-                      gu_row0=0, down_i32=None, dn_row0=0, stage_events=None, stream=None) -> None:
-    """The expert stage with down weights in down_format (DOWN_IQ4_NL or
-    DOWN_Q4_0, both [E, L, F/32, 18] uint8); with debug=True the optional
-    outputs of expert_forward_debug are filled, otherwise no debug struct is
-    passed."""
+def expert_forward_ex(x_q8_1, router_idx, router_w, gateup, down, down_format: int, s: Shapes, y, workspace, *,
+                      gateup_format: int = GATEUP_Q3_K, debug: bool = False, h_q8_1=None, perm=None, offsets=None,
+                      dropped=None, gateup_i32=None, gu_row0=0, down_i32=None, dn_row0=0, stage_events=None,
+                      stream=None) -> None:
+    """The expert stage with gate/up weights in gateup_format (GATEUP_Q3_K:
+    [E, 2F, L/256, 110]; GATEUP_Q4_0: [E, 2F, L/32, 18]) and down weights in
+    down_format (DOWN_IQ4_NL or DOWN_Q4_0, both [E, L, F/32, 18] uint8); with
+    debug=True the optional outputs of expert_forward_debug are filled,
+    otherwise no debug struct is passed."""
     d = None
     if debug:
         d, ev = _debug(h_q8_1, perm, offsets, dropped, gateup_i32, gu_row0, down_i32, dn_row0, stage_events)
-    rc = lib().lat_moe_expert_forward_ex(_ptr(x_q8_1), _ptr(router_idx), _ptr(router_w), _ptr(gateup_q3k), _ptr(down),
-                                         int(down_format), ctypes.byref(s), _ptr(y), _ptr(workspace),
+    rc = lib().lat_moe_expert_forward_ex(_ptr(x_q8_1), _ptr(router_idx), _ptr(router_w), _ptr(gateup),
+                                         int(gateup_format), _ptr(down), int(down_format), ctypes.byref(s), _ptr(y),
+                                         _ptr(workspace),
                                          workspace.numel() * workspace.element_size(), _stream(stream),
                                          ctypes.byref(d) if d is not None else None)
     _check(rc)

@@ -97,11 +97,14 @@ int check_device(int* num_cus) {
   return state[dev] == 1 ? LAT_MOE_OK : LAT_MOE_EDEVICE;
 }
 
-int forward_impl(const void* x, const int32_t* idx, const float* w, const void* gu, const void* dn, int down_fmt,
-                 const lat_moe_shapes* s, float* y, void* ws, size_t ws_bytes, void* stream,
+int forward_impl(const void* x, const int32_t* idx, const float* w, const void* gu, int gu_fmt, const void* dn,
+                 int down_fmt, const lat_moe_shapes* s, float* y, void* ws, size_t ws_bytes, void* stream,
                  const lat_moe_debug* dbg) {
   if (!shapes_ok(s)) return LAT_MOE_EINVAL;
   if (down_fmt != LAT_MOE_DOWN_IQ4_NL && down_fmt != LAT_MOE_DOWN_Q4_0) return LAT_MOE_EINVAL;
+  if (gu_fmt != LAT_MOE_GATEUP_Q3_K && gu_fmt != LAT_MOE_GATEUP_Q4_0) return LAT_MOE_EINVAL;
+  // one expert's Q4_0 gate/up weights below 2 GiB too (32-bit offsets)
+  if (gu_fmt == LAT_MOE_GATEUP_Q4_0 && (int64_t)2 * s->F * (s->L / 32) * 18 >= (int64_t)1 << 31) return LAT_MOE_EINVAL;
   if (s->T > 0) {
     const void* ptrs[] = {x, idx, w, gu, dn, y, ws};
     for (const void* p : ptrs)
@@ -131,16 +134,19 @@ int forward_impl(const void* x, const int32_t* idx, const float* w, const void* 
   hipEvent_t const* ev = (dbg && dbg->stage_events) ? reinterpret_cast<hipEvent_t const*>(dbg->stage_events) : nullptr;
   auto mark = [&](int i) { return ev ? hipEventRecord(ev[i], st) : hipSuccess; };
   if (mark(0) != hipSuccess) return LAT_MOE_ELAUNCH;
-  if (launch_route(idx, xb, sh, wk, st) != hipSuccess) return LAT_MOE_ELAUNCH;
+  const bool small = small_path(sh);  // decode-sized batch: GEMV-shaped kernels
+  // Q4_0 gate/up weights take the persistent kernel at every batch size
+  const bool gu_small = small && gu_fmt == LAT_MOE_GATEUP_Q3_K;
+  if (launch_route(idx, xb, sh, wk, gu_small, st) != hipSuccess) return LAT_MOE_ELAUNCH;
   if (mark(1) != hipSuccess) return LAT_MOE_ELAUNCH;
   ProbeRows pg{nullptr, 0, 0}, pd{nullptr, 0, 0};
   if (dbg && dbg->gateup_i32) pg = ProbeRows{dbg->gateup_i32, dbg->gu_row0, dbg->gu_rows};
   if (dbg && dbg->down_i32) pd = ProbeRows{dbg->down_i32, dbg->dn_row0, dbg->dn_rows};
-  const bool small = small_path(sh);  // decode-sized batch: GEMV-shaped kernels
   const uint8_t* gub = static_cast<const uint8_t*>(gu);
   const uint8_t* dnb = static_cast<const uint8_t*>(dn);
-  if ((small ? launch_gateup_small(sh, wk, gub, pg.out ? &pg : nullptr, st)
-             : launch_gateup(sh, wk, gub, pg.out ? &pg : nullptr, st)) != hipSuccess)
+  if ((gu_fmt == LAT_MOE_GATEUP_Q4_0 ? launch_gateup_q40(sh, wk, gub, pg.out ? &pg : nullptr, st)
+       : gu_small                     ? launch_gateup_small(sh, wk, gub, pg.out ? &pg : nullptr, st)
+                                      : launch_gateup(sh, wk, gub, pg.out ? &pg : nullptr, st)) != hipSuccess)
     return LAT_MOE_ELAUNCH;
   if (mark(2) != hipSuccess) return LAT_MOE_ELAUNCH;
   const int fmt = down_fmt == LAT_MOE_DOWN_Q4_0 ? kDownQ40 : kDownIq4Nl;
@@ -199,8 +205,8 @@ size_t lat_moe_workspace_size(const lat_moe_shapes* shapes) {
 int lat_moe_expert_forward(const void* x_q8_1, const int32_t* router_idx, const float* router_w,
                            const void* gateup_q3k, const void* down_iq4nl, const lat_moe_shapes* shapes, float* y,
                            void* workspace, size_t workspace_bytes, void* stream) {
-  return forward_impl(x_q8_1, router_idx, router_w, gateup_q3k, down_iq4nl, LAT_MOE_DOWN_IQ4_NL, shapes, y, workspace,
-                      workspace_bytes, stream, nullptr);
+  return forward_impl(x_q8_1, router_idx, router_w, gateup_q3k, LAT_MOE_GATEUP_Q3_K, down_iq4nl, LAT_MOE_DOWN_IQ4_NL,
+                      shapes, y, workspace, workspace_bytes, stream, nullptr);
 }
 
 int lat_moe_expert_forward_debug(const void* x_q8_1, const int32_t* router_idx, const float* router_w,
@@ -208,15 +214,15 @@ int lat_moe_expert_forward_debug(const void* x_q8_1, const int32_t* router_idx, 
                                  float* y, void* workspace, size_t workspace_bytes, void* stream,
                                  const lat_moe_debug* dbg) {
   if (!dbg) return LAT_MOE_EINVAL;
-  return forward_impl(x_q8_1, router_idx, router_w, gateup_q3k, down_iq4nl, LAT_MOE_DOWN_IQ4_NL, shapes, y, workspace,
-                      workspace_bytes, stream, dbg);
+  return forward_impl(x_q8_1, router_idx, router_w, gateup_q3k, LAT_MOE_GATEUP_Q3_K, down_iq4nl, LAT_MOE_DOWN_IQ4_NL,
+                      shapes, y, workspace, workspace_bytes, stream, dbg);
 }
 
 int lat_moe_expert_forward_ex(const void* x_q8_1, const int32_t* router_idx, const float* router_w,
-                              const void* gateup_q3k, const void* down, int32_t down_format,
+                              const void* gateup, int32_t gateup_format, const void* down, int32_t down_format,
                               const lat_moe_shapes* shapes, float* y, void* workspace, size_t workspace_bytes,
                               void* stream, const lat_moe_debug* dbg) {
-  return forward_impl(x_q8_1, router_idx, router_w, gateup_q3k, down, down_format, shapes, y, workspace,
+  return forward_impl(x_q8_1, router_idx, router_w, gateup, gateup_format, down, down_format, shapes, y, workspace,
                       workspace_bytes, stream, dbg);
 }
 

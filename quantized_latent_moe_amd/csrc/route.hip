@@ -374,15 +374,15 @@ __global__ __launch_bounds__(256) void k_route_scatter(const int32_t* __restrict
 
 }  // namespace
 
-hipError_t launch_route(const int32_t* idx, const uint8_t* x, const Shapes& s, const Work& w, hipStream_t st) {
+hipError_t launch_route(const int32_t* idx, const uint8_t* x, const Shapes& s, const Work& w, bool gather,
+                        hipStream_t st) {
   const int64_t n = s.pairs();
   int nbits = 0;
   while ((1 << nbits) < s.E) ++nbits;
   const int64_t nxb = s.T * (s.L / 32);
   const unsigned xblocks = (unsigned)((nxb + kSplitPerBlock - 1) / kSplitPerBlock);
-  // The small-batch kernels read the gathered rows and not the split ones
-  // (small batches: T * k <= kGatherRows and L <= 1024).
-  const bool gather = small_path(s);
+  // The GEMV-shaped gate/up kernel reads the gathered rows and not the split
+  // ones (small batches: T * k <= kGatherRows and L <= 1024).
   if (n <= kSmallPairs && s.E <= 512) {  // (2 + 16) * E + kGatherRows ints of LDS
     hipLaunchKernelGGL(k_route_small, dim3(gather ? 1 : 1 + xblocks), dim3(1024),
                        ((2 + 16) * s.E + kGatherRows) * sizeof(int32_t), st, idx, (int)n, s.E, nbits, w.offsets,

@@ -65,12 +65,18 @@ def test_argument_errors_before_any_hip_call():
     assert rc == 1
     # the format entry point: its format argument is checked first, then as above
     ex = lm.lib().lat_moe_expert_forward_ex
-    for fmt, rc in ((lm.DOWN_IQ4_NL, 0), (lm.DOWN_Q4_0, 0), (2, 1), (-1, 1)):
-        assert ex(None, None, None, None, None, fmt, ctypes.byref(lm.shapes(0, 256, 512, 8, 2)), None, None, 0, None,
-                  None) == rc, fmt
-    assert ex(*good[:5], 7, ctypes.byref(s), good[5], good[6], need, None, None) == 1
-    assert ex(*good[:4], None, lm.DOWN_Q4_0, ctypes.byref(s), good[5], good[6], need, None, None) == 1
-    assert ex(*good[:5], lm.DOWN_Q4_0, ctypes.byref(s), good[5], good[6], need - 1, None, None) == 2
+    s0 = ctypes.byref(lm.shapes(0, 256, 512, 8, 2))
+    for gfmt, dfmt, rc in ((lm.GATEUP_Q3_K, lm.DOWN_IQ4_NL, 0), (lm.GATEUP_Q4_0, lm.DOWN_Q4_0, 0),
+                           (lm.GATEUP_Q3_K, 2, 1), (lm.GATEUP_Q3_K, -1, 1), (2, lm.DOWN_IQ4_NL, 1)):
+        assert ex(None, None, None, None, gfmt, None, dfmt, s0, None, None, 0, None, None) == rc, (gfmt, dfmt)
+    g5 = good[:4] + [lm.GATEUP_Q3_K, good[4]]
+    assert ex(*g5, 7, ctypes.byref(s), good[5], good[6], need, None, None) == 1
+    assert ex(*good[:4], lm.GATEUP_Q4_0, None, lm.DOWN_Q4_0, ctypes.byref(s), good[5], good[6], need, None, None) == 1
+    assert ex(*g5, lm.DOWN_Q4_0, ctypes.byref(s), good[5], good[6], need - 1, None, None) == 2
+    # one expert's Q4_0 gate/up rows past 2 GiB (Q3_K rows of the same shape fit)
+    big = lm.shapes(1, 65536, 32768, 1, 1)
+    assert ex(*good[:4], lm.GATEUP_Q4_0, good[4], lm.DOWN_Q4_0, ctypes.byref(big), good[5], good[6], 1 << 40, None,
+              None) == 1
     assert lm.lib().lat_moe_quantize_q8_1(0x1000, 4, 40, 0x2000, None) == 1
     assert lm.lib().lat_moe_quantize_q8_1(0x1004, 4, 64, 0x2000, None) == 1
     assert lm.lib().lat_moe_quantize_q8_1(None, 0, 64, None, None) == 0

@@ -119,3 +119,99 @@ def test_q4_0_down_full_size_sampled():
     rng = np.random.default_rng(17)
     toks = np.array(sorted(set(rng.choice(wl.T, 10, replace=False).tolist()) | {0, wl.T - 1}), np.int64)
     _check(I, xq, out, dn_rows, toks=toks)
+
+
+# ---- Q4_0 gate/up weights (the persistent kernel at every batch size) ------
+
+def _run_gu(I, xq, gu, down_format, gu_rows, dn_rows):
+    wl = I.wl
+    dev = torch.device("cuda", 0)
+    P = wl.T * wl.k
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    x, idx, w = t(xq), t(I.router_idx.astype(np.int32)), t(I.router_w.astype(np.float32))
+    g, dn = t(gu), t(I.down_iq4nl)
+    s = lm.shapes(wl.T, wl.L, wl.F, wl.E, wl.k)
+    ws = torch.empty(max(lm.workspace_size(s), 256), dtype=torch.uint8, device=dev)
+    y = torch.full((max(wl.T, 1), wl.L), np.nan, dtype=torch.float32, device=dev)
+    h = torch.empty((P, wl.F // 32, 36), dtype=torch.uint8, device=dev)
+    perm = torch.full((P,), -7, dtype=torch.int32, device=dev)
+    gi = torch.zeros((P, gu_rows[1], wl.L // 32), dtype=torch.int32, device=dev)
+    di = torch.zeros((P, dn_rows[1], wl.F // 32), dtype=torch.int32, device=dev)
+    lm.expert_forward_ex(x, idx, w, g, dn, down_format, s, y, ws, gateup_format=lm.GATEUP_Q4_0, debug=True,
+                         h_q8_1=h, perm=perm, gateup_i32=gi, gu_row0=gu_rows[0], down_i32=di, dn_row0=dn_rows[0])
+    torch.cuda.synchronize()
+    out = dict(y=y[:wl.T].cpu().numpy(), h=h.cpu().numpy(), perm=perm.cpu().numpy(), gu_i32=gi.cpu().numpy(),
+               dn_i32=di.cpu().numpy())
+    y2 = torch.full_like(y, np.nan)
+    lm.expert_forward_ex(x, idx, w, g, dn, down_format, s, y2, ws, gateup_format=lm.GATEUP_Q4_0)
+    torch.cuda.synchronize()
+    out["y_plain"] = y2[:wl.T].cpu().numpy()
+    return out
+
+
+def _check_gu(I, xq, gu, out, dfmt, gu_rows, dn_rows, toks=None):
+    wl = I.wl
+    ids = I.router_idx.reshape(-1)
+    valid = (ids >= 0) & (ids < wl.E)
+    order = np.nonzero(valid)[0][np.argsort(ids[valid], kind="stable")]
+    assert np.array_equal(out["perm"][: order.size], order.astype(np.int32))
+    if toks is None:
+        toks = np.arange(wl.T)
+    allp = (toks[:, None] * wl.k + np.arange(wl.k)[None, :]).reshape(-1)
+    pairs = allp[valid[allp]]
+    r0, nr = gu_rows
+    pp, rr = np.repeat(pairs, nr), np.tile(np.arange(r0, r0 + nr), pairs.size).astype(np.int32)
+    ref = oracle.probe_gateup(xq, I.router_idx, gu, wl.L, wl.F, wl.E, pp, rr, gateup_format=Q40)
+    assert np.array_equal(out["gu_i32"][pairs].reshape(-1, wl.L // 32), ref), "Q4_0 gate/up block dots differ"
+    r0, nr = dn_rows
+    pp, rr = np.repeat(pairs, nr), np.tile(np.arange(r0, r0 + nr), pairs.size).astype(np.int32)
+    ref = oracle.probe_down(out["h"], I.router_idx, I.down_iq4nl, wl.L, wl.F, wl.E, pp, rr, down_format=dfmt)
+    assert np.array_equal(out["dn_i32"][pairs].reshape(-1, wl.F // 32), ref), "down block dots differ"
+    say(f"{wl.name}: {pairs.size} pairs of Q4_0 gate/up and {dfmt} down block dots bit-exact")
+    full = oracle.forward(xq, I.router_idx, I.router_w, gu, I.down_iq4nl, wl.L, wl.F, wl.E, tokens=toks,
+                          gateup_format=Q40, down_format=dfmt)
+    check_h(out["h"][allp], full.h, label=f"{wl.name} (Q4_0 gate/up)")
+    ys = oracle.down_combine(out["h"], I.router_idx, I.router_w, I.down_iq4nl, wl.L, wl.F, wl.E, tokens=toks,
+                             down_format=dfmt)
+    check_y(out["y"][toks], ys, label=f"{wl.name} Q4_0 gate/up stage-wise")
+    e2e = np.abs(out["y"][toks] - full.y).max() / np.sqrt(np.mean(full.y ** 2))
+    say(f"{wl.name} Q4_0 gate/up end-to-end y max|err|/rms = {e2e:.3e}")
+    assert e2e < 2e-2
+    assert np.array_equal(out["y_plain"], out["y"])
+
+
+GU_CASES = [
+    (WORKLOADS["tiny"], "q4_0"),
+    (WORKLOADS["decode"], "iq4_nl"),                                                     # 32 pairs: 1-token tiles
+    (Workload("gu40_one_step", T=100, L=256, F=96, E=4, k=2, zipf_s=1.1, seed=41), "q4_0"),  # one K step, half tile
+    (Workload("gu40_ragged", T=200, L=512, F=288, E=6, k=3, zipf_s=1.1, n_masked=1, seed=42), "iq4_nl"),
+    (Workload("gu40_wide", T=300, L=1024, F=512, E=8, k=4, zipf_s=1.1, seed=43), "q4_0"),
+    (Workload("gu40_few", T=6, L=768, F=160, E=5, k=4, zipf_s=1.1, seed=44), "q4_0"),
+]
+
+
+@pytest.mark.parametrize("wl,dfmt", GU_CASES, ids=lambda v: getattr(v, "name", v))
+def test_q4_0_gateup_full_compare(wl, dfmt):
+    from quantized_latent_moe_amd.inputs import make_gateup_q4_0
+    say(f"Q4_0 gate/up case {wl}, down {dfmt}")
+    I = make_inputs(wl)
+    xq = oracle.quantize_q8_1(I.x)
+    gu = make_gateup_q4_0(wl)
+    gu_rows = (max(0, wl.F - 24), min(48, 2 * wl.F - max(0, wl.F - 24)))
+    dn_rows = (wl.L - 32, 32)
+    out = _run_gu(I, xq, gu, lm.DOWN_Q4_0 if dfmt == "q4_0" else lm.DOWN_IQ4_NL, gu_rows, dn_rows)
+    _check_gu(I, xq, gu, out, dfmt, gu_rows, dn_rows)
+
+
+def test_q4_0_gateup_full_size_sampled():
+    from quantized_latent_moe_amd.inputs import make_gateup_q4_0
+    wl = WORKLOADS["prefill_5k"]
+    say(f"Q4_0 gate/up case {wl} (sampled)")
+    I = make_inputs(wl)
+    xq = oracle.quantize_q8_1(I.x)
+    gu = make_gateup_q4_0(wl)
+    out = _run_gu(I, xq, gu, lm.DOWN_Q4_0, (wl.F - 4, 8), (0, 8))
+    say(f"{wl.name} Q4_0 gate/up: GPU done")
+    rng = np.random.default_rng(19)
+    toks = np.array(sorted(set(rng.choice(wl.T, 10, replace=False).tolist()) | {0, wl.T - 1}), np.int64)
+    _check_gu(I, xq, gu, out, "q4_0", (wl.F - 4, 8), (0, 8), toks=toks)
