@@ -134,19 +134,17 @@ int forward_impl(const void* x, const int32_t* idx, const float* w, const void* 
   hipEvent_t const* ev = (dbg && dbg->stage_events) ? reinterpret_cast<hipEvent_t const*>(dbg->stage_events) : nullptr;
   auto mark = [&](int i) { return ev ? hipEventRecord(ev[i], st) : hipSuccess; };
   if (mark(0) != hipSuccess) return LAT_MOE_ELAUNCH;
-  const bool small = small_path(sh);  // decode-sized batch: GEMV-shaped kernels
-  // Q4_0 gate/up weights take the persistent kernel at every batch size
-  const bool gu_small = small && gu_fmt == LAT_MOE_GATEUP_Q3_K;
-  if (launch_route(idx, xb, sh, wk, gu_small, st) != hipSuccess) return LAT_MOE_ELAUNCH;
+  const bool small = small_path(sh);  // decode-sized batch: GEMV-shaped kernels (either weight format)
+  if (launch_route(idx, xb, sh, wk, small, st) != hipSuccess) return LAT_MOE_ELAUNCH;
   if (mark(1) != hipSuccess) return LAT_MOE_ELAUNCH;
   ProbeRows pg{nullptr, 0, 0}, pd{nullptr, 0, 0};
   if (dbg && dbg->gateup_i32) pg = ProbeRows{dbg->gateup_i32, dbg->gu_row0, dbg->gu_rows};
   if (dbg && dbg->down_i32) pd = ProbeRows{dbg->down_i32, dbg->dn_row0, dbg->dn_rows};
   const uint8_t* gub = static_cast<const uint8_t*>(gu);
   const uint8_t* dnb = static_cast<const uint8_t*>(dn);
-  if ((gu_fmt == LAT_MOE_GATEUP_Q4_0 ? launch_gateup_q40(sh, wk, gub, pg.out ? &pg : nullptr, st)
-       : gu_small                     ? launch_gateup_small(sh, wk, gub, pg.out ? &pg : nullptr, st)
-                                      : launch_gateup(sh, wk, gub, pg.out ? &pg : nullptr, st)) != hipSuccess)
+  if ((small                          ? launch_gateup_small(sh, wk, gub, gu_fmt, pg.out ? &pg : nullptr, st)
+       : gu_fmt == LAT_MOE_GATEUP_Q4_0 ? launch_gateup_q40(sh, wk, gub, pg.out ? &pg : nullptr, st)
+                                       : launch_gateup(sh, wk, gub, pg.out ? &pg : nullptr, st)) != hipSuccess)
     return LAT_MOE_ELAUNCH;
   if (mark(2) != hipSuccess) return LAT_MOE_ELAUNCH;
   const int fmt = down_fmt == LAT_MOE_DOWN_Q4_0 ? kDownQ40 : kDownIq4Nl;

@@ -189,7 +189,7 @@ __device__ __forceinline__ uint4 buf_u128(rsrc_t r, int voff, int soff) {
 hipError_t launch_route(const int32_t* idx, const uint8_t* x, const Shapes& s, const Work& w, bool gather,
                         hipStream_t st);
 hipError_t launch_gateup(const Shapes& s, const Work& w, const uint8_t* gu, const ProbeRows* probe, hipStream_t st);
-// Gate/up weights in Q4_0 (18-byte blocks, a scale per 32 values), any batch size.
+// Gate/up weights in Q4_0 (18-byte blocks, a scale per 32 values), batches beyond small_path.
 hipError_t launch_gateup_q40(const Shapes& s, const Work& w, const uint8_t* gu, const ProbeRows* probe,
                              hipStream_t st);
 hipError_t launch_down(const uint8_t* dn, int fmt, const float* router_w, const Shapes& s, const Work& w,
@@ -198,7 +198,7 @@ hipError_t launch_down(const uint8_t* dn, int fmt, const float* router_w, const 
 // GEMV-shaped gate/up and down kernels.
 constexpr int kSmallMaxPairs = kGatherRows;
 bool small_path(const Shapes& s);
-hipError_t launch_gateup_small(const Shapes& s, const Work& w, const uint8_t* gu, const ProbeRows* probe,
+hipError_t launch_gateup_small(const Shapes& s, const Work& w, const uint8_t* gu, int fmt, const ProbeRows* probe,
                                hipStream_t st);
 hipError_t launch_down_small(const uint8_t* dn, int fmt, const float* router_w, const Shapes& s, const Work& w,
                              const ProbeRows* probe, hipStream_t st);

@@ -23,6 +23,12 @@
 // acc_sb += d_x * I32 per block and acc += d_w * acc_sb per super-block; down
 // folds acc += (d_dn * d_H) * J32 per block.  32 features are one q8_1 block
 // of H, so SwiGLU and the requant finish inside a half wave.
+//
+// Gate/up weights in Q4_0 take the same workgroups: a thread's K slice is 8
+// whole 18-byte blocks (144 contiguous bytes, 16-byte aligned), the nibbles
+// are split into low and high halves by masks, and the block dot is
+// I32 = sum nib * x - 8 * sum x (the same per-16 code sums), folded as
+// acc += d_w * fl(d_x * I32) per block.
 #include "lat_moe_internal.h"
 
 namespace latmoe {
@@ -35,7 +41,7 @@ constexpr int kSmallThreads = 256;
 // Gate/up: workgroup (tile j of the route table -> expert, 32 features f0).
 // Threads: row r = t >> 2 of 64 (32 gate rows f0.., 32 up rows F+f0..), K
 // slice q = t & 3 (super-blocks q, q + 4, ...).
-template <bool PROBE>
+template <bool PROBE, int GFMT>
 __global__ __launch_bounds__(kSmallThreads) void k_gateup_small(
     const int8_t* __restrict__ xg, const float* __restrict__ xgd, const uint8_t* __restrict__ gu,
     const int32_t* __restrict__ perm, const int32_t* __restrict__ tiles, const int32_t* __restrict__ misc, int L,
@@ -46,7 +52,8 @@ __global__ __launch_bounds__(kSmallThreads) void k_gateup_small(
   const int e = te.x, pos0 = te.y, cnt = te.z;  // cnt <= kGatherRows
   const int f0 = blockIdx.y * 32;
   const int tid = threadIdx.x, lane = tid & 63;
-  const int nsb = L / 256, nxb = L / 32, nsub = L / 16, row_bytes = nsb * kQ3kBytes;
+  constexpr bool kQ40 = GFMT == LAT_MOE_GATEUP_Q4_0;
+  const int nsb = L / 256, nxb = L / 32, nsub = L / 16, row_bytes = nsb * (kQ40 ? 8 * kQ40Bytes : kQ3kBytes);
   // LDS: xs[kSmallTok][L] | xds[kSmallTok][nxb] | xsum[kSmallTok][nsub] | gus[64][kSmallTok]
   int8_t* xs = reinterpret_cast<int8_t*>(smem);
   float* xds = reinterpret_cast<float*>(xs + kSmallTok * L);
@@ -64,8 +71,16 @@ __global__ __launch_bounds__(kSmallThreads) void k_gateup_small(
   // registers: bytes 0..107 as 16-byte pieces and a 12-byte tail (buffer loads
   // at 2-byte-aligned offsets return the bytes there), d as a 16-bit load.
   // Adjacent threads read adjacent blocks, a wave 16 whole rows.
-  uint32_t blk[28];
-  {
+  // Q4_0: the slice's 8 blocks (144 bytes) as nine 16-byte loads.
+  uint32_t blk[kQ40 ? 36 : 28];
+  if constexpr (kQ40) {
+    const int boff = q < nsb ? wrow * row_bytes + q * 8 * kQ40Bytes : kOutOfRange;
+#pragma unroll
+    for (int c = 0; c < 9; ++c) {
+      const uint4 v = buf_u128(rw, boff, 16 * c);
+      blk[4 * c] = v.x, blk[4 * c + 1] = v.y, blk[4 * c + 2] = v.z, blk[4 * c + 3] = v.w;
+    }
+  } else {
     const int boff = q < nsb ? wrow * row_bytes + q * kQ3kBytes : kOutOfRange;
 #pragma unroll
     for (int c = 0; c < 6; ++c) {
@@ -113,7 +128,56 @@ __global__ __launch_bounds__(kSmallThreads) void k_gateup_small(
     float acc[kSmallTok];
 #pragma unroll
     for (int tk = 0; tk < kSmallTok; ++tk) acc[tk] = 0.f;
-    if (q < nsb) {
+    if (kQ40 && q < nsb) {
+      const int sb = q;
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb) {
+        // block kb at byte 18 kb of the slice: d, then 16 nibble bytes
+        const int base = 18 * kb, wi = base >> 2;
+        uint32_t nw[4], d16;
+        if ((base & 3) == 0) {
+          d16 = blk[wi] & 0xffffu;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) nw[w] = __builtin_amdgcn_alignbyte(blk[wi + w + 1], blk[wi + w], 2);
+        } else {
+          d16 = blk[wi] >> 16;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) nw[w] = blk[wi + 1 + w];
+        }
+        const float dwb = half_bits_to_float(d16);
+        uint32_t lo[4], hi[4];  // values 0..15 (low nibbles) and 16..31 (high nibbles)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          lo[w] = nw[w] & 0x0f0f0f0fu;
+          hi[w] = (nw[w] >> 4) & 0x0f0f0f0fu;
+        }
+#pragma unroll
+        for (int tk = 0; tk < kSmallTok; ++tk) {
+          if (tk < nt) {
+            const uint4* xp = reinterpret_cast<const uint4*>(xs + tk * L + sb * 256 + 32 * kb);
+            const uint4 x0 = xp[0], x1 = xp[1];
+            int dn = __builtin_amdgcn_sdot4((int)lo[0], (int)x0.x, 0, false);
+            dn = __builtin_amdgcn_sdot4((int)lo[1], (int)x0.y, dn, false);
+            dn = __builtin_amdgcn_sdot4((int)lo[2], (int)x0.z, dn, false);
+            dn = __builtin_amdgcn_sdot4((int)lo[3], (int)x0.w, dn, false);
+            dn = __builtin_amdgcn_sdot4((int)hi[0], (int)x1.x, dn, false);
+            dn = __builtin_amdgcn_sdot4((int)hi[1], (int)x1.y, dn, false);
+            dn = __builtin_amdgcn_sdot4((int)hi[2], (int)x1.z, dn, false);
+            dn = __builtin_amdgcn_sdot4((int)hi[3], (int)x1.w, dn, false);
+            const int2 sx = *reinterpret_cast<const int2*>(&xsum[tk * nsub + sb * 16 + 2 * kb]);
+            const int I = dn - 8 * (sx.x + sx.y);  // sum (nib - 8) x
+            const float t = xds[tk * nxb + sb * 8 + kb] * (float)I;
+            acc[tk] = __builtin_fmaf(dwb, t, acc[tk]);
+            if (PROBE) {
+              const int rr = wrow - probe.row0;
+              if (rr >= 0 && rr < probe.rows)
+                probe.out[((int64_t)perm[pos0 + g0 + tk] * probe.rows + rr) * nxb + sb * 8 + kb] = I;
+            }
+          }
+        }
+      }
+    }
+    if (!kQ40 && q < nsb) {
       const int sb = q;
       const float dw = half_bits_to_float(blk[27] & 0xffffu);
       float asb[kSmallTok];
@@ -326,18 +390,18 @@ bool small_path(const Shapes& s) {
   return s.pairs() <= kSmallMaxPairs && s.L <= 1024 && s.F <= 2048;
 }
 
-hipError_t launch_gateup_small(const Shapes& s, const Work& w, const uint8_t* gu, const ProbeRows* probe,
+hipError_t launch_gateup_small(const Shapes& s, const Work& w, const uint8_t* gu, int fmt, const ProbeRows* probe,
                                hipStream_t st) {
   const int nxb = s.L / 32;
   const size_t lds = kSmallTok * s.L + 4 * kSmallTok * nxb + 4 * kSmallTok * (s.L / 16) + 4 * 64 * kSmallTok;
   const dim3 grid((unsigned)(s.pairs() < s.E ? s.pairs() : s.E), s.F / 32);
   const ProbeRows none = {nullptr, 0, 0};
-  if (probe)
-    hipLaunchKernelGGL(k_gateup_small<true>, grid, dim3(kSmallThreads), lds, st, w.xg, w.xgd, gu, w.perm, w.tiles,
-                       w.misc, s.L, s.F, w.h_codes, w.h_ds, *probe);
-  else
-    hipLaunchKernelGGL(k_gateup_small<false>, grid, dim3(kSmallThreads), lds, st, w.xg, w.xgd, gu, w.perm, w.tiles,
-                       w.misc, s.L, s.F, w.h_codes, w.h_ds, none);
+  const ProbeRows pr = probe ? *probe : none;
+  const bool q40 = fmt == LAT_MOE_GATEUP_Q4_0;
+  auto kern = probe ? (q40 ? k_gateup_small<true, LAT_MOE_GATEUP_Q4_0> : k_gateup_small<true, LAT_MOE_GATEUP_Q3_K>)
+                    : (q40 ? k_gateup_small<false, LAT_MOE_GATEUP_Q4_0> : k_gateup_small<false, LAT_MOE_GATEUP_Q3_K>);
+  hipLaunchKernelGGL(kern, grid, dim3(kSmallThreads), lds, st, w.xg, w.xgd, gu, w.perm, w.tiles, w.misc, s.L, s.F,
+                     w.h_codes, w.h_ds, pr);
   return hipGetLastError();
 }
 
