@@ -1,7 +1,9 @@
 """GPU parity of the expert stage with Q4_0 down weights (lat_moe_expert_forward_ex)
 against the CPU oracle, through the C ABI, on every down kernel: the
 GEMV-shaped one (at most 64 pairs), the persistent one (F % 256 == 0) and the
-per-tile one (other F).
+per-tile one (other F); and with Q4_0 gate/up weights on both gate/up kernels
+that take them (the GEMV-shaped one for at most 64 pairs, k_gateup_q40
+otherwise).
 
 Criteria as for IQ4_NL (tests/_gpu.py): routing exact, gate/up and down block
 dots bit-exact, H codes >= 99.99 % equal and within +-1 with d_H within one
@@ -215,3 +217,37 @@ def test_q4_0_gateup_full_size_sampled():
     rng = np.random.default_rng(19)
     toks = np.array(sorted(set(rng.choice(wl.T, 10, replace=False).tolist()) | {0, wl.T - 1}), np.int64)
     _check_gu(I, xq, gu, out, "q4_0", (wl.F - 4, 8), (0, 8), toks=toks)
+
+
+@pytest.mark.parametrize("T", [9, 100], ids=["small_kernel", "persistent_kernel"])
+def test_q4_0_gateup_invalid_and_duplicate_ids(T):
+    """Q4_0 gate/up with dropped and repeated ids (27 pairs take the GEMV-shaped
+    kernel, 300 the persistent one): only valid pairs count; every id invalid
+    gives y = 0."""
+    from quantized_latent_moe_amd.inputs import make_gateup_q4_0
+    wl = Workload(f"gu40_edge_{T}", T=T, L=256, F=96, E=5, k=3, zipf_s=1.1, seed=18)
+    say(f"Q4_0 gate/up edge case {wl}")
+    I = make_inputs(wl)
+    xq = oracle.quantize_q8_1(I.x)
+    gu = make_gateup_q4_0(wl)
+    idx = I.router_idx.copy()
+    idx[0, :] = [-1, 5, 1 << 20]
+    idx[1, :] = [2, 2, 2]
+    idx[4, 2] = -3
+    I.router_idx[...] = idx
+    rows = ((0, 2 * wl.F), (0, wl.L))
+    out = _run_gu(I, xq, gu, lm.DOWN_Q4_0, *rows)
+    assert (out["y"][0] == 0).all()
+    _check_gu(I, xq, gu, out, "q4_0", *rows)
+    I.router_idx[...] = 7
+    out = _run_gu(I, xq, gu, lm.DOWN_Q4_0, *rows)
+    assert (out["y"] == 0).all() and (out["y_plain"] == 0).all()
+
+
+def test_q4_0_empty_batch_is_noop():
+    s = lm.shapes(0, 1024, 2048, 128, 8)
+    dummy = torch.empty(16, dtype=torch.uint8, device="cuda")
+    y = torch.full((1, 1024), 3.0, device="cuda")
+    lm.expert_forward_ex(dummy, dummy, dummy, dummy, dummy, lm.DOWN_Q4_0, s, y, dummy, gateup_format=lm.GATEUP_Q4_0)
+    torch.cuda.synchronize()
+    assert (y == 3.0).all()
