@@ -251,3 +251,49 @@ def test_q4_0_empty_batch_is_noop():
     lm.expert_forward_ex(dummy, dummy, dummy, dummy, dummy, lm.DOWN_Q4_0, s, y, dummy, gateup_format=lm.GATEUP_Q4_0)
     torch.cuda.synchronize()
     assert (y == 3.0).all()
+
+
+@pytest.mark.parametrize("name", ["decode", "gu40_graph"])
+def test_q4_0_stage_graph_replays_exactly(name):
+    """The stage with Q4_0 gate/up and down weights captured in a graph (the
+    GEMV-shaped kernels at decode; the large route path and the persistent
+    Q4_0 kernels at 1200 pairs): every replay, with eager work between
+    replays, gives the eager call's y bit for bit."""
+    from quantized_latent_moe_amd.inputs import make_gateup_q4_0
+    wl = WORKLOADS["decode"] if name == "decode" else Workload("gu40_graph", T=300, L=1024, F=512, E=8, k=4,
+                                                               zipf_s=1.1, seed=45)
+    say(f"Q4_0 graph case {wl}")
+    I = make_inputs(wl)
+    xq = oracle.quantize_q8_1(I.x)
+    dev = torch.device("cuda", 0)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    x, idx, w = t(xq), t(I.router_idx.astype(np.int32)), t(I.router_w.astype(np.float32))
+    g, dn = t(make_gateup_q4_0(wl)), t(I.down_iq4nl)
+    s = lm.shapes(wl.T, wl.L, wl.F, wl.E, wl.k)
+    ws = torch.empty(lm.workspace_size(s), dtype=torch.uint8, device=dev)
+    y = torch.empty((wl.T, wl.L), dtype=torch.float32, device=dev)
+
+    def step():
+        lm.expert_forward_ex(x, idx, w, g, dn, lm.DOWN_Q4_0, s, y, ws, gateup_format=lm.GATEUP_Q4_0)
+
+    step()
+    torch.cuda.synchronize()
+    y_eager = y.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    scratch = torch.randn(1 << 20, device=dev)
+    for r in range(4):
+        y.fill_(float("nan"))
+        ws.fill_(0x5A)                  # the workspace needs no initialisation
+        graph.replay()
+        scratch.mul_(1.0001)            # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_eager), f"replay {r}"
+    say(f"{wl.name}: 4 graph replays of the Q4_0 stage equal the eager call")
