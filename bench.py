@@ -427,11 +427,14 @@ KERNEL_SOURCES = {"k_gateup": "gateup.hip", "k_down": "down.hip", "k_gateup_q40"
 
 
 def kernel_source_hash(kernel):
-    """sha256 over the kernel's source file and the shared internal header."""
+    """sha256 over the kernel's source file, the shared internal header and the
+    flags the source is compiled with."""
     import hashlib
+    from quantized_latent_moe_amd import build as hipbuild
     h = hashlib.sha256()
     for f in (KERNEL_SOURCES[kernel], "lat_moe_internal.h"):
         h.update(open(os.path.join(ROOT, "quantized_latent_moe_amd", "csrc", f), "rb").read())
+    h.update(" ".join(hipbuild.compile_flags(KERNEL_SOURCES[kernel])).encode())
     return h.hexdigest()
 
 

@@ -3,8 +3,11 @@ from __future__ import annotations
 
 import glob
 import os
+import shutil
 import subprocess
 import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
@@ -21,17 +24,45 @@ FLAGS = [
 ]
 
 
+# Extra flags of single sources.  gateup.hip: LLVM's max-ILP machine scheduler
+# interleaves the Q3_K gate/up kernel's fold with its MFMAs better (gate/up
+# about 1.5% faster at 5268 and 21000 tokens); the other kernels gain nothing
+# from it (down is slightly slower).
+SOURCE_FLAGS = {"gateup.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
+
+
 def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
+def compile_flags(source: str) -> list:
+    """The flags one source's object is compiled with."""
+    return [f for f in FLAGS if f != "-shared"] + SOURCE_FLAGS.get(os.path.basename(source), [])
+
+
 def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(HERE, "..", "include"), "-o", tmp, *sources()]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.check_call(cmd)
-    os.replace(tmp, LIB)
+    """Compile every source to an object with its flags, in parallel, then
+    link the shared library."""
+    tmpdir = tempfile.mkdtemp(prefix="latmoe_build_")
+    try:
+        def compile_one(src):
+            obj = os.path.join(tmpdir, os.path.basename(src) + ".o")
+            cmd = [HIPCC, *compile_flags(src), "-I", os.path.join(HERE, "..", "include"), "-c", "-o", obj, src]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            subprocess.check_call(cmd)
+            return obj
+
+        with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
+            objs = list(ex.map(compile_one, sources()))
+        tmp = LIB + ".tmp%d" % os.getpid()
+        cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.check_call(cmd)
+        os.replace(tmp, LIB)
+    finally:
+        shutil.rmtree(tmpdir, ignore_errors=True)
     return LIB
 
 
