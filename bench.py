@@ -87,12 +87,34 @@ class Stage:
         self.y = torch.empty((wl.T, wl.L), dtype=torch.float32, device=dev)
         torch.cuda.synchronize()
 
-    def step(self):
+    def step(self, deterministic=True):
         if self.ex:
-            self.lm.expert_forward_ex(self.x, self.idx, self.w, self.gu, self.dn, self.down_format, self.s, self.y,
-                                      self.ws, gateup_format=self.gateup_format)
-        else:
+            self.lm.expert_forward_fmt(self.x, self.idx, self.w, self.gu, self.dn, self.down_format, self.s, self.y,
+                                       self.ws, gateup_format=self.gateup_format, deterministic=deterministic)
+        elif deterministic:
             self.lm.expert_forward(self.x, self.idx, self.w, self.gu, self.dn, self.s, self.y, self.ws)
+        else:
+            self.lm.expert_forward_ex(self.x, self.idx, self.w, self.gu, self.dn, self.s, self.y, self.ws,
+                                      deterministic=False)
+
+    def routing_draws(self, n):
+        """Device copies of the workload's routing (draw 0) and n - 1 more
+        draws of activations and routing with the same weights: a list of
+        (x q8_1, router_idx, router_w, algorithmic counts)."""
+        import numpy as np
+        torch, lm = self.torch, self.lm
+        from quantized_latent_moe_amd.inputs import make_routing_draws
+        out = [(self.x, self.idx, self.w, algorithmic(self.wl, self.inputs.router_idx))]
+        for x, idx, w in make_routing_draws(self.wl, n - 1):
+            xq = torch.empty_like(self.x)
+            lm.quantize_q8_1(torch.from_numpy(x).cuda(), xq)
+            out.append((xq, torch.from_numpy(np.ascontiguousarray(idx)).cuda(),
+                        torch.from_numpy(np.ascontiguousarray(w)).cuda(), algorithmic(self.wl, idx)))
+        torch.cuda.synchronize()
+        return out
+
+    def use(self, draw):
+        self.x, self.idx, self.w = draw[0], draw[1], draw[2]
 
     def prime(self, seconds=0.1):
         """Part of setup, before the counted warm-up: run the stage for about
@@ -105,24 +127,25 @@ class Stage:
                 self.step()
             torch.cuda.synchronize()
 
-    def step_timed(self, events):
+    def step_timed(self, events, deterministic=True):
         if self.ex:
-            self.lm.expert_forward_ex(self.x, self.idx, self.w, self.gu, self.dn, self.down_format, self.s, self.y,
-                                      self.ws, gateup_format=self.gateup_format, debug=True, stage_events=events)
+            self.lm.expert_forward_fmt(self.x, self.idx, self.w, self.gu, self.dn, self.down_format, self.s, self.y,
+                                       self.ws, gateup_format=self.gateup_format, debug=True, stage_events=events,
+                                       deterministic=deterministic)
         else:
-            self.lm.expert_forward_debug(self.x, self.idx, self.w, self.gu, self.dn, self.s, self.y, self.ws,
-                                         stage_events=events)
+            self.lm.expert_forward_ex(self.x, self.idx, self.w, self.gu, self.dn, self.s, self.y, self.ws,
+                                      stage_events=events, deterministic=deterministic)
 
-    def time_steps(self, steps, warmup):
+    def time_steps(self, steps, warmup, deterministic=True):
         torch = self.torch
         for _ in range(warmup):
-            self.step()
+            self.step(deterministic)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
         e0.record()
         for _ in range(steps):
-            self.step()
+            self.step(deterministic)
         e1.record()
         torch.cuda.synchronize()
         wall = (time.perf_counter() - t0) * 1e3 / steps
@@ -178,7 +201,7 @@ class Stage:
         torch.cuda.synchronize()
         return router_us, e0.elapsed_time(e1) * 1e3 / steps
 
-    def stage_times(self, steps):
+    def stage_times(self, steps, deterministic=True):
         """Mean ms of route / gate-up / down / combine over `steps` calls."""
         torch = self.torch
         evs = []
@@ -189,7 +212,7 @@ class Stage:
             evs.append(ev)
         torch.cuda.synchronize()
         for ev in evs:
-            self.step_timed(ev)
+            self.step_timed(ev, deterministic)
         torch.cuda.synchronize()
         acc = [0.0] * 4
         for ev in evs:
@@ -311,6 +334,66 @@ class DenseStage:
 COLD_REPS = {"tiny": 50, "decode": 50, "mid_prefill": 50, "prefill_5k": 20, "prefill_21k": 10}
 
 
+def decode_cold(st, reps, draws=4):
+    """One call at a time with the L2s and the 256 MB last-level cache evicted
+    before each (a 1 GiB buffer written), rotating among `draws` routings of
+    the workload (the same weights), so no call finds its experts in cache:
+    median, p10 and p90 µs, and the algorithmic bytes of each call (its
+    active experts' weights, x, routing, y) over its time."""
+    import numpy as np
+    torch = st.torch
+    ds = st.routing_draws(draws)
+    evict = torch.empty((1 << 30) // 4, dtype=torch.float32, device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    times, gbs = [], []
+    for i in range(reps):
+        d = ds[i % len(ds)]
+        st.use(d)
+        evict.fill_(1.0)
+        e0.record()
+        st.step()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3
+        times.append(us)
+        gbs.append(d[3]["bytes"] / (us * 1e-6) / 1e9)
+    st.use(ds[0])
+    del evict
+    torch.cuda.empty_cache()
+    med = float(np.median(times))
+    return {"median_us": round(med, 2), "p10_us": round(float(np.percentile(times, 10)), 2),
+            "p90_us": round(float(np.percentile(times, 90)), 2), "calls": reps, "routing_draws": len(ds),
+            "active_experts": [d[3]["active"] for d in ds], "alg_bytes": [d[3]["bytes"] for d in ds],
+            "hbm_gbs_median": round(float(np.median(gbs)), 1),
+            "hbm_frac_median": round(float(np.median(gbs)) / PEAK_HBM_GBS, 4)}
+
+
+def combine_report(names, steps, warmup):
+    """The two combines at the large workloads: the slot buffer with the
+    ordered combine kernel (deterministic, the default) and the fp32 atomic
+    adds of the down kernel into y (deterministic = 0): ms per step back to
+    back, and the route / gate-up / down / combine times by events."""
+    import torch
+    from quantized_latent_moe_amd.inputs import WORKLOADS
+    stage = ["route", "gateup", "down", "combine"]
+    rep = {}
+    for name in names:
+        st = Stage(WORKLOADS[name])
+        st.prime()
+        r = {}
+        for label, det in (("slots", True), ("atomic", False)):
+            ms, _ = st.time_steps(steps, warmup, deterministic=det)
+            times = st.stage_times(steps, deterministic=det)
+            r[label] = {"ms_per_step": round(ms, 5), "stage_ms": {k: round(v, 5) for k, v in zip(stage, times)}}
+            print(f"[bench] {name} combine {label}: {ms * 1e3:.1f} us/step, route {times[0] * 1e3:.1f}, down "
+                  f"{times[2] * 1e3:.1f}, combine {times[3] * 1e3:.1f} us", file=sys.stderr, flush=True)
+        r["atomic_over_slots"] = round(r["atomic"]["ms_per_step"] / r["slots"]["ms_per_step"], 4)
+        rep[name] = r
+        del st
+        torch.cuda.empty_cache()
+    return rep
+
+
 def device_info():
     """CU count from the device properties, and a measured plain streaming
     copy (1 GiB read and 1 GiB written per call, bytes of both counted) next
@@ -401,8 +484,23 @@ def cpu_baseline_dense(dwl, target_s):
             "sample": f"first {n} of {dwl.T} tokens of {dwl.name}, D and U, {dt:.1f} s"}
 
 
-def cpu_baseline(wl, target_s):
-    """The oracle, as it stands, on the first n tokens of the same workload."""
+def host_cpu():
+    """CPU model and the host threads this process may use."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"cpu_model": model, "nproc": len(os.sched_getaffinity(0)), "cpu_count": os.cpu_count()}
+
+
+def cpu_baseline(wl, target_s, runs=3):
+    """The oracle, as it stands, on the first n tokens of the same workload:
+    the median of `runs` timed runs, n chosen for about target_s / runs
+    seconds each."""
     import numpy as np
     import oracle
     from quantized_latent_moe_amd.inputs import make_inputs
@@ -415,12 +513,17 @@ def cpu_baseline(wl, target_s):
     t0 = time.perf_counter()
     run(n0)
     per_tok = (time.perf_counter() - t0) / n0
-    n = int(min(wl.T, max(n0, target_s / max(per_tok, 1e-9))))
-    t0 = time.perf_counter()
-    run(n)
-    dt = time.perf_counter() - t0
-    return {"value": round(n / dt, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"first {n} of {wl.T} tokens of {wl.name} ({n * wl.k} routed pairs), {dt:.1f} s"}
+    n = int(min(wl.T, max(n0, target_s / runs / max(per_tok, 1e-9))))
+    rates = []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        run(n)
+        rates.append(n / (time.perf_counter() - t0))
+    med = float(np.median(rates))
+    return {"value": round(med, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {n} of {wl.T} tokens of {wl.name} ({n * wl.k} routed pairs), median of {runs} runs "
+                      f"({', '.join(f'{r:.1f}' for r in rates)} tokens/s), {n * runs / med:.1f} s in all",
+            "runs_tokens_per_s": [round(r, 3) for r in rates], **host_cpu()}
 
 
 KERNEL_SOURCES = {"k_gateup": "gateup.hip", "k_down": "down.hip", "k_gateup_q40": "gateup_q40.hip"}
@@ -548,9 +651,11 @@ def main():
     ap.add_argument("--no-per-config", action="store_true",
                     help="skip the cold-cache timing of every workload (per_config)")
     ap.add_argument("--no-formats", action="store_true", help="skip the Q4_0 weight timings")
+    ap.add_argument("--no-combine", action="store_true",
+                    help="skip the slot-buffer vs atomic-add combine comparison at prefill_5k and prefill_21k")
     ap.add_argument("--formats-only", action="store_true",
                     help="time only the stage with Q4_0 gate/up and down weights, at --workload")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=18.0, help="CPU oracle time over its 3 runs")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="first run a plain device copy of MIB MiB (three times), the reference for counter scaling")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -609,15 +714,15 @@ def main():
     achieved = ops[dom] / (dom_ms * 1e-3) / 1e12
     kernel = {"gateup": "k_gateup", "down": "k_down"}[dom]
     fold_tops = folds[dom] / (dom_ms * 1e-3) / 1e12
-    # The dominant kernel is bound by the per-block fp32 scale fold on the VALU
-    # (2 unpacked VALU lane-ops per 32-value block result: about 4x the MFMA
-    # time of the block), so the roofline is that ALU one; the int8 MFMA
-    # figures are given beside it.
-    roofline = {"bound": "alu", "kernel": kernel, "achieved": round(fold_tops, 2), "peak": round(PEAK_VALU_TOPS, 1),
-                "unit": "T lane-op/s", "frac": round(fold_tops / PEAK_VALU_TOPS, 4),
+    # The dominant kernel against the int8 MFMA peak (the metric's roof).  Its
+    # binding limit is the per-block fp32 scale fold on the VALU (2 unpacked
+    # VALU lane-ops per 32-value block result, about 4x the block's MFMA
+    # time), given beside it as fold_valu.
+    roofline = {"bound": "mfma", "kernel": kernel, "achieved": round(achieved, 2), "peak": PEAK_INT8_TOPS,
+                "unit": "TOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 4),
                 "traffic": read_traffic(kernel, wl.name), "launch_ms": round(dom_ms, 5),
-                "mfma": {"achieved": round(achieved, 2), "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
-                         "frac": round(achieved / PEAK_INT8_TOPS, 4)}}
+                "fold_valu": {"bound": "alu", "achieved": round(fold_tops, 2), "peak": round(PEAK_VALU_TOPS, 1),
+                              "unit": "T lane-op/s", "frac": round(fold_tops / PEAK_VALU_TOPS, 4)}}
     total_ops = alg["ops_gateup"] + alg["ops_down"]
     out = {
         "metric": METRIC,
@@ -651,17 +756,26 @@ def main():
         dms, _ = ds.time_steps(max(args.steps, 50), args.warmup)
         dstage = ds.stage_times(max(args.steps, 50))
         gbs = dalg["bytes"] / (dms * 1e-3) / 1e9
+        cold = decode_cold(ds, 100)
         r_us, g_us = ds.router_and_graph(max(args.steps, 50))
-        out["decode"] = {"workload": dwl.name, "us_per_step": round(dms * 1e3, 2),
-                         "alg_bytes": dalg["bytes"], "hbm_gbs": round(gbs, 1),
-                         "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
-                         "stage_us": {n: round(v * 1e3, 2) for n, v in zip(names, dstage)},
+        # headline: caches evicted before every call, four routings in turn;
+        # back to back (same routing, weights may stay in the last-level
+        # cache between calls) beside it
+        out["decode"] = {"workload": dwl.name, "us_per_step": cold["median_us"],
+                         "hbm_gbs": cold["hbm_gbs_median"], "hbm_frac": cold["hbm_frac_median"],
+                         "cold": cold,
+                         "warm": {"us_per_step": round(dms * 1e3, 2), "alg_bytes": dalg["bytes"],
+                                  "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+                                  "stage_us": {n: round(v * 1e3, 2) for n, v in zip(names, dstage)}},
                          "router_us": round(r_us, 2),
                          "router_and_stage_graph_us_per_step": round(g_us, 2)}
         print(f"[bench] decode router {r_us:.2f} us, router + stage from one graph {g_us:.2f} us/step",
               file=sys.stderr, flush=True)
-        print(f"[bench] decode {dms * 1e3:.2f} us/step, {gbs:.0f} GB/s", file=sys.stderr, flush=True)
+        print(f"[bench] decode cold {cold['median_us']:.2f} us/step ({cold['hbm_gbs_median']:.0f} GB/s), "
+              f"back to back {dms * 1e3:.2f} us/step ({gbs:.0f} GB/s)", file=sys.stderr, flush=True)
         del ds
+    if not args.no_combine:
+        out["combine"] = combine_report(["prefill_5k", "prefill_21k"], args.steps, args.warmup)
     if not args.no_formats:
         out["down_q4_0"] = q4_0_report(args.steps, args.warmup, gateup_q4_0=False)
         out["gateup_down_q4_0"] = q4_0_report(args.steps, args.warmup, gateup_q4_0=True)

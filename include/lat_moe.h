@@ -84,7 +84,9 @@ int lat_moe_expert_forward(const void* x_q8_1, const int32_t* router_idx, const 
                            const void* gateup_q3k, const void* down_iq4nl, const lat_moe_shapes* shapes,
                            float* y, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Optional device outputs of the debug entry point.  Any pointer may be NULL. */
+/* Options and optional device outputs of lat_moe_expert_forward_ex.  Any
+ * pointer may be NULL.  A zero-filled struct asks for no debug output and
+ * for the combine by atomic adds (deterministic = 0). */
 typedef struct lat_moe_debug {
   void* h_q8_1;         /* [T*k][F/32] q8_1: H of every pair p = t*k + j, ggml layout;
                            pairs with an invalid expert id get all-zero blocks */
@@ -108,16 +110,32 @@ typedef struct lat_moe_debug {
    * and after the combine, so elapsed times between consecutive events are the
    * stage durations.  NULL to skip.  Recording adds no kernel. */
   void* const* stage_events;
+  /* How the k expert outputs of a token are summed into y (the weighted
+   * combine; the pages do not say):
+   *   nonzero  each pair's weighted row goes to a slot of the workspace and a
+   *            combine kernel adds a token's slots in slot order j = 0..k-1:
+   *            the same inputs give bitwise identical y (what
+   *            lat_moe_expert_forward does);
+   *   0        the down kernel adds each weighted row into y with fp32 atomic
+   *            adds (y is zeroed by the route pass): no slot buffer and no
+   *            combine kernel, but the order of the k additions, and so the
+   *            rounding of y, may change from call to call.
+   * Batches of at most 64 pairs (L <= 1024, F <= 2048) sum a token's experts
+   * in slot order inside the down kernel either way, so their y is always
+   * deterministic. */
+  int32_t deterministic;
 } lat_moe_debug;
 
-/* Same computation as lat_moe_expert_forward (same kernels, same y), plus the
- * requested debug outputs.  Row ranges must lie inside [0, 2F) and [0, L). */
-int lat_moe_expert_forward_debug(const void* x_q8_1, const int32_t* router_idx, const float* router_w,
-                                 const void* gateup_q3k, const void* down_iq4nl, const lat_moe_shapes* shapes,
-                                 float* y, void* workspace, size_t workspace_bytes, void* stream,
-                                 const lat_moe_debug* dbg);
+/* The expert stage with options and debug outputs: the arguments and rules of
+ * lat_moe_expert_forward, plus dbg (host memory, may be NULL: then the call is
+ * lat_moe_expert_forward).  Debug row ranges must lie inside [0, 2F) and
+ * [0, L); stage_events, when given, must hold five non-NULL events. */
+int lat_moe_expert_forward_ex(const void* x_q8_1, const int32_t* router_idx, const float* router_w,
+                              const void* gateup_q3k, const void* down_iq4nl, const lat_moe_shapes* shapes,
+                              float* y, void* workspace, size_t workspace_bytes, void* stream,
+                              const lat_moe_debug* dbg);
 
-/* Formats of the down weights for lat_moe_expert_forward_ex.  Both are
+/* Formats of the down weights for lat_moe_expert_forward_fmt.  Both are
  * 18-byte blocks of 32 weights, fp16 d then 16 bytes of 4-bit indices
  * (element i < 16 in the low nibble of byte i, element i >= 16 in the high
  * nibble of byte i - 16); a weight is d * K(index) with
@@ -129,7 +147,7 @@ int lat_moe_expert_forward_debug(const void* x_q8_1, const int32_t* router_idx, 
 #define LAT_MOE_DOWN_IQ4_NL 0
 #define LAT_MOE_DOWN_Q4_0 1
 
-/* Formats of the gate/up weights for lat_moe_expert_forward_ex:
+/* Formats of the gate/up weights for lat_moe_expert_forward_fmt:
  *   LAT_MOE_GATEUP_Q3_K  [E][2F][L/256] Q3_K super-blocks (110 B), as above;
  *   LAT_MOE_GATEUP_Q4_0  [E][2F][L/32] Q4_0 blocks (18 B, the layout above,
  *                        weight = d * (nibble - 8)), one scale per 32 values:
@@ -142,15 +160,14 @@ int lat_moe_expert_forward_debug(const void* x_q8_1, const int32_t* router_idx, 
 /* The expert stage with a choice of weight formats: gateup is [E][2F][...]
  * blocks of gateup_format and down [E][L][F/32] blocks of down_format (any
  * other value returns LAT_MOE_EINVAL).  Every other argument, rule and result
- * is that of lat_moe_expert_forward (with Q4_0 gate/up weights one expert's
- * 2F * L/32 * 18 bytes must stay below 2^31); dbg may be NULL (then nothing
- * more is written) or as for lat_moe_expert_forward_debug, whose probes then
+ * is that of lat_moe_expert_forward_ex (with Q4_0 gate/up weights one expert's
+ * 2F * L/32 * 18 bytes must stay below 2^31); dbg may be NULL, and its probes
  * hold the formats' integer dots.  With LAT_MOE_GATEUP_Q3_K and
- * LAT_MOE_DOWN_IQ4_NL the call is lat_moe_expert_forward(_debug). */
-int lat_moe_expert_forward_ex(const void* x_q8_1, const int32_t* router_idx, const float* router_w,
-                              const void* gateup, int32_t gateup_format, const void* down, int32_t down_format,
-                              const lat_moe_shapes* shapes, float* y, void* workspace, size_t workspace_bytes,
-                              void* stream, const lat_moe_debug* dbg);
+ * LAT_MOE_DOWN_IQ4_NL the call is lat_moe_expert_forward_ex. */
+int lat_moe_expert_forward_fmt(const void* x_q8_1, const int32_t* router_idx, const float* router_w,
+                               const void* gateup, int32_t gateup_format, const void* down, int32_t down_format,
+                               const lat_moe_shapes* shapes, float* y, void* workspace, size_t workspace_bytes,
+                               void* stream, const lat_moe_debug* dbg);
 
 /* Round fp32 rows to q8_1 with the rule above: x [rows][cols] -> out
  * [rows][cols/32] q8_1 blocks (cols % 32 == 0, rows >= 0).  This is the rounding

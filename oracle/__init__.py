@@ -57,6 +57,7 @@ def lib() -> ctypes.CDLL:
         c.orc_probe_gateup_fmt.argtypes = [P, P, P, i32, i64, i32, i32, i32, i32, i64, P, P, P, P]
         c.orc_forward_fmt.restype = i64
         c.orc_down_combine.argtypes = [P, P, P, P, i64, i32, i32, i32, i32, P, i64, P]
+        c.orc_h_blocks_fmt.argtypes = [P, P, P, i32, i64, i32, i32, i32, i32, i64, P, P, P]
         c.orc_down_combine_fmt.argtypes = [P, P, P, P, i32, i64, i32, i32, i32, i32, P, i64, P]
         c.orc_probe_down_fmt.argtypes = [P, P, P, i32, i64, i32, i32, i32, i32, i64, P, P, P]
         c.orc_probe_gateup.argtypes = [P, P, P, i64, i32, i32, i32, i32, i64, P, P, P, P]
@@ -207,6 +208,21 @@ def down_combine(h_q8: np.ndarray, router_idx: np.ndarray, router_w: np.ndarray,
     lib().orc_down_combine_fmt(_p(h), _p(idx), _p(w), _p(_c(down, np.uint8)), DOWN_FORMATS[down_format], T, L, F, E,
                                k, _p(tok), n_tok, _p(y))
     return y
+
+
+def h_blocks(x_q8, router_idx, gateup, L, F, E, pairs, fblocks, gateup_format="q3_k"):
+    """H q8_1 blocks of chosen (pair, 32-feature block) entries -> uint8 [n, 36]:
+    the forward's G/U rows of those features, SwiGLU and the q8_1 rounding."""
+    idx = _c(router_idx, np.int32)
+    T, k = idx.shape
+    pairs = _c(pairs, np.int64)
+    fb = _c(fblocks, np.int32)
+    assert pairs.size == fb.size and (fb.size == 0 or (fb.min() >= 0 and fb.max() < F // 32))
+    assert pairs.size == 0 or (pairs.min() >= 0 and pairs.max() < T * k)
+    out = np.zeros((pairs.size, 36), np.uint8)
+    lib().orc_h_blocks_fmt(_p(_c(x_q8, np.uint8)), _p(idx), _p(_c(gateup, np.uint8)), GATEUP_FORMATS[gateup_format],
+                           T, L, F, E, k, pairs.size, _p(pairs), _p(fb), _p(out))
+    return out
 
 
 def probe_gateup(x_q8, router_idx, gateup, L, F, E, pairs, rows, want_i16=False, gateup_format="q3_k"):

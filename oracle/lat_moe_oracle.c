@@ -20,8 +20,8 @@
  * Source: "Run Edge0-145B Q3_K on AMD HIP (Linux, gfx1100) #1", section
  * "Contents" (gate/up reads Q3_K, applies SwiGLU and rounds H to q8_1; down
  * reads IQ4_NL) and the lat_q3k_w11.cu commit message (the same pipeline,
- * "each expert read where it is", and the sub-block scale folded into the
- * integer operand as (4 - code) * (scale - 32), range [-128, 124], so one
+ * each expert's weights read in place, and the sub-block scale folded into
+ * the integer operand as (4 - code) * (scale - 32), range [-128, 124], so one
  * integer dot covers a whole 32-value activation block).  Grouping tokens by
  * expert is a scheduling choice that does not change the result, so the
  * oracle simply walks the pairs token by token.
@@ -340,22 +340,32 @@ static void down_row_dots(int fmt, const uint8_t* row, const uint8_t* h, int F, 
 /* The expert stage, one pair at a time                                      */
 /* ------------------------------------------------------------------------ */
 
-/* Gate/up of one pair: G[F], U[F] in fp64.
- *   G/U[r] = sum over blocks b (ascending) of dw[r][b/8] * dx[b] * I32[r][b]. */
-static void pair_gateup(int fmt, const uint8_t* xrow, const uint8_t* gu_e, int L, int F, double* G, double* U) {
+/* One gate/up row r of expert weights gu_e against the token's q8_1 row, in
+ * fp64: sum over blocks b (ascending) of dw[r][b/8] (Q3_K; dw[r][b] for Q4_0)
+ * * dx[b] * I32[r][b].  I32, dw and dx are caller scratch of L/32 entries;
+ * dx holds the activation block scales. */
+static double gateup_row(int fmt, const uint8_t* xrow, const uint8_t* gu_e, int L, int r, int32_t* I32, double* dw,
+                         const double* dx) {
   int nb = L / Q81_VALUES;
   int64_t row_bytes = gu_row_bytes(fmt, L);
+  if (fmt == GU_Q4_0)
+    gateup_row_dots_q4_0(gu_e + r * row_bytes, xrow, L, I32, NULL, dw);
+  else
+    gateup_row_dots(gu_e + r * row_bytes, xrow, L, I32, NULL, dw);
+  double acc = 0.0;
+  for (int b = 0; b < nb; ++b) acc += dw[fmt == GU_Q4_0 ? b : b / 8] * dx[b] * (double)I32[b];
+  return acc;
+}
+
+/* Gate/up of one pair: G[F], U[F] in fp64 (rows 0..F-1 gate, F..2F-1 up). */
+static void pair_gateup(int fmt, const uint8_t* xrow, const uint8_t* gu_e, int L, int F, double* G, double* U) {
+  int nb = L / Q81_VALUES;
   int32_t* I32 = (int32_t*)malloc(sizeof(int32_t) * nb);
   double* dw = (double*)malloc(sizeof(double) * nb);  /* per super-block (Q3_K) or per block (Q4_0) */
   double* dx = (double*)malloc(sizeof(double) * nb);
   for (int b = 0; b < nb; ++b) dx[b] = orc_half_to_double(rd16(xrow + (int64_t)b * Q81_BYTES));
   for (int r = 0; r < 2 * F; ++r) {
-    if (fmt == GU_Q4_0)
-      gateup_row_dots_q4_0(gu_e + r * row_bytes, xrow, L, I32, NULL, dw);
-    else
-      gateup_row_dots(gu_e + r * row_bytes, xrow, L, I32, NULL, dw);
-    double acc = 0.0;
-    for (int b = 0; b < nb; ++b) acc += dw[fmt == GU_Q4_0 ? b : b / 8] * dx[b] * (double)I32[b];
+    double acc = gateup_row(fmt, xrow, gu_e, L, r, I32, dw, dx);
     if (r < F) G[r] = acc;
     else U[r - F] = acc;
   }
@@ -490,6 +500,45 @@ void orc_down_combine_fmt(const uint8_t* h_q8, const int32_t* idx, const float* 
 void orc_down_combine(const uint8_t* h_q8, const int32_t* idx, const float* w, const uint8_t* down, int64_t T,
                       int L, int F, int E, int k, const int64_t* tokens, int64_t n_tok, double* y) {
   orc_down_combine_fmt(h_q8, idx, w, down, DOWN_IQ4NL, T, L, F, E, k, tokens, n_tok, y);
+}
+
+/* H of chosen 32-feature blocks, for checking H at sizes where the whole
+ * stage is too slow: for i < n, the q8_1 block fb[i] of pair p = pair[i]'s H
+ * (36 bytes at out + 36 i), that is G and U of features 32 fb .. 32 fb + 31
+ * (gate/up rows f and F + f), SwiGLU and the q8_1 rounding -- the steps of
+ * orc_forward_fmt for those 64 weight rows alone, so the bytes equal the
+ * forward's H block.  Pairs with an expert id outside [0, E) give zeros. */
+void orc_h_blocks_fmt(const uint8_t* x_q8, const int32_t* idx, const uint8_t* gateup, int gu_fmt, int64_t T, int L,
+                      int F, int E, int k, int64_t n, const int64_t* pair, const int32_t* fb, uint8_t* out) {
+  int nb = L / Q81_VALUES;
+  int64_t xrow_bytes = (int64_t)nb * Q81_BYTES;
+  int64_t gu_e_bytes = (int64_t)2 * F * gu_row_bytes(gu_fmt, L);
+  (void)T;
+#pragma omp parallel for schedule(dynamic, 64)
+  for (int64_t i = 0; i < n; ++i) {
+    int64_t p = pair[i];
+    int e = idx[p];
+    uint8_t* o = out + i * Q81_BYTES;
+    if (e < 0 || e >= E) {
+      memset(o, 0, Q81_BYTES);
+      continue;
+    }
+    const uint8_t* xrow = x_q8 + (p / k) * xrow_bytes;
+    int32_t* I32 = (int32_t*)malloc(sizeof(int32_t) * nb);
+    double* dw = (double*)malloc(sizeof(double) * nb);
+    double* dx = (double*)malloc(sizeof(double) * nb);
+    double G[Q81_VALUES], U[Q81_VALUES];
+    for (int b = 0; b < nb; ++b) dx[b] = orc_half_to_double(rd16(xrow + (int64_t)b * Q81_BYTES));
+    for (int f = 0; f < Q81_VALUES; ++f) {
+      int feat = fb[i] * Q81_VALUES + f;
+      G[f] = gateup_row(gu_fmt, xrow, gateup + e * gu_e_bytes, L, feat, I32, dw, dx);
+      U[f] = gateup_row(gu_fmt, xrow, gateup + e * gu_e_bytes, L, F + feat, I32, dw, dx);
+    }
+    pair_swiglu_q8_1(G, U, Q81_VALUES, o);
+    free(I32);
+    free(dw);
+    free(dx);
+  }
 }
 
 /* Integer block-dot probes.

@@ -15,10 +15,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liblatmoe.so")
 
 LAT_MOE_MAX_E = 1024
-# down-weight formats of lat_moe_expert_forward_ex (both 18-byte blocks of 32)
+# down-weight formats of lat_moe_expert_forward_fmt (both 18-byte blocks of 32)
 DOWN_IQ4_NL = 0
 DOWN_Q4_0 = 1
-# gate/up-weight formats of lat_moe_expert_forward_ex
+# gate/up-weight formats of lat_moe_expert_forward_fmt
 GATEUP_Q3_K = 0
 GATEUP_Q4_0 = 1
 
@@ -26,8 +26,8 @@ GATEUP_Q4_0 = 1
 EXPORTED = (
     "lat_moe_workspace_size",
     "lat_moe_expert_forward",
-    "lat_moe_expert_forward_debug",
     "lat_moe_expert_forward_ex",
+    "lat_moe_expert_forward_fmt",
     "lat_moe_quantize_q8_1",
     "lat_moe_dense_q8_0",
     "lat_moe_dense_q8_0_debug",
@@ -57,6 +57,7 @@ class Debug(ctypes.Structure):
         ("dn_row0", ctypes.c_int32),
         ("dn_rows", ctypes.c_int32),
         ("stage_events", ctypes.POINTER(ctypes.c_void_p)),
+        ("deterministic", ctypes.c_int32),
     ]
 
 
@@ -80,12 +81,13 @@ def lib() -> ctypes.CDLL:
         c.lat_moe_workspace_size.restype = ctypes.c_size_t
         c.lat_moe_expert_forward.argtypes = [P, P, P, P, P, ctypes.POINTER(Shapes), P, P, ctypes.c_size_t, P]
         c.lat_moe_expert_forward.restype = ctypes.c_int
-        c.lat_moe_expert_forward_debug.argtypes = [P, P, P, P, P, ctypes.POINTER(Shapes), P, P, ctypes.c_size_t, P,
-                                                   ctypes.POINTER(Debug)]
-        c.lat_moe_expert_forward_debug.restype = ctypes.c_int
-        c.lat_moe_expert_forward_ex.argtypes = [P, P, P, P, ctypes.c_int32, P, ctypes.c_int32, ctypes.POINTER(Shapes),
-                                                P, P, ctypes.c_size_t, P, ctypes.POINTER(Debug)]
+        c.lat_moe_expert_forward_ex.argtypes = [P, P, P, P, P, ctypes.POINTER(Shapes), P, P, ctypes.c_size_t, P,
+                                                ctypes.POINTER(Debug)]
         c.lat_moe_expert_forward_ex.restype = ctypes.c_int
+        c.lat_moe_expert_forward_fmt.argtypes = [P, P, P, P, ctypes.c_int32, P, ctypes.c_int32,
+                                                 ctypes.POINTER(Shapes), P, P, ctypes.c_size_t, P,
+                                                 ctypes.POINTER(Debug)]
+        c.lat_moe_expert_forward_fmt.restype = ctypes.c_int
         c.lat_moe_quantize_q8_1.argtypes = [P, ctypes.c_int64, ctypes.c_int32, P, P]
         c.lat_moe_quantize_q8_1.restype = ctypes.c_int
         i32, i64 = ctypes.c_int32, ctypes.c_int64
@@ -144,7 +146,7 @@ def expert_forward(x_q8_1, router_idx, router_w, gateup_q3k, down_iq4nl, s: Shap
     _check(rc)
 
 
-def _debug(h_q8_1, perm, offsets, dropped, gateup_i32, gu_row0, down_i32, dn_row0, stage_events):
+def _debug(h_q8_1, perm, offsets, dropped, gateup_i32, gu_row0, down_i32, dn_row0, stage_events, deterministic):
     ev = None
     if stage_events is not None:
         if len(stage_events) != 5:
@@ -153,41 +155,45 @@ def _debug(h_q8_1, perm, offsets, dropped, gateup_i32, gu_row0, down_i32, dn_row
     d = Debug(_ptr(h_q8_1), _ptr(perm), _ptr(offsets), _ptr(dropped), _ptr(gateup_i32), int(gu_row0),
               0 if gateup_i32 is None else int(gateup_i32.shape[1]), _ptr(down_i32), int(dn_row0),
               0 if down_i32 is None else int(down_i32.shape[1]),
-              ctypes.cast(ev, ctypes.POINTER(ctypes.c_void_p)) if ev is not None else None)
+              ctypes.cast(ev, ctypes.POINTER(ctypes.c_void_p)) if ev is not None else None,
+              1 if deterministic else 0)
     return d, ev
 
 
-def expert_forward_debug(x_q8_1, router_idx, router_w, gateup_q3k, down_iq4nl, s: Shapes, y, workspace, *,
-                         h_q8_1=None, perm=None, offsets=None, dropped=None, gateup_i32=None, gu_row0=0,
-                         down_i32=None, dn_row0=0, stage_events=None, stream=None) -> None:
-    """As expert_forward, plus the optional debug outputs of lat_moe_debug.
-    gateup_i32 is [T*k, rows, L/32] int32 and down_i32 [T*k, rows, F/32];
-    stage_events is a list of five recorded torch.cuda.Event(enable_timing=True)."""
-    d, ev = _debug(h_q8_1, perm, offsets, dropped, gateup_i32, gu_row0, down_i32, dn_row0, stage_events)
-    rc = lib().lat_moe_expert_forward_debug(_ptr(x_q8_1), _ptr(router_idx), _ptr(router_w), _ptr(gateup_q3k),
-                                            _ptr(down_iq4nl), ctypes.byref(s), _ptr(y), _ptr(workspace),
-                                            workspace.numel() * workspace.element_size(), _stream(stream),
-                                            ctypes.byref(d))
+def expert_forward_ex(x_q8_1, router_idx, router_w, gateup_q3k, down_iq4nl, s: Shapes, y, workspace, *,
+                      deterministic: bool = True, h_q8_1=None, perm=None, offsets=None, dropped=None, gateup_i32=None,
+                      gu_row0=0, down_i32=None, dn_row0=0, stage_events=None, stream=None) -> None:
+    """As expert_forward, with the options and optional debug outputs of
+    lat_moe_debug: deterministic=False sums each token's experts into y by
+    fp32 atomic adds (no slot buffer, no combine kernel); gateup_i32 is
+    [T*k, rows, L/32] int32 and down_i32 [T*k, rows, F/32]; stage_events is a
+    list of five recorded torch.cuda.Event(enable_timing=True)."""
+    d, ev = _debug(h_q8_1, perm, offsets, dropped, gateup_i32, gu_row0, down_i32, dn_row0, stage_events,
+                   deterministic)
+    rc = lib().lat_moe_expert_forward_ex(_ptr(x_q8_1), _ptr(router_idx), _ptr(router_w), _ptr(gateup_q3k),
+                                         _ptr(down_iq4nl), ctypes.byref(s), _ptr(y), _ptr(workspace),
+                                         workspace.numel() * workspace.element_size(), _stream(stream),
+                                         ctypes.byref(d))
     _check(rc)
 
 
-def expert_forward_ex(x_q8_1, router_idx, router_w, gateup, down, down_format: int, s: Shapes, y, workspace, *,
-                      gateup_format: int = GATEUP_Q3_K, debug: bool = False, h_q8_1=None, perm=None, offsets=None,
-                      dropped=None, gateup_i32=None, gu_row0=0, down_i32=None, dn_row0=0, stage_events=None,
-                      stream=None) -> None:
+def expert_forward_fmt(x_q8_1, router_idx, router_w, gateup, down, down_format: int, s: Shapes, y, workspace, *,
+                       gateup_format: int = GATEUP_Q3_K, debug: bool = False, deterministic: bool = True,
+                       h_q8_1=None, perm=None, offsets=None, dropped=None, gateup_i32=None, gu_row0=0, down_i32=None,
+                       dn_row0=0, stage_events=None, stream=None) -> None:
     """The expert stage with gate/up weights in gateup_format (GATEUP_Q3_K:
     [E, 2F, L/256, 110]; GATEUP_Q4_0: [E, 2F, L/32, 18]) and down weights in
     down_format (DOWN_IQ4_NL or DOWN_Q4_0, both [E, L, F/32, 18] uint8); with
-    debug=True the optional outputs of expert_forward_debug are filled,
-    otherwise no debug struct is passed."""
+    debug=True (or deterministic=False) the options and optional outputs of
+    expert_forward_ex are passed, otherwise no debug struct is."""
     d = None
-    if debug:
-        d, ev = _debug(h_q8_1, perm, offsets, dropped, gateup_i32, gu_row0, down_i32, dn_row0, stage_events)
-    rc = lib().lat_moe_expert_forward_ex(_ptr(x_q8_1), _ptr(router_idx), _ptr(router_w), _ptr(gateup),
-                                         int(gateup_format), _ptr(down), int(down_format), ctypes.byref(s), _ptr(y),
-                                         _ptr(workspace),
-                                         workspace.numel() * workspace.element_size(), _stream(stream),
-                                         ctypes.byref(d) if d is not None else None)
+    if debug or not deterministic:
+        d, ev = _debug(h_q8_1, perm, offsets, dropped, gateup_i32, gu_row0, down_i32, dn_row0, stage_events,
+                       deterministic)
+    rc = lib().lat_moe_expert_forward_fmt(_ptr(x_q8_1), _ptr(router_idx), _ptr(router_w), _ptr(gateup),
+                                          int(gateup_format), _ptr(down), int(down_format), ctypes.byref(s), _ptr(y),
+                                          _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                          _stream(stream), ctypes.byref(d) if d is not None else None)
     _check(rc)
 
 

@@ -100,6 +100,8 @@ int check_device(int* num_cus) {
 int forward_impl(const void* x, const int32_t* idx, const float* w, const void* gu, int gu_fmt, const void* dn,
                  int down_fmt, const lat_moe_shapes* s, float* y, void* ws, size_t ws_bytes, void* stream,
                  const lat_moe_debug* dbg) {
+  // the slot buffer and ordered combine unless the caller asks for atomic adds
+  const bool deterministic = dbg ? dbg->deterministic != 0 : true;
   if (!shapes_ok(s)) return LAT_MOE_EINVAL;
   if (down_fmt != LAT_MOE_DOWN_IQ4_NL && down_fmt != LAT_MOE_DOWN_Q4_0) return LAT_MOE_EINVAL;
   if (gu_fmt != LAT_MOE_GATEUP_Q3_K && gu_fmt != LAT_MOE_GATEUP_Q4_0) return LAT_MOE_EINVAL;
@@ -135,7 +137,9 @@ int forward_impl(const void* x, const int32_t* idx, const float* w, const void* 
   auto mark = [&](int i) { return ev ? hipEventRecord(ev[i], st) : hipSuccess; };
   if (mark(0) != hipSuccess) return LAT_MOE_ELAUNCH;
   const bool small = small_path(sh);  // decode-sized batch: GEMV-shaped kernels (either weight format)
-  if (launch_route(idx, xb, sh, wk, small, st) != hipSuccess) return LAT_MOE_ELAUNCH;
+  // atomic combine: the route pass zeroes y, down adds into it, no combine kernel
+  const bool atomic = !deterministic && !small;
+  if (launch_route(idx, xb, sh, wk, small, atomic ? y : nullptr, st) != hipSuccess) return LAT_MOE_ELAUNCH;
   if (mark(1) != hipSuccess) return LAT_MOE_ELAUNCH;
   ProbeRows pg{nullptr, 0, 0}, pd{nullptr, 0, 0};
   if (dbg && dbg->gateup_i32) pg = ProbeRows{dbg->gateup_i32, dbg->gu_row0, dbg->gu_rows};
@@ -149,10 +153,10 @@ int forward_impl(const void* x, const int32_t* idx, const float* w, const void* 
   if (mark(2) != hipSuccess) return LAT_MOE_ELAUNCH;
   const int fmt = down_fmt == LAT_MOE_DOWN_Q4_0 ? kDownQ40 : kDownIq4Nl;
   if ((small ? launch_down_small(dnb, fmt, w, sh, wk, pd.out ? &pd : nullptr, st)
-             : launch_down(dnb, fmt, w, sh, wk, pd.out ? &pd : nullptr, st)) != hipSuccess)
+             : launch_down(dnb, fmt, w, sh, wk, atomic ? y : nullptr, pd.out ? &pd : nullptr, st)) != hipSuccess)
     return LAT_MOE_ELAUNCH;
   if (mark(3) != hipSuccess) return LAT_MOE_ELAUNCH;
-  if (launch_combine(idx, sh, wk, y, st) != hipSuccess) return LAT_MOE_ELAUNCH;
+  if (!atomic && launch_combine(idx, sh, wk, y, st) != hipSuccess) return LAT_MOE_ELAUNCH;
   if (mark(4) != hipSuccess) return LAT_MOE_ELAUNCH;
   if (dbg) {
     if (dbg->h_q8_1 && launch_export_h(sh, wk, static_cast<uint8_t*>(dbg->h_q8_1), st) != hipSuccess)
@@ -207,19 +211,17 @@ int lat_moe_expert_forward(const void* x_q8_1, const int32_t* router_idx, const 
                       shapes, y, workspace, workspace_bytes, stream, nullptr);
 }
 
-int lat_moe_expert_forward_debug(const void* x_q8_1, const int32_t* router_idx, const float* router_w,
-                                 const void* gateup_q3k, const void* down_iq4nl, const lat_moe_shapes* shapes,
-                                 float* y, void* workspace, size_t workspace_bytes, void* stream,
-                                 const lat_moe_debug* dbg) {
-  if (!dbg) return LAT_MOE_EINVAL;
+int lat_moe_expert_forward_ex(const void* x_q8_1, const int32_t* router_idx, const float* router_w,
+                              const void* gateup_q3k, const void* down_iq4nl, const lat_moe_shapes* shapes, float* y,
+                              void* workspace, size_t workspace_bytes, void* stream, const lat_moe_debug* dbg) {
   return forward_impl(x_q8_1, router_idx, router_w, gateup_q3k, LAT_MOE_GATEUP_Q3_K, down_iq4nl, LAT_MOE_DOWN_IQ4_NL,
                       shapes, y, workspace, workspace_bytes, stream, dbg);
 }
 
-int lat_moe_expert_forward_ex(const void* x_q8_1, const int32_t* router_idx, const float* router_w,
-                              const void* gateup, int32_t gateup_format, const void* down, int32_t down_format,
-                              const lat_moe_shapes* shapes, float* y, void* workspace, size_t workspace_bytes,
-                              void* stream, const lat_moe_debug* dbg) {
+int lat_moe_expert_forward_fmt(const void* x_q8_1, const int32_t* router_idx, const float* router_w,
+                               const void* gateup, int32_t gateup_format, const void* down, int32_t down_format,
+                               const lat_moe_shapes* shapes, float* y, void* workspace, size_t workspace_bytes,
+                               void* stream, const lat_moe_debug* dbg) {
   return forward_impl(x_q8_1, router_idx, router_w, gateup, gateup_format, down, down_format, shapes, y, workspace,
                       workspace_bytes, stream, dbg);
 }

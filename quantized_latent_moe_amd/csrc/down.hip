@@ -15,7 +15,8 @@
 // (contiguous per sorted pair) and fp16 d_H.  The 4-bit indices expand to int8
 // through the 16-entry table with two v_perm_b32 lookups and a byte select.
 // Epilogue: O * router_w[p] is written to the pair's slot row (pair order), so
-// the combine sums each token's k slots in a fixed order.
+// the combine sums each token's k slots in a fixed order; or, for the combine
+// by atomic adds, added into the token's row of y with fp32 atomics.
 #include <type_traits>
 
 #include "lat_moe_internal.h"
@@ -35,14 +36,30 @@ constexpr int kRawHalfPer = kRawHalf / kThreads;               // 9
 static_assert(kRawHalf % kThreads == 0, "staging split");
 static_assert(kNT * 16 == 2 * kThreads && kNT * 8 == kThreads && kLT * 8 == kThreads, "staging split");
 
-template <bool PROBE, bool ALIGNED16, int FMT>
+// Four consecutive floats of an output row: a 16-byte store into a slot row,
+// or four fp32 atomic adds into y (global_atomic_add_f32, no return value).
+template <bool ATOMIC>
+__device__ __forceinline__ void store_or_add(float* dst, float4 v) {
+  if constexpr (ATOMIC) {
+    unsafeAtomicAdd(dst + 0, v.x);
+    unsafeAtomicAdd(dst + 1, v.y);
+    unsafeAtomicAdd(dst + 2, v.z);
+    unsafeAtomicAdd(dst + 3, v.w);
+  } else {
+    *reinterpret_cast<float4*>(dst) = v;
+  }
+}
+
+// out: the slot rows [T*k][L] (ATOMIC false) or y [T][L] (ATOMIC true: each
+// pair's weighted row is added into its token's row with fp32 atomic adds).
+template <bool PROBE, bool ALIGNED16, int FMT, bool ATOMIC>
 __global__ __launch_bounds__(kThreads) void k_down_generic(const uint8_t* __restrict__ dn, const float* __restrict__ router_w,
                                                    const int32_t* __restrict__ perm,
                                                    const int32_t* __restrict__ tiles,
                                                    const int32_t* __restrict__ offsets,
-                                                   const int32_t* __restrict__ misc, int L, int F,
+                                                   const int32_t* __restrict__ misc, int L, int F, int k,
                                                    const int8_t* __restrict__ h_codes,
-                                                   const uint32_t* __restrict__ h_ds, float* __restrict__ slots,
+                                                   const uint32_t* __restrict__ h_ds, float* __restrict__ out,
                                                    ProbeRows probe) {
   __shared__ __align__(16) uint8_t raw[kLT * kRawStride];
   __shared__ __align__(16) int8_t As[kLT * kOpStride];
@@ -203,13 +220,13 @@ __global__ __launch_bounds__(kThreads) void k_down_generic(const uint8_t* __rest
     __syncthreads();
   }
 
-  // ---- epilogue: weighted output rows into the pair's slot
+  // ---- epilogue: weighted output rows into the pair's slot (or y)
   if (!active) return;
   const int n = 32 * tsub + col;
   const int p = pid[n];
   if (p >= 0) {
     const float wgt = router_w[p];
-    float* dst = slots + (int64_t)p * L + l0 + 32 * lsub + 4 * khalf;
+    float* dst = out + (int64_t)(ATOMIC ? p / k : p) * L + l0 + 32 * lsub + 4 * khalf;
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) {
       float4 v;
@@ -217,7 +234,7 @@ __global__ __launch_bounds__(kThreads) void k_down_generic(const uint8_t* __rest
       v.y = acc[4 * qq + 1] * wgt;
       v.z = acc[4 * qq + 2] * wgt;
       v.w = acc[4 * qq + 3] * wgt;
-      *reinterpret_cast<float4*>(dst + 8 * qq) = v;
+      store_or_add<ATOMIC>(dst + 8 * qq, v);
     }
   }
 }
@@ -282,14 +299,14 @@ __device__ __forceinline__ DItem ditem(int i, int nlt, const int32_t* tiles) {
   return it;
 }
 
-template <bool PROBE, int FMT>
+template <bool PROBE, int FMT, bool ATOMIC>
 __global__ __launch_bounds__(kWsThreads) void k_down(const uint8_t* __restrict__ dn, const float* __restrict__ router_w,
                                                      const int32_t* __restrict__ perm,
                                                      const int32_t* __restrict__ tiles,
                                                      const int32_t* __restrict__ offsets,
-                                                     const int32_t* __restrict__ misc, int pairs, int L, int F,
+                                                     const int32_t* __restrict__ misc, int pairs, int L, int F, int k,
                                                      const int8_t* __restrict__ h_codes,
-                                                     const uint32_t* __restrict__ h_ds, float* __restrict__ slots,
+                                                     const uint32_t* __restrict__ h_ds, float* __restrict__ out,
                                                      ProbeRows probe) {
   __shared__ __align__(16) uint8_t raw[kWsLT * kWsStep];
   __shared__ __align__(16) int8_t As[2][kWsLT * 256];
@@ -537,13 +554,13 @@ __global__ __launch_bounds__(kWsThreads) void k_down(const uint8_t* __restrict__
         mma(std::false_type{}, grp_tag, b);
       }
       if (++csb == nsb) {
-        // ---- weighted output rows into the pairs' slots
+        // ---- weighted output rows into the pairs' slots (or added into y)
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           const int pr = t ? pair1 : pair0;
           const float wgt = t ? w1 : w0;
           if (pr >= 0) {
-            float* dst = slots + (int64_t)pr * L + cur.l0 + 32 * rs + 4 * khalf;
+            float* dst = out + (int64_t)(ATOMIC ? pr / k : pr) * L + cur.l0 + 32 * rs + 4 * khalf;
 #pragma unroll
             for (int qq = 0; qq < 4; ++qq) {
               const float* a = t ? acc1 : acc0;
@@ -552,7 +569,7 @@ __global__ __launch_bounds__(kWsThreads) void k_down(const uint8_t* __restrict__
               v.y = a[4 * qq + 1] * wgt;
               v.z = a[4 * qq + 2] * wgt;
               v.w = a[4 * qq + 3] * wgt;
-              *reinterpret_cast<float4*>(dst + 8 * qq) = v;
+              store_or_add<ATOMIC>(dst + 8 * qq, v);
             }
           }
         }
@@ -566,20 +583,20 @@ __global__ __launch_bounds__(kWsThreads) void k_down(const uint8_t* __restrict__
   else consumer_loop(std::integral_constant<int, 0>{});
 }
 
-template <bool PROBE, int FMT>
+template <bool PROBE, int FMT, bool ATOMIC>
 void launch_variant(bool aligned, dim3 grid, hipStream_t st, const uint8_t* dn, const float* router_w,
-                    const Shapes& s, const Work& w, ProbeRows probe) {
+                    const Shapes& s, const Work& w, float* out, ProbeRows probe) {
   if (aligned)
-    hipLaunchKernelGGL((k_down_generic<PROBE, true, FMT>), grid, dim3(kThreads), 0, st, dn, router_w, w.perm, w.tiles,
-                       w.offsets, w.misc, s.L, s.F, w.h_codes, w.h_ds, w.slots, probe);
+    hipLaunchKernelGGL((k_down_generic<PROBE, true, FMT, ATOMIC>), grid, dim3(kThreads), 0, st, dn, router_w, w.perm,
+                       w.tiles, w.offsets, w.misc, s.L, s.F, s.k, w.h_codes, w.h_ds, out, probe);
   else
-    hipLaunchKernelGGL((k_down_generic<PROBE, false, FMT>), grid, dim3(kThreads), 0, st, dn, router_w, w.perm, w.tiles,
-                       w.offsets, w.misc, s.L, s.F, w.h_codes, w.h_ds, w.slots, probe);
+    hipLaunchKernelGGL((k_down_generic<PROBE, false, FMT, ATOMIC>), grid, dim3(kThreads), 0, st, dn, router_w, w.perm,
+                       w.tiles, w.offsets, w.misc, s.L, s.F, s.k, w.h_codes, w.h_ds, out, probe);
 }
 
-template <int FMT>
-void launch_fmt(const uint8_t* dn, const float* router_w, const Shapes& s, const Work& w, const ProbeRows* probe,
-                hipStream_t st) {
+template <int FMT, bool ATOMIC>
+void launch_fmt(const uint8_t* dn, const float* router_w, const Shapes& s, const Work& w, float* out,
+                const ProbeRows* probe, hipStream_t st) {
   const ProbeRows none = {nullptr, 0, 0};
   if (s.F % 256 == 0 && ((uintptr_t)dn & 15u) == 0) {
     // one persistent workgroup per CU, a multiple of the XCD count
@@ -587,11 +604,11 @@ void launch_fmt(const uint8_t* dn, const float* router_w, const Shapes& s, const
     if (grid < kXcds) grid = kXcds;
     const int pairs = (int)s.pairs();
     if (probe)
-      hipLaunchKernelGGL((k_down<true, FMT>), dim3(grid), dim3(kWsThreads), 0, st, dn, router_w, w.perm, w.tiles,
-                         w.offsets, w.misc, pairs, s.L, s.F, w.h_codes, w.h_ds, w.slots, *probe);
+      hipLaunchKernelGGL((k_down<true, FMT, ATOMIC>), dim3(grid), dim3(kWsThreads), 0, st, dn, router_w, w.perm,
+                         w.tiles, w.offsets, w.misc, pairs, s.L, s.F, s.k, w.h_codes, w.h_ds, out, *probe);
     else
-      hipLaunchKernelGGL((k_down<false, FMT>), dim3(grid), dim3(kWsThreads), 0, st, dn, router_w, w.perm, w.tiles,
-                         w.offsets, w.misc, pairs, s.L, s.F, w.h_codes, w.h_ds, w.slots, none);
+      hipLaunchKernelGGL((k_down<false, FMT, ATOMIC>), dim3(grid), dim3(kWsThreads), 0, st, dn, router_w, w.perm,
+                         w.tiles, w.offsets, w.misc, pairs, s.L, s.F, s.k, w.h_codes, w.h_ds, out, none);
     return;
   }
   const dim3 grid(w.max_tiles, s.L / kLT);
@@ -599,19 +616,26 @@ void launch_fmt(const uint8_t* dn, const float* router_w, const Shapes& s, const
   // that also means F is a multiple of 256, so every step is a full 144-byte chunk.
   const bool aligned = ((int64_t)(s.F / 32) * kIq4Bytes) % 16 == 0 && ((uintptr_t)dn & 15u) == 0;
   if (probe)
-    launch_variant<true, FMT>(aligned, grid, st, dn, router_w, s, w, *probe);
+    launch_variant<true, FMT, ATOMIC>(aligned, grid, st, dn, router_w, s, w, out, *probe);
   else
-    launch_variant<false, FMT>(aligned, grid, st, dn, router_w, s, w, none);
+    launch_variant<false, FMT, ATOMIC>(aligned, grid, st, dn, router_w, s, w, out, none);
 }
 
 }  // namespace
 
 hipError_t launch_down(const uint8_t* dn, int fmt, const float* router_w, const Shapes& s, const Work& w,
-                       const ProbeRows* probe, hipStream_t st) {
-  if (fmt == kDownQ40)
-    launch_fmt<kDownQ40>(dn, router_w, s, w, probe, st);
-  else
-    launch_fmt<kDownIq4Nl>(dn, router_w, s, w, probe, st);
+                       float* y_atomic, const ProbeRows* probe, hipStream_t st) {
+  if (y_atomic) {
+    if (fmt == kDownQ40)
+      launch_fmt<kDownQ40, true>(dn, router_w, s, w, y_atomic, probe, st);
+    else
+      launch_fmt<kDownIq4Nl, true>(dn, router_w, s, w, y_atomic, probe, st);
+  } else {
+    if (fmt == kDownQ40)
+      launch_fmt<kDownQ40, false>(dn, router_w, s, w, w.slots, probe, st);
+    else
+      launch_fmt<kDownIq4Nl, false>(dn, router_w, s, w, w.slots, probe, st);
+  }
   return hipGetLastError();
 }
 

@@ -185,15 +185,18 @@ __device__ __forceinline__ uint4 buf_u128(rsrc_t r, int voff, int soff) {
 // Kernel launchers (each returns hipGetLastError() after the enqueue).
 // Sorts pairs by expert and splits the q8_1 activations x into codes and scales.
 // gather: also copy small batches' rows in sorted order for the GEMV-shaped
-// gate/up kernel (which then needs no split rows).
+// gate/up kernel (which then needs no split rows).  yzero: y [T][L] to fill
+// with zeros for the down kernel's atomic adds, or null.
 hipError_t launch_route(const int32_t* idx, const uint8_t* x, const Shapes& s, const Work& w, bool gather,
-                        hipStream_t st);
+                        float* yzero, hipStream_t st);
 hipError_t launch_gateup(const Shapes& s, const Work& w, const uint8_t* gu, const ProbeRows* probe, hipStream_t st);
 // Gate/up weights in Q4_0 (18-byte blocks, a scale per 32 values), batches beyond small_path.
 hipError_t launch_gateup_q40(const Shapes& s, const Work& w, const uint8_t* gu, const ProbeRows* probe,
                              hipStream_t st);
+// y_atomic null: each pair's weighted row goes to its slot; otherwise it is
+// added into y_atomic [T][L] (zeroed beforehand) with fp32 atomic adds.
 hipError_t launch_down(const uint8_t* dn, int fmt, const float* router_w, const Shapes& s, const Work& w,
-                       const ProbeRows* probe, hipStream_t st);
+                       float* y_atomic, const ProbeRows* probe, hipStream_t st);
 // Batches of at most kSmallMaxPairs pairs (L <= 1024, F <= 2048) take the
 // GEMV-shaped gate/up and down kernels.
 constexpr int kSmallMaxPairs = kGatherRows;

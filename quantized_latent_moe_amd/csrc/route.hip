@@ -1,8 +1,8 @@
 // Counting sort of routed pairs by expert, on the device.
 //
-// The grouped GEMMs read every expert's weights in place and need the pairs
-// routed to each expert together ("each expert read where it is", page "Run
-// Edge0-145B Q3_K on AMD HIP (Linux, gfx1100) #1", lat_q3k_w11.cu commit).
+// The grouped GEMMs read each expert's weights in place (page "Run
+// Edge0-145B Q3_K on AMD HIP (Linux, gfx1100) #1", lat_q3k_w11.cu commit
+// message), so the pairs routed to one expert have to sit together.
 // Result: perm (pair ids grouped by expert, ascending within an expert),
 // offsets[E+1], the table of (expert, first position, pairs) token tiles of
 // kTileN pairs, and the dropped / valid / tile counts.  No host
@@ -15,7 +15,8 @@
 // passes over chunks of kRouteChunk pairs (per-chunk histograms; one
 // workgroup scanning chunks and experts; per-chunk stable scatter).  In both
 // the first launch carries extra workgroups that split the q8_1 activations
-// into int8 codes and fp32 scales (independent work, one launch fewer).
+// into int8 codes and fp32 scales (independent work, one launch fewer), and,
+// for the combine by atomic adds, workgroups that zero y.
 // Stable ranks inside a wave come from ballots over the bits of the id.
 #include "lat_moe_internal.h"
 
@@ -37,6 +38,15 @@ __device__ __forceinline__ void split_block(const uint8_t* __restrict__ x, int64
   dst[0] = lo;
   dst[1] = hi;
   xd[db] = half_bits_to_float(src[0] & 0xffffu);
+}
+
+// Zeroes floats [i0, i0 + kZeroPerBlock) of y (clipped to n): the extra
+// workgroups of the first route launch clear y for the down kernel's atomic
+// adds.  float4 stores; n is a multiple of 4 (L % 256 == 0).
+constexpr int kZeroPerBlock = 16384;
+__device__ __forceinline__ void zero_chunk(float* __restrict__ y, int64_t n, int64_t i0) {
+  for (int64_t i = i0 + 4 * (int64_t)threadIdx.x; i < i0 + kZeroPerBlock && i < n; i += 4 * (int64_t)blockDim.x)
+    *reinterpret_cast<float4*>(y + i) = float4{0.f, 0.f, 0.f, 0.f};
 }
 
 // Rows of the first nvalid sorted pairs (pair ids perm[0..nvalid), token =
@@ -136,8 +146,13 @@ __global__ __launch_bounds__(1024) void k_route_small(const int32_t* __restrict_
                                                       const uint8_t* __restrict__ x, int64_t nxb,
                                                       int8_t* __restrict__ xc, float* __restrict__ xd, int gather,
                                                       int k, int rb, int8_t* __restrict__ xg,
-                                                      float* __restrict__ xgd) {
+                                                      float* __restrict__ xgd, int xblocks, float* __restrict__ yzero,
+                                                      int64_t ny) {
   if (blockIdx.x > 0) {
+    if ((int)blockIdx.x > xblocks) {  // y for the atomic combine
+      zero_chunk(yzero, ny, (int64_t)(blockIdx.x - 1 - xblocks) * kZeroPerBlock);
+      return;
+    }
     const int64_t b = (int64_t)(blockIdx.x - 1) * kSplitPerBlock + threadIdx.x;
     if (b < nxb) split_block(x, b, b, xc, xd);
     return;
@@ -261,7 +276,12 @@ __global__ __launch_bounds__(256) void k_route_hist(const int32_t* __restrict__ 
                                                     int nchunk, int32_t* __restrict__ chunk_hist,
                                                     int32_t* __restrict__ chunk_bad, const uint8_t* __restrict__ x,
                                                     int64_t nxb, int8_t* __restrict__ xc,
-                                                    float* __restrict__ xd) {
+                                                    float* __restrict__ xd, int xblocks, float* __restrict__ yzero,
+                                                    int64_t ny) {
+  if ((int)blockIdx.x >= nchunk + xblocks) {  // y for the atomic combine
+    zero_chunk(yzero, ny, (int64_t)(blockIdx.x - nchunk - xblocks) * kZeroPerBlock);
+    return;
+  }
   if ((int)blockIdx.x >= nchunk) {
     const int64_t b0 = (int64_t)(blockIdx.x - nchunk) * kSplitPerBlock;
     for (int i = threadIdx.x; i < kSplitPerBlock; i += blockDim.x)
@@ -375,22 +395,26 @@ __global__ __launch_bounds__(256) void k_route_scatter(const int32_t* __restrict
 }  // namespace
 
 hipError_t launch_route(const int32_t* idx, const uint8_t* x, const Shapes& s, const Work& w, bool gather,
-                        hipStream_t st) {
+                        float* yzero, hipStream_t st) {
   const int64_t n = s.pairs();
   int nbits = 0;
   while ((1 << nbits) < s.E) ++nbits;
   const int64_t nxb = s.T * (s.L / 32);
   const unsigned xblocks = (unsigned)((nxb + kSplitPerBlock - 1) / kSplitPerBlock);
+  const int64_t ny = yzero ? s.T * s.L : 0;
+  const unsigned zblocks = (unsigned)((ny + kZeroPerBlock - 1) / kZeroPerBlock);
   // The GEMV-shaped gate/up kernel reads the gathered rows and not the split
   // ones (small batches: T * k <= kGatherRows and L <= 1024).
   if (n <= kSmallPairs && s.E <= 512) {  // (2 + 16) * E + kGatherRows ints of LDS
-    hipLaunchKernelGGL(k_route_small, dim3(gather ? 1 : 1 + xblocks), dim3(1024),
+    const unsigned xb = gather ? 0 : xblocks;
+    hipLaunchKernelGGL(k_route_small, dim3(1 + xb + zblocks), dim3(1024),
                        ((2 + 16) * s.E + kGatherRows) * sizeof(int32_t), st, idx, (int)n, s.E, nbits, w.offsets,
-                       w.tiles, w.misc, w.perm, x, nxb, w.xc, w.xd, gather ? 1 : 0, s.k, s.L / 32, w.xg, w.xgd);
+                       w.tiles, w.misc, w.perm, x, nxb, w.xc, w.xd, gather ? 1 : 0, s.k, s.L / 32, w.xg, w.xgd,
+                       (int)xb, yzero, ny);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(k_route_hist, dim3(w.nchunk + xblocks), dim3(256), s.E * sizeof(int32_t), st, idx, n, s.E,
-                     w.nchunk, w.chunk_hist, w.chunk_bad, x, nxb, w.xc, w.xd);
+  hipLaunchKernelGGL(k_route_hist, dim3(w.nchunk + xblocks + zblocks), dim3(256), s.E * sizeof(int32_t), st, idx, n,
+                     s.E, w.nchunk, w.chunk_hist, w.chunk_bad, x, nxb, w.xc, w.xd, (int)xblocks, yzero, ny);
   hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(1024), 0, st, w.chunk_hist, w.chunk_bad, w.nchunk, s.E, w.offsets,
                      w.tiles, w.misc);
   hipLaunchKernelGGL(k_route_scatter, dim3(w.nchunk), dim3(256), 5 * s.E * sizeof(int32_t), st, idx, n, s.E, nbits,

@@ -118,6 +118,22 @@ def _route(rng: np.random.Generator, wl: Workload) -> tuple:
     return order.astype(np.int32), top.astype(np.float32), raw
 
 
+def make_routing_draws(wl: Workload, n: int) -> list:
+    """n more draws of the workload's activations and routing (steps 1-4 of
+    the recipe, x then logits, skew and top-k), each from a stream of its own
+    (seed [seed, 8 + i]); the weights are not redrawn.  A timing that rotates
+    among them finds no call's experts left in cache by the call before.
+    Returns a list of (x float32 [T, L], router_idx int32 [T, k], router_w
+    float32 [T, k])."""
+    out = []
+    for i in range(n):
+        rng = np.random.default_rng([wl.seed, 8 + i])
+        x = rng.standard_normal((wl.T, wl.L), dtype=np.float32)
+        idx, w, _ = _route(rng, wl)
+        out.append((x, idx, w))
+    return out
+
+
 def random_q3k(rng: np.random.Generator, shape: tuple) -> np.ndarray:
     """Uniform random Q3_K blocks with fp16 scales d ~ U(0.005, 0.015)."""
     b = rng.integers(0, 256, size=shape + (Q3K_BLOCK_BYTES,), dtype=np.uint8)

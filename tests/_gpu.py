@@ -8,7 +8,11 @@ through its C ABI, and compare with the oracle by the stage's criteria:
       the oracle's down projection and combine fed the GPU's own H (the GPU's
       fp32 folds and the oracle's fp64 folds may round a few H codes
       differently, and each such +-1 legitimately moves a whole output row).
-      The end-to-end difference against the oracle's own y is reported.
+  E2E y end to end: max |y_gpu - y_oracle| <= 1e-2 * rms(y_oracle).  The
+      stated 2e-3 * rms is read stage-wise (C3): rounding alone flips a few H
+      codes by one (about 3 in 10^6 at the 5268-token shape), and one flip
+      moves its token's row by w * d_H * K * d_dn, up to about 3.5e-3 * rms
+      there; 1e-2 leaves room for a few flips on one row and nothing more.
 """
 from __future__ import annotations
 
@@ -21,6 +25,7 @@ import oracle
 import quantized_latent_moe_amd as lm
 
 Y_TOL = 2e-3        # C3, relative to rms(y_ref)
+E2E_TOL = 1e-2      # y end to end, relative to rms(y_oracle)
 H_EQUAL = 0.9999    # C2
 
 
@@ -54,7 +59,7 @@ class Gpu:
         torch.cuda.synchronize()
         return self.y[: self.wl.T].cpu().numpy()
 
-    def forward_debug(self, gu_rows=None, dn_rows=None):
+    def forward_debug(self, gu_rows=None, dn_rows=None, deterministic=True):
         wl = self.wl
         P = wl.T * wl.k
         dev = self.x.device
@@ -67,10 +72,10 @@ class Gpu:
             gi = torch.zeros((P, gu_rows[1], wl.L // 32), dtype=torch.int32, device=dev)
         if dn_rows is not None:
             di = torch.zeros((P, dn_rows[1], wl.F // 32), dtype=torch.int32, device=dev)
-        lm.expert_forward_debug(self.x, self.idx, self.w, self.gu, self.dn, self.s, self.y, self.ws, h_q8_1=h,
+        lm.expert_forward_ex(self.x, self.idx, self.w, self.gu, self.dn, self.s, self.y, self.ws, h_q8_1=h,
                                 perm=perm, offsets=offs, dropped=dropped, gateup_i32=gi,
                                 gu_row0=0 if gu_rows is None else gu_rows[0], down_i32=di,
-                                dn_row0=0 if dn_rows is None else dn_rows[0])
+                                dn_row0=0 if dn_rows is None else dn_rows[0], deterministic=deterministic)
         torch.cuda.synchronize()
         out = dict(y=self.y[: wl.T].cpu().numpy(), h=h.cpu().numpy(), perm=perm.cpu().numpy(),
                    offsets=offs.cpu().numpy(), dropped=int(dropped.item()))
@@ -110,6 +115,15 @@ def check_y(y_gpu, y_ref, label=""):
     say(f"{label} y max|err| / rms = {err / max(rms, 1e-30):.3e}")
     assert err <= Y_TOL * rms + 1e-30, (err, rms)
     return err / max(rms, 1e-30)
+
+
+def check_e2e(y_gpu, y_ref, label=""):
+    rms = float(np.sqrt(np.mean(y_ref ** 2))) if y_ref.size else 0.0
+    err = float(np.abs(y_gpu - y_ref).max()) if y_ref.size else 0.0
+    rel = err / max(rms, 1e-30)
+    say(f"{label} end-to-end y max|err| / rms = {rel:.3e} (the literal 2e-3 {'met' if rel <= Y_TOL else 'NOT met'})")
+    assert err <= E2E_TOL * rms + 1e-30, (err, rms)
+    return rel
 
 
 def stagewise_y(out, I, tokens=None):

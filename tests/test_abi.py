@@ -27,6 +27,25 @@ def test_exports_every_declared_symbol():
     assert lm.version() >= 100
 
 
+def test_boundary_entry_points_and_debug_struct():
+    """The boundary's calls (workspace size, the stage, the stage with the
+    debug struct, error strings) are exported, and the binding's debug struct
+    has the header's fields in the header's order, the deterministic flag
+    last."""
+    for n in ("lat_moe_workspace_size", "lat_moe_expert_forward", "lat_moe_expert_forward_ex", "lat_moe_strerror"):
+        assert n in _declared()
+    src = open(os.path.join(ROOT, "include", "lat_moe.h")).read()
+    body = re.search(r"typedef struct lat_moe_debug \{(.*?)\} lat_moe_debug;", src, flags=re.S).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    fields = []
+    for decl in body.split(";"):
+        decl = decl.strip()
+        if decl:
+            fields += [re.sub(r"[^\w]", "", n.split()[-1]) for n in decl.split(",")]
+    assert fields == [f[0] for f in lm.Debug._fields_]
+    assert fields[-1] == "deterministic"
+
+
 def test_workspace_size():
     ok = lm.shapes(5268, 1024, 2048, 128, 8)
     ws = lm.workspace_size(ok)
@@ -59,12 +78,22 @@ def test_argument_errors_before_any_hip_call():
     # T = 0 is a no-op that touches nothing
     assert _fwd([None] * 7, lm.shapes(0, 256, 512, 8, 2), 0) == 0
     # debug row ranges are validated too
-    d = lm.Debug(None, None, None, None, 0x1000, 1000, 40, None, 0, 0, None)
-    rc = lm.lib().lat_moe_expert_forward_debug(*good[:5], ctypes.byref(s), good[5], good[6], need, None,
-                                               ctypes.byref(d))
-    assert rc == 1
+    fx = lm.lib().lat_moe_expert_forward_ex
+    for det in (0, 1):
+        d = lm.Debug(None, None, None, None, 0x1000, 1000, 40, None, 0, 0, None, det)
+        assert fx(*good[:5], ctypes.byref(s), good[5], good[6], need, None, ctypes.byref(d)) == 1
+        d = lm.Debug(None, None, None, None, None, 0, 0, 0x1000, 250, 7, None, det)
+        assert fx(*good[:5], ctypes.byref(s), good[5], good[6], need, None, ctypes.byref(d)) == 1
+    # _ex with no debug struct is the plain call: same argument checks
+    for i in range(7):
+        p = list(good)
+        p[i] = None
+        assert fx(*p[:5], ctypes.byref(s), p[5], p[6], need, None, None) == 1
+    assert fx(*good[:5], ctypes.byref(s), good[5], good[6], need - 1, None, None) == 2
+    assert fx(None, None, None, None, None, ctypes.byref(lm.shapes(0, 256, 512, 8, 2)), None, None, 0, None,
+              None) == 0
     # the format entry point: its format argument is checked first, then as above
-    ex = lm.lib().lat_moe_expert_forward_ex
+    ex = lm.lib().lat_moe_expert_forward_fmt
     s0 = ctypes.byref(lm.shapes(0, 256, 512, 8, 2))
     for gfmt, dfmt, rc in ((lm.GATEUP_Q3_K, lm.DOWN_IQ4_NL, 0), (lm.GATEUP_Q4_0, lm.DOWN_Q4_0, 0),
                            (lm.GATEUP_Q3_K, 2, 1), (lm.GATEUP_Q3_K, -1, 1), (2, lm.DOWN_IQ4_NL, 1)):

@@ -152,3 +152,59 @@ def test_single_expert_is_dense_swiglu_ffn():
         assert (np.abs(r.y[t] - y) <= bound).all()
         # and the bound is not vacuous: the requant error is a small part of y
         assert np.abs(r.y[t] - y).max() < 0.02 * np.abs(y).max()
+
+
+FORMATS = [("q3_k", "iq4_nl"), ("q4_0", "q4_0"), ("q3_k", "q4_0"), ("q4_0", "iq4_nl")]
+
+
+def _gateup(I, gfmt):
+    from quantized_latent_moe_amd.inputs import make_gateup_q4_0
+    return I.gateup_q3k if gfmt == "q3_k" else make_gateup_q4_0(I.wl)
+
+
+@pytest.mark.parametrize("gfmt,dfmt", FORMATS)
+def test_token_subset_equals_rows_of_full_run(gfmt, dfmt):
+    """The token-subset mode (what the full-size GPU checks use) evaluates
+    exactly the rows of the full run: y, H, G/U and the dropped count of the
+    chosen tokens, byte for byte, in the order the tokens are given (repeats
+    and an invalid id included), for both stage entry points."""
+    T, L, F, E, k = 12, 256, 96, 5, 3
+    I, xq = _case(T=T, L=L, F=F, E=E, k=k, seed=31, zipf=1.1)
+    idx = I.router_idx.copy()
+    idx[4, 1] = -2          # dropped pair
+    idx[7, :] = 3           # one expert in every slot
+    gu = _gateup(I, gfmt)
+    full = oracle.forward(xq, idx, I.router_w, gu, I.down_iq4nl, L, F, E, want_gu=True, gateup_format=gfmt,
+                          down_format=dfmt)
+    toks = np.array([7, 0, 4, 11, 4, 2], np.int64)
+    sub = oracle.forward(xq, idx, I.router_w, gu, I.down_iq4nl, L, F, E, tokens=toks, want_gu=True,
+                         gateup_format=gfmt, down_format=dfmt)
+    pairs = (toks[:, None] * k + np.arange(k)[None, :]).reshape(-1)
+    assert np.array_equal(sub.y, full.y[toks])
+    assert np.array_equal(sub.h, full.h[pairs])
+    assert np.array_equal(sub.gu, full.gu[pairs])
+    assert full.dropped == 1 and sub.dropped == 2     # token 4 is evaluated twice
+    yd = oracle.down_combine(full.h, idx, I.router_w, I.down_iq4nl, L, F, E, down_format=dfmt)
+    ys = oracle.down_combine(full.h, idx, I.router_w, I.down_iq4nl, L, F, E, tokens=toks, down_format=dfmt)
+    assert np.array_equal(ys, yd[toks])
+    # fed the oracle's own H, down + combine is the forward's y
+    assert np.array_equal(yd, full.y)
+
+
+@pytest.mark.parametrize("gfmt", ["q3_k", "q4_0"])
+def test_h_blocks_equal_forward_blocks(gfmt):
+    """h_blocks (H of single 32-feature blocks, for checks at full size)
+    returns the forward's H block, byte for byte, for every (pair, block),
+    in any order, zeros for a dropped pair."""
+    T, L, F, E, k = 6, 512, 96, 4, 2
+    I, xq = _case(T=T, L=L, F=F, E=E, k=k, seed=32)
+    idx = I.router_idx.copy()
+    idx[2, 0] = E      # dropped
+    gu = _gateup(I, gfmt)
+    full = oracle.forward(xq, idx, I.router_w, gu, I.down_iq4nl, L, F, E, gateup_format=gfmt)
+    P, nfb = T * k, F // 32
+    pairs = np.repeat(np.arange(P), nfb)[::-1].copy()
+    fb = np.tile(np.arange(nfb), P)[::-1].copy()
+    got = oracle.h_blocks(xq, idx, gu, L, F, E, pairs, fb, gateup_format=gfmt)
+    assert np.array_equal(got, full.h[pairs, fb])
+    assert not got[(pairs == 4) & (fb == 0)].any()
