@@ -49,6 +49,7 @@ extern "C" {
 #define LAT_MOE_EWORKSPACE 2 /* workspace_bytes smaller than lat_moe_workspace_size() */
 #define LAT_MOE_EDEVICE 3    /* current device is not a gfx950 (MI355X/MI350X) */
 #define LAT_MOE_ELAUNCH 4    /* a kernel launch failed (hipGetLastError after enqueue) */
+#define LAT_MOE_ESCRATCH 5   /* the shapes need more workspace than LAT_MOE_NOALLOC_SCRATCH_BYTES */
 
 #define LAT_MOE_MAX_E 1024
 #define LAT_MOE_ROUTER_MAX_E 1024 /* experts the router takes */
@@ -83,6 +84,22 @@ size_t lat_moe_workspace_size(const lat_moe_shapes* shapes);
 int lat_moe_expert_forward(const void* x_q8_1, const int32_t* router_idx, const float* router_w,
                            const void* gateup_q3k, const void* down_iq4nl, const lat_moe_shapes* shapes,
                            float* y, void* workspace, size_t workspace_bytes, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the expert
+ * stage of lat_moe_expert_forward (same arguments without the workspace,
+ * same kernels, same y bit for bit), its workspace taken from a device array
+ * of LAT_MOE_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it
+ * runs on until the process ends.  Shapes whose lat_moe_workspace_size
+ * exceeds that return LAT_MOE_ESCRATCH (nothing enqueued); with L = 1024,
+ * F = 2048 and k = 8 that is above about 1300 tokens.  The call allocates
+ * nothing.  All calls on one GPU share its array: calls that overlap in time
+ * on one GPU (other streams, other threads) race, and must be serialised by
+ * the caller. */
+#define LAT_MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int lat_moe_expert_forward_noalloc(const void* x_q8_1, const int32_t* router_idx, const float* router_w,
+                                   const void* gateup_q3k, const void* down_iq4nl, const lat_moe_shapes* shapes,
+                                   float* y, void* stream);
 
 /* Options and optional device outputs of lat_moe_expert_forward_ex.  Any
  * pointer may be NULL.  A zero-filled struct asks for no debug output and

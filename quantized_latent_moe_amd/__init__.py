@@ -28,6 +28,7 @@ EXPORTED = (
     "lat_moe_expert_forward",
     "lat_moe_expert_forward_ex",
     "lat_moe_expert_forward_fmt",
+    "lat_moe_expert_forward_noalloc",
     "lat_moe_quantize_q8_1",
     "lat_moe_dense_q8_0",
     "lat_moe_dense_q8_0_debug",
@@ -88,6 +89,8 @@ def lib() -> ctypes.CDLL:
                                                  ctypes.POINTER(Shapes), P, P, ctypes.c_size_t, P,
                                                  ctypes.POINTER(Debug)]
         c.lat_moe_expert_forward_fmt.restype = ctypes.c_int
+        c.lat_moe_expert_forward_noalloc.argtypes = [P, P, P, P, P, ctypes.POINTER(Shapes), P, P]
+        c.lat_moe_expert_forward_noalloc.restype = ctypes.c_int
         c.lat_moe_quantize_q8_1.argtypes = [P, ctypes.c_int64, ctypes.c_int32, P, P]
         c.lat_moe_quantize_q8_1.restype = ctypes.c_int
         i32, i64 = ctypes.c_int32, ctypes.c_int64
@@ -143,6 +146,18 @@ def expert_forward(x_q8_1, router_idx, router_w, gateup_q3k, down_iq4nl, s: Shap
     rc = lib().lat_moe_expert_forward(_ptr(x_q8_1), _ptr(router_idx), _ptr(router_w), _ptr(gateup_q3k),
                                       _ptr(down_iq4nl), ctypes.byref(s), _ptr(y), _ptr(workspace),
                                       workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(rc)
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+ESCRATCH = 5
+
+
+def expert_forward_noalloc(x_q8_1, router_idx, router_w, gateup_q3k, down_iq4nl, s: Shapes, y, stream=None) -> None:
+    """As expert_forward without a workspace: the library's fixed per-GPU
+    scratch (NOALLOC_SCRATCH_BYTES) is used, and nothing is allocated."""
+    rc = lib().lat_moe_expert_forward_noalloc(_ptr(x_q8_1), _ptr(router_idx), _ptr(router_w), _ptr(gateup_q3k),
+                                              _ptr(down_iq4nl), ctypes.byref(s), _ptr(y), _stream(stream))
     _check(rc)
 
 

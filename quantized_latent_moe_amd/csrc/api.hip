@@ -197,6 +197,18 @@ int dense_impl(int wfmt, const void* x_q8_1, const void* w, int64_t T, int32_t N
 
 }  // namespace
 
+namespace latmoe {
+
+int stage_forward(const void* x, const int32_t* idx, const float* w, const void* gu, const void* dn,
+                  const lat_moe_shapes* s, float* y, void* ws, size_t ws_bytes, void* stream) {
+  return forward_impl(x, idx, w, gu, LAT_MOE_GATEUP_Q3_K, dn, LAT_MOE_DOWN_IQ4_NL, s, y, ws, ws_bytes, stream,
+                      nullptr);
+}
+
+int device_check(int* num_cus) { return check_device(num_cus); }
+
+}  // namespace latmoe
+
 extern "C" {
 
 size_t lat_moe_workspace_size(const lat_moe_shapes* shapes) {
@@ -282,6 +294,7 @@ const char* lat_moe_strerror(int code) {
     case LAT_MOE_EWORKSPACE: return "workspace smaller than lat_moe_workspace_size()";
     case LAT_MOE_EDEVICE: return "current device is not a gfx950 with 64-wide wavefronts";
     case LAT_MOE_ELAUNCH: return "kernel launch failed";
+    case LAT_MOE_ESCRATCH: return "shapes need more workspace than the no-allocation entry point's fixed scratch";
     default: return "unknown error";
   }
 }

@@ -182,6 +182,14 @@ __device__ __forceinline__ uint4 buf_u128(rsrc_t r, int voff, int soff) {
   return uint4{v[0], v[1], v[2], v[3]};
 }
 
+// The expert stage (Q3_K gate/up, IQ4_NL down, ordered combine) on a given
+// workspace: lat_moe_expert_forward's checks and launches.
+int stage_forward(const void* x, const int32_t* idx, const float* w, const void* gu, const void* dn,
+                  const lat_moe_shapes* s, float* y, void* ws, size_t ws_bytes, void* stream);
+// LAT_MOE_OK if the current device is a gfx950 with 64-wide wavefronts (and
+// its CU count in *num_cus if not null); cached per device.
+int device_check(int* num_cus);
+
 // Kernel launchers (each returns hipGetLastError() after the enqueue).
 // Sorts pairs by expert and splits the q8_1 activations x into codes and scales.
 // gather: also copy small batches' rows in sorted order for the GEMV-shaped

@@ -111,8 +111,29 @@ def test_argument_errors_before_any_hip_call():
     assert lm.lib().lat_moe_quantize_q8_1(None, 0, 64, None, None) == 0
 
 
+def test_noalloc_argument_errors_before_any_hip_call():
+    """The no-allocation entry point checks its arguments, and the fixed
+    scratch against the shapes' workspace, before any HIP call."""
+    f = lm.lib().lat_moe_expert_forward_noalloc
+    good = [0x10000 * (i + 1) for i in range(6)]  # aligned, never dereferenced on these paths
+    s = lm.shapes(4, 1024, 2048, 128, 8)
+    assert lm.workspace_size(s) <= lm.NOALLOC_SCRATCH_BYTES
+    for i in range(6):
+        p = list(good)
+        p[i] = None
+        assert f(*p[:5], ctypes.byref(s), p[5], None) == 1
+        p[i] = good[i] + 4
+        assert f(*p[:5], ctypes.byref(s), p[5], None) == 1
+    assert f(*good[:5], ctypes.byref(lm.shapes(4, 200, 2048, 128, 8)), good[5], None) == 1
+    big = lm.shapes(5268, 1024, 2048, 128, 8)
+    assert lm.workspace_size(big) > lm.NOALLOC_SCRATCH_BYTES
+    assert f(*good[:5], ctypes.byref(big), good[5], None) == lm.ESCRATCH
+    assert "scratch" in lm.strerror(lm.ESCRATCH)
+    assert f(None, None, None, None, None, ctypes.byref(lm.shapes(0, 1024, 2048, 128, 8)), None, None) == 0
+
+
 def test_strerror():
-    for c in range(5):
+    for c in range(6):
         assert lm.strerror(c)
     assert "unknown" in lm.strerror(99)
 
