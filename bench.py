@@ -334,22 +334,42 @@ class DenseStage:
 COLD_REPS = {"tiny": 50, "decode": 50, "mid_prefill": 50, "prefill_5k": 20, "prefill_21k": 10}
 
 
+class Evictor:
+    """Streams a 1 GiB buffer through the caches by reading it (a sum into
+    one float): larger than the 256 MB last-level cache and the L2s, and it
+    leaves them holding clean lines, so the next call pays no write-back of
+    the eviction's own data inside its timed window."""
+
+    def __init__(self):
+        import torch
+        self.torch = torch
+        self.buf = torch.ones((1 << 30) // 4, dtype=torch.float32, device="cuda")
+        self.out = torch.empty((), dtype=torch.float32, device="cuda")
+
+    def __call__(self):
+        self.torch.sum(self.buf, dim=0, out=self.out)
+
+    def free(self):
+        del self.buf, self.out
+        self.torch.cuda.empty_cache()
+
+
 def decode_cold(st, reps, draws=4):
     """One call at a time with the L2s and the 256 MB last-level cache evicted
-    before each (a 1 GiB buffer written), rotating among `draws` routings of
+    before each (a 1 GiB buffer read), rotating among `draws` routings of
     the workload (the same weights), so no call finds its experts in cache:
     median, p10 and p90 µs, and the algorithmic bytes of each call (its
     active experts' weights, x, routing, y) over its time."""
     import numpy as np
     torch = st.torch
     ds = st.routing_draws(draws)
-    evict = torch.empty((1 << 30) // 4, dtype=torch.float32, device="cuda")
+    evict = Evictor()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     times, gbs = [], []
     for i in range(reps):
         d = ds[i % len(ds)]
         st.use(d)
-        evict.fill_(1.0)
+        evict()
         e0.record()
         st.step()
         e1.record()
@@ -358,8 +378,7 @@ def decode_cold(st, reps, draws=4):
         times.append(us)
         gbs.append(d[3]["bytes"] / (us * 1e-6) / 1e9)
     st.use(ds[0])
-    del evict
-    torch.cuda.empty_cache()
+    evict.free()
     med = float(np.median(times))
     return {"median_us": round(med, 2), "p10_us": round(float(np.percentile(times, 10)), 2),
             "p90_us": round(float(np.percentile(times, 90)), 2), "calls": reps, "routing_draws": len(ds),
@@ -420,12 +439,12 @@ def device_info():
 
 def per_config(names):
     """Every workload timed one call at a time, with the L2s and the 256 MB
-    last-level cache evicted before each call (a 1 GiB buffer written), as the
+    last-level cache evicted before each call (a 1 GiB buffer read), as the
     median, p10 and p90 of the call time; and the back-to-back rate."""
     import numpy as np
     import torch
     from quantized_latent_moe_amd.inputs import WORKLOADS
-    evict = torch.empty((1 << 30) // 4, dtype=torch.float32, device="cuda")
+    evict = Evictor()
     out = {}
     for name in names:
         wl = WORKLOADS[name]
@@ -435,7 +454,7 @@ def per_config(names):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         times = []
         for _ in range(COLD_REPS[name]):
-            evict.fill_(1.0)
+            evict()
             e0.record()
             st.step()
             e1.record()
@@ -454,8 +473,7 @@ def per_config(names):
               f"p90 {out[name]['cold_us']['p90']}), back-to-back {warm_ms * 1e3:.1f} us", file=sys.stderr, flush=True)
         del st
         torch.cuda.empty_cache()
-    del evict
-    torch.cuda.empty_cache()
+    evict.free()
     return out
 
 
@@ -653,6 +671,8 @@ def main():
     ap.add_argument("--no-formats", action="store_true", help="skip the Q4_0 weight timings")
     ap.add_argument("--no-combine", action="store_true",
                     help="skip the slot-buffer vs atomic-add combine comparison at prefill_5k and prefill_21k")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="time only the decode workload (cold, rotating routings; and back to back) and print it")
     ap.add_argument("--formats-only", action="store_true",
                     help="time only the stage with Q4_0 gate/up and down weights, at --workload")
     ap.add_argument("--cpu-seconds", type=float, default=18.0, help="CPU oracle time over its 3 runs")
@@ -696,6 +716,15 @@ def main():
         return
     if args.formats_only:
         print(json.dumps(q4_0_report(args.steps, args.warmup, gateup_q4_0=True, workloads=(wl.name,))), flush=True)
+        return
+    if args.decode_only:
+        ds = Stage(WORKLOADS["decode"])
+        ds.prime()
+        dms, _ = ds.time_steps(max(args.steps, 50), args.warmup)
+        cold = decode_cold(ds, max(args.steps, 50))
+        print(f"[bench] decode cold {cold['median_us']:.2f} us/step ({cold['hbm_gbs_median']:.0f} GB/s), "
+              f"back to back {dms * 1e3:.2f} us/step", file=sys.stderr, flush=True)
+        print(json.dumps({"workload": "decode", "cold": cold, "warm_us_per_step": round(dms * 1e3, 2)}), flush=True)
         return
     st = Stage(wl)
     st.prime()

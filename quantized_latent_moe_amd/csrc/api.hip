@@ -30,7 +30,7 @@ bool shapes_ok(const lat_moe_shapes* s) {
 }
 
 struct Layout {
-  size_t chunk_hist, chunk_bad, offsets, misc, tiles, perm, h_codes, h_ds, slots, xc, xd, xg, xgd, total;
+  size_t chunk_hist, chunk_bad, offsets, misc, tiles, perm, h_codes, h_ds, slots, xc, xd, total;
   int nchunk, max_tiles;
 };
 
@@ -51,8 +51,6 @@ Layout layout(const lat_moe_shapes* s) {
   L.slots = o;      o = align_up(o + sizeof(float) * (size_t)P * s->L);
   L.xc = o;         o = align_up(o + (size_t)s->T * s->L);
   L.xd = o;         o = align_up(o + sizeof(float) * (size_t)s->T * (s->L / 32));
-  L.xg = o;         o = align_up(o + (size_t)kGatherRows * s->L);
-  L.xgd = o;        o = align_up(o + sizeof(float) * (size_t)kGatherRows * (s->L / 32));
   L.total = o;
   return L;
 }
@@ -71,8 +69,6 @@ Work carve(const Layout& L, void* ws) {
   w.slots = reinterpret_cast<float*>(b + L.slots);
   w.xc = reinterpret_cast<int8_t*>(b + L.xc);
   w.xd = reinterpret_cast<float*>(b + L.xd);
-  w.xg = reinterpret_cast<int8_t*>(b + L.xg);
-  w.xgd = reinterpret_cast<float*>(b + L.xgd);
   w.nchunk = L.nchunk;
   w.max_tiles = L.max_tiles;
   w.num_cus = 1;
@@ -136,31 +132,45 @@ int forward_impl(const void* x, const int32_t* idx, const float* w, const void* 
   hipEvent_t const* ev = (dbg && dbg->stage_events) ? reinterpret_cast<hipEvent_t const*>(dbg->stage_events) : nullptr;
   auto mark = [&](int i) { return ev ? hipEventRecord(ev[i], st) : hipSuccess; };
   if (mark(0) != hipSuccess) return LAT_MOE_ELAUNCH;
-  const bool small = small_path(sh);  // decode-sized batch: GEMV-shaped kernels (either weight format)
-  // atomic combine: the route pass zeroes y, down adds into it, no combine kernel
-  const bool atomic = !deterministic && !small;
-  if (launch_route(idx, xb, sh, wk, small, atomic ? y : nullptr, st) != hipSuccess) return LAT_MOE_ELAUNCH;
-  if (mark(1) != hipSuccess) return LAT_MOE_ELAUNCH;
+  const bool small = decode_path(sh);  // decode-sized batch: two launches on the routing as given
   ProbeRows pg{nullptr, 0, 0}, pd{nullptr, 0, 0};
   if (dbg && dbg->gateup_i32) pg = ProbeRows{dbg->gateup_i32, dbg->gu_row0, dbg->gu_rows};
   if (dbg && dbg->down_i32) pd = ProbeRows{dbg->down_i32, dbg->dn_row0, dbg->dn_rows};
   const uint8_t* gub = static_cast<const uint8_t*>(gu);
   const uint8_t* dnb = static_cast<const uint8_t*>(dn);
-  if ((small                          ? launch_gateup_small(sh, wk, gub, gu_fmt, pg.out ? &pg : nullptr, st)
-       : gu_fmt == LAT_MOE_GATEUP_Q4_0 ? launch_gateup_q40(sh, wk, gub, pg.out ? &pg : nullptr, st)
-                                       : launch_gateup(sh, wk, gub, pg.out ? &pg : nullptr, st)) != hipSuccess)
-    return LAT_MOE_ELAUNCH;
-  if (mark(2) != hipSuccess) return LAT_MOE_ELAUNCH;
   const int fmt = down_fmt == LAT_MOE_DOWN_Q4_0 ? kDownQ40 : kDownIq4Nl;
-  if ((small ? launch_down_small(dnb, fmt, w, sh, wk, pd.out ? &pd : nullptr, st)
-             : launch_down(dnb, fmt, w, sh, wk, atomic ? y : nullptr, pd.out ? &pd : nullptr, st)) != hipSuccess)
-    return LAT_MOE_ELAUNCH;
-  if (mark(3) != hipSuccess) return LAT_MOE_ELAUNCH;
-  if (!atomic && launch_combine(idx, sh, wk, y, st) != hipSuccess) return LAT_MOE_ELAUNCH;
-  if (mark(4) != hipSuccess) return LAT_MOE_ELAUNCH;
-  if (dbg) {
-    if (dbg->h_q8_1 && launch_export_h(sh, wk, static_cast<uint8_t*>(dbg->h_q8_1), st) != hipSuccess)
+  if (small) {
+    // The sort runs only when its outputs are asked for (debug): the decode
+    // kernels group the pairs themselves.
+    if (dbg && (dbg->perm || dbg->offsets || dbg->dropped) &&
+        launch_route(idx, xb, sh, wk, nullptr, st) != hipSuccess)
       return LAT_MOE_ELAUNCH;
+    if (mark(1) != hipSuccess) return LAT_MOE_ELAUNCH;
+    if (launch_decode(sh, wk, xb, idx, w, gub, gu_fmt, dnb, fmt, y, pg.out ? &pg : nullptr, pd.out ? &pd : nullptr,
+                      st, ev ? ev[2] : nullptr) != hipSuccess)
+      return LAT_MOE_ELAUNCH;
+    if (mark(3) != hipSuccess || mark(4) != hipSuccess) return LAT_MOE_ELAUNCH;
+    if (dbg && dbg->h_q8_1 &&
+        launch_export_h_pairs(idx, sh, wk, static_cast<uint8_t*>(dbg->h_q8_1), st) != hipSuccess)
+      return LAT_MOE_ELAUNCH;
+  } else {
+    // atomic combine: the route pass zeroes y, down adds into it, no combine kernel
+    const bool atomic = !deterministic;
+    if (launch_route(idx, xb, sh, wk, atomic ? y : nullptr, st) != hipSuccess) return LAT_MOE_ELAUNCH;
+    if (mark(1) != hipSuccess) return LAT_MOE_ELAUNCH;
+    if ((gu_fmt == LAT_MOE_GATEUP_Q4_0 ? launch_gateup_q40(sh, wk, gub, pg.out ? &pg : nullptr, st)
+                                       : launch_gateup(sh, wk, gub, pg.out ? &pg : nullptr, st)) != hipSuccess)
+      return LAT_MOE_ELAUNCH;
+    if (mark(2) != hipSuccess) return LAT_MOE_ELAUNCH;
+    if (launch_down(dnb, fmt, w, sh, wk, atomic ? y : nullptr, pd.out ? &pd : nullptr, st) != hipSuccess)
+      return LAT_MOE_ELAUNCH;
+    if (mark(3) != hipSuccess) return LAT_MOE_ELAUNCH;
+    if (!atomic && launch_combine(idx, sh, wk, y, st) != hipSuccess) return LAT_MOE_ELAUNCH;
+    if (mark(4) != hipSuccess) return LAT_MOE_ELAUNCH;
+    if (dbg && dbg->h_q8_1 && launch_export_h(sh, wk, static_cast<uint8_t*>(dbg->h_q8_1), st) != hipSuccess)
+      return LAT_MOE_ELAUNCH;
+  }
+  if (dbg) {
     if (dbg->perm && launch_copy_i32(wk.perm, dbg->perm, sh.pairs(), st) != hipSuccess) return LAT_MOE_ELAUNCH;
     if (dbg->offsets && launch_copy_i32(wk.offsets, dbg->offsets, s->E + 1, st) != hipSuccess) return LAT_MOE_ELAUNCH;
     if (dbg->dropped && launch_copy_i32(wk.misc + kMiscDropped, dbg->dropped, 1, st) != hipSuccess)

@@ -1,0 +1,531 @@
+// Gate/up and down for decode-sized batches: two launches that read the
+// routing directly (no sort, no gather, no combine kernel).
+//
+// Same computation as the grouped GEMMs (page "Run Edge0-145B Q3_K on AMD HIP
+// (Linux, gfx1100) #1", section "Contents": gate/up on Q3_K with SwiGLU and
+// the q8_1 rounding of H, down on IQ4_NL), for batches of at most
+// kDecodeMaxPairs routed pairs with L <= 1024 and F <= 2048, where each
+// active expert holds a handful of tokens and the stage is the stream of the
+// active experts' weights: every byte of them should be in flight as soon as
+// the routing is known.
+//
+// Gate/up, workgroup (pair slot p, 32 features f0..): each wave loads all
+// router ids at once (one load, a lane per pair), so the workgroup knows its
+// expert e = idx[p] and whether p is the first slot routed to e; only the
+// first one works, for every pair of e (a ballot gives them, in pair order).
+// Its 256 threads then issue the loads of the expert's 64 weight rows (gate
+// f0.., up F+f0..; a thread takes one 110-byte super-block of one row, or
+// eight Q4_0 blocks, straight into registers) together with the pairs'
+// q8_1 activation rows (into LDS).  H is written in pair order.
+//
+// Q3_K dots: the int8 operand is 7 - c = 3 - v (v = c - 4 the weight value),
+// formed from the bitwise complements of qs and hmask: (~qs >> 2j) & 3 is
+// 3 - low2 and bit (4n + j) of ~hmask is 1 - hbit.  With the
+// per-16 sums of x, sigma * sum v x = sigma * (3 sum x - sum (7 - c) x), the
+// scale-folded 32-value block dot I32 of the large kernels; then
+// acc_sb += d_x * I32 per block and acc += d_w * acc_sb per super-block.
+// Q4_0 gate/up: I32 = sum nibble * x - 8 sum x, acc += d_w * fl(d_x * I32).
+// The 32 features are one q8_1 block of H, so SwiGLU and the requant finish
+// inside a half wave.
+//
+// Down, workgroup (token t, 8 output rows l0..): its 512 threads are (slot
+// j, row, K slice of 8 blocks); per pass of 8 slots each thread loads the
+// 144 contiguous bytes of its row's slice for expert idx[t][j] (8 threads
+// cover a whole 1152-byte row) while the token's H rows (pair order, no
+// dependence on the routing) go to LDS; block dots J32 by v_dot4 against the
+// table-expanded indices, acc += fl(d_dn * d_H) * J32, a sum over the 8
+// slices, and y[t][l] = sum over j of w[t][j] * O_j taken in slot order: the
+// combine happens here, deterministically.
+#include <type_traits>
+
+#include "lat_moe_internal.h"
+
+namespace latmoe {
+namespace {
+
+constexpr int kTok = 2;                 // tokens per pass of the gate/up kernel (an expert holds 1-2 at decode)
+constexpr int kGuThreads = 256;         // 64 weight rows x 4 K slices
+constexpr int kDnRows = 8;              // output rows per down workgroup
+constexpr int kDnSlots = 8;             // pairs of the token per pass of the down kernel
+constexpr int kDnSlices = 8;            // K slices of 8 blocks (F <= 2048)
+constexpr int kDnThreads = kDnRows * kDnSlots * kDnSlices;  // 512
+constexpr int kDnMaxK = kDecodeMaxPairs;  // experts per token (T >= 1)
+static_assert(kDnThreads == 512 && kDecodeMaxPairs <= 64, "one lane per pair in a wave");
+
+// Router ids of the batch in the lanes of the calling wave: lane p < P holds
+// router_idx[p], the others -1 (one buffer load, no branch around it).
+__device__ __forceinline__ int load_ids(const int32_t* __restrict__ idx, int P) {
+  const int lane = threadIdx.x & 63;
+  const rsrc_t r = make_rsrc(idx, (uint32_t)P * 4u);
+  const int v = (int)buf_u32(r, lane < P ? lane * 4 : kOutOfRange, 0);
+  return lane < P ? v : -1;
+}
+
+// (x >> s) moved so that bit s of every byte lands on bit 2, other bits 0.
+template <int S>
+__device__ __forceinline__ uint32_t bit_to_2(uint32_t x) {
+  if constexpr (S >= 2)
+    return (x >> (S - 2)) & 0x04040404u;
+  else
+    return (x << (2 - S)) & 0x04040404u;
+}
+
+// ---------------------------------------------------------------------------
+template <bool PROBE, int GFMT>
+__global__ __launch_bounds__(kGuThreads, 4) void k_dec_gateup(const uint8_t* __restrict__ x, const int32_t* __restrict__ idx,
+                                                         const uint8_t* __restrict__ gu, int T, int P, int k, int L,
+                                                         int F, int E, int8_t* __restrict__ h_codes,
+                                                         uint32_t* __restrict__ h_ds, ProbeRows probe) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int p = blockIdx.x;
+  const int f0 = blockIdx.y * 32;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int ids = load_ids(idx, P);
+  const int e = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_readlane(ids, p));
+  if ((unsigned)e >= (unsigned)E) return;
+  const uint64_t same = __ballot(ids == e);  // the pairs routed to e (lanes >= P hold -1)
+  if (same & ((1ull << p) - 1)) return;      // an earlier slot has this expert
+  const int cnt = __popcll(same);
+
+  constexpr bool kQ40 = GFMT == LAT_MOE_GATEUP_Q4_0;
+  const int nsb = L / 256, nxb = L / 32, nsub = L / 16, nfb = F / 32;
+  const int row_bytes = nsb * (kQ40 ? 8 * kQ40Bytes : kQ3kBytes);
+  const int r = tid >> 2, q = tid & 3;
+  const int wrow = r < 32 ? f0 + r : F + f0 + r - 32;  // weight row of the expert
+  const rsrc_t rw = make_rsrc(gu + (int64_t)e * 2 * F * row_bytes, (uint32_t)(2 * F * row_bytes));
+  // This thread's K slice straight into registers: one super-block (bytes
+  // 0..107 as six 16-byte pieces and a 12-byte tail, d as a 16-bit load; buffer
+  // loads at 2-byte-aligned offsets return the bytes there), or 8 Q4_0 blocks
+  // (144 bytes, nine 16-byte loads).  Adjacent threads read adjacent slices.
+  uint32_t blk[kQ40 ? 36 : 28];
+  if constexpr (kQ40) {
+    const int boff = q < nsb ? wrow * row_bytes + q * 8 * kQ40Bytes : kOutOfRange;
+#pragma unroll
+    for (int c = 0; c < 9; ++c) {
+      const uint4 v = buf_u128(rw, boff, 16 * c);
+      blk[4 * c] = v.x, blk[4 * c + 1] = v.y, blk[4 * c + 2] = v.z, blk[4 * c + 3] = v.w;
+    }
+  } else {
+    const int boff = q < nsb ? wrow * row_bytes + q * kQ3kBytes : kOutOfRange;
+#pragma unroll
+    for (int c = 0; c < 6; ++c) {
+      const uint4 v = buf_u128(rw, boff, 16 * c);
+      blk[4 * c] = v.x, blk[4 * c + 1] = v.y, blk[4 * c + 2] = v.z, blk[4 * c + 3] = v.w;
+    }
+    const auto t3 = __builtin_amdgcn_raw_buffer_load_b96(rw, boff, 96, 0);
+    blk[24] = t3[0], blk[25] = t3[1], blk[26] = t3[2];
+    blk[27] = buf_u16(rw, boff, 108);
+  }
+  // LDS: xs[kTok][L] | xds[kTok][nxb] | xsum[kTok][nsub] | gus[64][kTok]
+  int8_t* xs = reinterpret_cast<int8_t*>(smem);
+  float* xds = reinterpret_cast<float*>(xs + kTok * L);
+  int* xsum = reinterpret_cast<int*>(xds + kTok * nxb);
+  float* gus = reinterpret_cast<float*>(xsum + kTok * nsub);
+  const rsrc_t rx = make_rsrc(x, (uint32_t)(T * nxb * kQ81Bytes));
+
+  // The pass's activation rows: thread (token tk, q8_1 block b) loads one
+  // block.  The first pass's loads are issued right behind the weight loads,
+  // so the two are in flight together.
+  uint64_t rest = same;  // pairs not yet loaded, lowest first
+  int pr[kTok];          // the pass's pairs (uniform), -1 past the end
+  const int tk = tid / nxb, b = tid - tk * nxb;
+  uint32_t dv;
+  uint4 xlo, xhi;
+  auto load_pass = [&]() {
+#pragma unroll
+    for (int i = 0; i < kTok; ++i) {
+      pr[i] = rest ? (int)__builtin_ctzll(rest) : -1;
+      if (rest) rest &= rest - 1;
+    }
+    // the pass's tokens as uniform values, then this thread's one
+    int tok = pr[0] >= 0 ? __builtin_amdgcn_readfirstlane(pr[0] / k) : -1;
+#pragma unroll
+    for (int i = 1; i < kTok; ++i) {
+      const int ti = pr[i] >= 0 ? __builtin_amdgcn_readfirstlane(pr[i] / k) : -1;
+      if (tk == i) tok = ti;
+    }
+    const int xoff = tid < kTok * nxb && tok >= 0 ? (int)__umul24((unsigned)__umul24(tok, nxb) + b, kQ81Bytes)
+                                                   : kOutOfRange;
+    dv = buf_u32(rx, xoff, 0);
+    xlo = buf_u128(rx, xoff, 4);
+    xhi = buf_u128(rx, xoff, 20);
+  };
+  load_pass();
+  for (int g0 = 0; g0 < cnt; g0 += kTok) {
+    const int nt = min(kTok, cnt - g0);
+    if (g0 > 0) {
+      __syncthreads();  // the previous pass's reads of xs / gus are done
+      load_pass();
+    }
+    if (tid < kTok * nxb) {
+      uint4* dst = reinterpret_cast<uint4*>(xs + tk * L + 32 * b);
+      dst[0] = xlo;
+      dst[1] = xhi;
+      xds[tk * nxb + b] = half_bits_to_float(dv & 0xffffu);
+      int s0 = __builtin_amdgcn_sdot4((int)xlo.x, 0x01010101, 0, false);
+      s0 = __builtin_amdgcn_sdot4((int)xlo.y, 0x01010101, s0, false);
+      s0 = __builtin_amdgcn_sdot4((int)xlo.z, 0x01010101, s0, false);
+      s0 = __builtin_amdgcn_sdot4((int)xlo.w, 0x01010101, s0, false);
+      int s1 = __builtin_amdgcn_sdot4((int)xhi.x, 0x01010101, 0, false);
+      s1 = __builtin_amdgcn_sdot4((int)xhi.y, 0x01010101, s1, false);
+      s1 = __builtin_amdgcn_sdot4((int)xhi.z, 0x01010101, s1, false);
+      s1 = __builtin_amdgcn_sdot4((int)xhi.w, 0x01010101, s1, false);
+      xsum[tk * nsub + 2 * b] = s0;  // sum of the 16 codes of each half
+      xsum[tk * nsub + 2 * b + 1] = s1;
+    }
+    __syncthreads();
+    // The weight words are re-read each pass (an empty asm marks them as
+    // changed), so the unpack below stays inside the pass, one block at a
+    // time, instead of being hoisted whole in front of the loop.
+#pragma unroll
+    for (int w = 0; w < (kQ40 ? 36 : 28); ++w) asm volatile("" : "+v"(blk[w]));
+
+    float acc[kTok];
+#pragma unroll
+    for (int t = 0; t < kTok; ++t) acc[t] = 0.f;
+    // The pass's dots for NT tokens (a compile-time count: no branch inside
+    // the blocks, so each block's operands die with it).
+    auto dots = [&](auto nt_tag) {
+      constexpr int NT = decltype(nt_tag)::value;
+      if (kQ40 && q < nsb) {
+        const int sb = q;
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb) {
+          // block kb at byte 18 kb of the slice: d, then 16 nibble bytes
+          const int base = 18 * kb, wi = base >> 2;
+          uint32_t nw[4], d16;
+          if ((base & 3) == 0) {
+            d16 = blk[wi] & 0xffffu;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) nw[w] = __builtin_amdgcn_alignbyte(blk[wi + w + 1], blk[wi + w], 2);
+          } else {
+            d16 = blk[wi] >> 16;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) nw[w] = blk[wi + 1 + w];
+          }
+          const float dwb = half_bits_to_float(d16);
+          uint32_t lo[4], hi[4];  // values 0..15 (low nibbles) and 16..31 (high nibbles)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            lo[w] = nw[w] & 0x0f0f0f0fu;
+            hi[w] = (nw[w] >> 4) & 0x0f0f0f0fu;
+          }
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            const uint4* xp = reinterpret_cast<const uint4*>(xs + t * L + sb * 256 + 32 * kb);
+            const uint4 x0 = xp[0], x1 = xp[1];
+            int dn = __builtin_amdgcn_sdot4((int)lo[0], (int)x0.x, 0, false);
+            dn = __builtin_amdgcn_sdot4((int)lo[1], (int)x0.y, dn, false);
+            dn = __builtin_amdgcn_sdot4((int)lo[2], (int)x0.z, dn, false);
+            dn = __builtin_amdgcn_sdot4((int)lo[3], (int)x0.w, dn, false);
+            dn = __builtin_amdgcn_sdot4((int)hi[0], (int)x1.x, dn, false);
+            dn = __builtin_amdgcn_sdot4((int)hi[1], (int)x1.y, dn, false);
+            dn = __builtin_amdgcn_sdot4((int)hi[2], (int)x1.z, dn, false);
+            dn = __builtin_amdgcn_sdot4((int)hi[3], (int)x1.w, dn, false);
+            const int2 sx = *reinterpret_cast<const int2*>(&xsum[t * nsub + sb * 16 + 2 * kb]);
+            const int I = dn - 8 * (sx.x + sx.y);  // sum (nibble - 8) x
+            const float tt = xds[t * nxb + sb * 8 + kb] * (float)I;
+            acc[t] = __builtin_fmaf(dwb, tt, acc[t]);
+            if (PROBE) {
+              const int rr = wrow - probe.row0;
+              if (rr >= 0 && rr < probe.rows) probe.out[((int64_t)pr[t] * probe.rows + rr) * nxb + sb * 8 + kb] = I;
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      if (!kQ40 && q < nsb) {
+        const int sb = q;
+        const float dw = half_bits_to_float(blk[27] & 0xffffu);
+        // 6-bit sub-block scales as bytes (s = 0..15), bit 5 flipped so that a
+        // signed 6-bit field extract gives sigma = sc6 - 32
+        const uint32_t c0 = blk[24], c1 = blk[25], c2 = blk[26];
+        const uint32_t xsc[4] = {((c0 & 0x0f0f0f0fu) | ((c2 << 4) & 0x30303030u)) ^ 0x20202020u,
+                                 ((c1 & 0x0f0f0f0fu) | ((c2 << 2) & 0x30303030u)) ^ 0x20202020u,
+                                 (((c0 >> 4) & 0x0f0f0f0fu) | (c2 & 0x30303030u)) ^ 0x20202020u,
+                                 (((c1 >> 4) & 0x0f0f0f0fu) | ((c2 >> 2) & 0x30303030u)) ^ 0x20202020u};
+        float asb[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) asb[t] = 0.f;
+        auto block = [&](auto kb_tag) {
+          constexpr int kb = decltype(kb_tag)::value;
+          constexpr int n = kb >> 2, j = kb & 3;
+          const int sg0 = __builtin_amdgcn_sbfe((int)xsc[(2 * kb) >> 2], 8 * ((2 * kb) & 3), 6);
+          const int sg1 = __builtin_amdgcn_sbfe((int)xsc[(2 * kb + 1) >> 2], 8 * ((2 * kb + 1) & 3), 6);
+          uint32_t op[8];  // 7 - c per byte, elements 32 kb + 4w ..
+#pragma unroll
+          for (int w = 0; w < 8; ++w)
+            op[w] = ((~blk[8 + 8 * n + w] >> (2 * j)) & 0x03030303u) | bit_to_2<4 * n + j>(~blk[w]);
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            const uint4* xp = reinterpret_cast<const uint4*>(xs + t * L + sb * 256 + 32 * kb);
+            const uint4 x0 = xp[0], x1 = xp[1];
+            int da = __builtin_amdgcn_sdot4((int)op[0], (int)x0.x, 0, false);
+            da = __builtin_amdgcn_sdot4((int)op[1], (int)x0.y, da, false);
+            da = __builtin_amdgcn_sdot4((int)op[2], (int)x0.z, da, false);
+            da = __builtin_amdgcn_sdot4((int)op[3], (int)x0.w, da, false);
+            int db = __builtin_amdgcn_sdot4((int)op[4], (int)x1.x, 0, false);
+            db = __builtin_amdgcn_sdot4((int)op[5], (int)x1.y, db, false);
+            db = __builtin_amdgcn_sdot4((int)op[6], (int)x1.z, db, false);
+            db = __builtin_amdgcn_sdot4((int)op[7], (int)x1.w, db, false);
+            const int2 sx = *reinterpret_cast<const int2*>(&xsum[t * nsub + sb * 16 + 2 * kb]);
+            // I32 = sum over the block of sigma * v * x, with v * x = 3x - (7 - c) x
+            const int I = sg0 * (3 * sx.x - da) + sg1 * (3 * sx.y - db);
+            asb[t] = __builtin_fmaf(xds[t * nxb + sb * 8 + kb], (float)I, asb[t]);
+            if (PROBE) {
+              const int rr = wrow - probe.row0;
+              if (rr >= 0 && rr < probe.rows) probe.out[((int64_t)pr[t] * probe.rows + rr) * nxb + sb * 8 + kb] = I;
+            }
+          }
+          // one block's operands live at a time
+          __builtin_amdgcn_sched_barrier(0);
+        };
+        block(std::integral_constant<int, 0>{});
+        block(std::integral_constant<int, 1>{});
+        block(std::integral_constant<int, 2>{});
+        block(std::integral_constant<int, 3>{});
+        block(std::integral_constant<int, 4>{});
+        block(std::integral_constant<int, 5>{});
+        block(std::integral_constant<int, 6>{});
+        block(std::integral_constant<int, 7>{});
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t] = __builtin_fmaf(dw, asb[t], acc[t]);
+      }
+    };
+    static_assert(kTok == 2, "passes of one or two tokens");
+    if (nt == 1)
+      dots(std::integral_constant<int, 1>{});
+    else
+      dots(std::integral_constant<int, 2>{});
+    // sum the row's 4 K slices (lanes 4r .. 4r+3)
+#pragma unroll
+    for (int t = 0; t < kTok; ++t) {
+      acc[t] += __shfl_xor(acc[t], 1);
+      acc[t] += __shfl_xor(acc[t], 2);
+    }
+    if (q == 0) {
+#pragma unroll
+      for (int t = 0; t < kTok; ++t) gus[r * kTok + t] = acc[t];
+    }
+    __syncthreads();
+    // ---- SwiGLU + q8_1 of H: half wave h of the workgroup takes token h
+    for (int t = tid >> 5; t < nt; t += kGuThreads / 32) {
+      // The q8_1 rule rounds every product to fp32 on its own.
+#pragma clang fp contract(off)
+      const int f = lane & 31;
+      const float gv = gus[f * kTok + t], uv = gus[(32 + f) * kTok + t];
+      const float sig = __builtin_amdgcn_rcpf(1.0f + __expf(-gv));
+      const float h = gv * sig * uv;
+      float amax = fabsf(h);
+#pragma unroll
+      for (int o = 16; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 32));
+      const float d = amax / 127.0f;
+      const float id = d != 0.0f ? 1.0f / d : 0.0f;
+      const int qv = round_half_away(h * id);
+      int sum = qv;
+#pragma unroll
+      for (int o = 16; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 32);
+      int pt = pr[0];
+#pragma unroll
+      for (int i = 1; i < kTok; ++i)
+        if (t == i) pt = pr[i];
+      h_codes[(int64_t)pt * F + f0 + f] = (int8_t)qv;
+      if (f == 0)
+        h_ds[(int64_t)pt * nfb + f0 / 32] =
+            float_to_half_bits(d) | (float_to_half_bits(fp32_barrier(d * (float)sum)) << 16);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// WHOLE: F % 256 == 0, so every slice is 8 whole blocks (144 bytes) inside
+// its row, loaded as nine 16-byte pieces; otherwise each block is loaded on
+// its own (d, then the 16 index bytes), so no load reaches past its row (a
+// load partly past the end of the buffer would come back zero).
+template <bool PROBE, int FMT, bool WHOLE>
+__global__ __launch_bounds__(kDnThreads) void k_dec_down(const uint8_t* __restrict__ dn, const int32_t* __restrict__ idx,
+                                                       const float* __restrict__ router_w, int P, int k, int L, int F,
+                                                       int E, const int8_t* __restrict__ h_codes,
+                                                       const uint32_t* __restrict__ h_ds, float* __restrict__ y,
+                                                       ProbeRows probe) {
+  __shared__ __align__(16) int8_t hs[kDnSlots][2048];  // the pass's H codes (F <= 2048)
+  __shared__ float hds[kDnSlots][64];                   // and their fp32 d_H
+  __shared__ float osum[kDnMaxK][kDnRows];              // O of each slot and row
+  const int t = blockIdx.x, l0 = blockIdx.y * kDnRows;
+  const int tid = threadIdx.x;
+  const int slice = tid & 7, row = (tid >> 3) & 7, slot = tid >> 6;  // a wave = one slot's 8 rows
+  const int nfb = F / 32, row_bytes = nfb * kIq4Bytes;
+  const int l = l0 + row;
+  const rsrc_t rh = make_rsrc(h_codes, (uint32_t)(P * F));
+  const rsrc_t rs = make_rsrc(h_ds, (uint32_t)(P * nfb * 4));
+  const rsrc_t ri = make_rsrc(idx, (uint32_t)P * 4u);
+
+  for (int j0 = 0; j0 < k; j0 += kDnSlots) {
+    const int j = j0 + slot;
+    const int pair = t * k + j;  // uniform per wave
+    // this slot's expert (one load per wave, uniform)
+    const int e = __builtin_amdgcn_readfirstlane((int)buf_u32(ri, j < k ? pair * 4 : kOutOfRange, 0));
+    const bool valid = j < k && (unsigned)e < (unsigned)E;
+    // H of the pass's pairs, pair order (independent of the routing): codes
+    // as 16-byte pieces i = tid, tid + 512 of 8 x 128, scales one per thread
+    uint4 hv[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int i = tid + kDnThreads * m, s = i >> 7, c = i & 127;
+      const bool ok = j0 + s < k && 16 * c < F;
+      hv[m] = buf_u128(rh, ok ? (t * k + j0 + s) * F + 16 * c : kOutOfRange, 0);
+    }
+    const int ds_s = tid >> 6, ds_b = tid & 63;
+    const uint32_t dv = buf_u32(rs, (j0 + ds_s < k && ds_b < nfb) ? ((t * k + j0 + ds_s) * nfb + ds_b) * 4 : kOutOfRange,
+                                0);
+    // this thread's slice: bytes 144 slice .. +143 of row l of expert e
+    const rsrc_t rw = make_rsrc(dn + (int64_t)(valid ? e : 0) * L * row_bytes, (uint32_t)(L * row_bytes));
+    const int woff = valid && 8 * slice < nfb ? l * row_bytes + 144 * slice : kOutOfRange;
+    uint32_t wb[36];
+    if constexpr (WHOLE) {
+#pragma unroll
+      for (int c = 0; c < 9; ++c) {
+        const uint4 v = buf_u128(rw, woff, 16 * c);
+        wb[4 * c] = v.x, wb[4 * c + 1] = v.y, wb[4 * c + 2] = v.z, wb[4 * c + 3] = v.w;
+      }
+    } else {
+      // block m: d into the 16-bit half at byte 18 m, indices at 18 m + 2 (the
+      // layout of the 144-byte piece, as the unpack below reads it)
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const int bo = 8 * slice + m < nfb ? woff + 18 * m : kOutOfRange;
+        const uint32_t d16 = buf_u16(rw, bo, 0);
+        const uint4 v = buf_u128(rw, bo, 2);
+        const int wi = (18 * m) >> 2;
+        if ((18 * m) & 3) {  // d in the high half of word wi (its low half: block m - 1's last two
+                             // index bytes), indices from word wi + 1 on
+          wb[wi] |= d16 << 16;
+          wb[wi + 1] = v.x, wb[wi + 2] = v.y, wb[wi + 3] = v.z, wb[wi + 4] = v.w;
+        } else {  // d in the low half of word wi, indices from byte 2 of it
+          wb[wi] = d16 | (v.x << 16);
+          wb[wi + 1] = (v.x >> 16) | (v.y << 16);
+          wb[wi + 2] = (v.y >> 16) | (v.z << 16);
+          wb[wi + 3] = (v.z >> 16) | (v.w << 16);
+          wb[wi + 4] = v.w >> 16;
+        }
+      }
+    }
+    if (j0 > 0) __syncthreads();  // the previous pass's reads of hs / hds are done
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int i = tid + kDnThreads * m;
+      *reinterpret_cast<uint4*>(&hs[i >> 7][16 * (i & 127)]) = hv[m];
+    }
+    hds[ds_s][ds_b] = half_bits_to_float(dv & 0xffffu);
+    __syncthreads();
+
+    float acc = 0.f;
+    if (valid) {
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const int b = 8 * slice + m;
+        if (b < nfb) {
+          // block m at byte 18 m of the slice: d, then 16 index bytes
+          const int base = 18 * m, wi = base >> 2;
+          uint32_t nw[4], d16;
+          if ((base & 3) == 0) {
+            d16 = wb[wi] & 0xffffu;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) nw[w] = __builtin_amdgcn_alignbyte(wb[wi + w + 1], wb[wi + w], 2);
+          } else {
+            d16 = wb[wi] >> 16;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) nw[w] = wb[wi + 1 + w];
+          }
+          const uint4* hp = reinterpret_cast<const uint4*>(&hs[slot][32 * b]);
+          const uint4 h0 = hp[0], h1 = hp[1];
+          const uint32_t hw[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+          int J = 0;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            J = __builtin_amdgcn_sdot4((int)down_lookup<FMT>(nw[w] & 0x0f0f0f0fu), (int)hw[w], J, false);
+            J = __builtin_amdgcn_sdot4((int)down_lookup<FMT>((nw[w] >> 4) & 0x0f0f0f0fu), (int)hw[4 + w], J, false);
+          }
+          acc = __builtin_fmaf(half_bits_to_float(d16) * hds[slot][b], (float)J, acc);
+          if (PROBE) {
+            const int rr = l - probe.row0;
+            if (rr >= 0 && rr < probe.rows) probe.out[((int64_t)pair * probe.rows + rr) * nfb + b] = J;
+          }
+        }
+      }
+    }
+    // sum the row's 8 slices (lanes 8 row .. 8 row + 7 of the wave)
+    acc += __shfl_xor(acc, 1);
+    acc += __shfl_xor(acc, 2);
+    acc += __shfl_xor(acc, 4);
+    if (slice == 0 && j < k) osum[j][row] = valid ? acc : 0.f;
+  }
+  __syncthreads();
+  // combine: y[t][l] = sum over the slots, in order, of w[t][j] * O_j[l]
+  if (tid < kDnRows) {
+    float v = 0.f;
+    for (int j = 0; j < k; ++j) v = __builtin_fmaf(router_w[t * k + j], osum[j][tid], v);
+    y[(int64_t)t * L + l0 + tid] = v;
+  }
+}
+
+// H of pair p in ggml q8_1 blocks (pairs with an invalid id: zero blocks).
+__global__ __launch_bounds__(256) void k_export_h_pairs(const int32_t* __restrict__ idx, int E, int64_t nblocks, int nfb,
+                                                       const int8_t* __restrict__ h_codes,
+                                                       const uint32_t* __restrict__ h_ds, uint8_t* __restrict__ h_out) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;  // one q8_1 block
+  if (q >= nblocks) return;
+  const int64_t p = q / nfb;
+  const int e = idx[p];
+  uint32_t* dst = reinterpret_cast<uint32_t*>(h_out + q * kQ81Bytes);
+  const bool ok = (unsigned)e < (unsigned)E;
+  const uint32_t* src = reinterpret_cast<const uint32_t*>(h_codes + q * 32);
+  dst[0] = ok ? h_ds[q] : 0u;
+#pragma unroll
+  for (int w = 0; w < 8; ++w) dst[1 + w] = ok ? src[w] : 0u;
+}
+
+}  // namespace
+
+bool decode_path(const Shapes& s) { return s.pairs() <= kDecodeMaxPairs && s.L <= 1024 && s.F <= 2048; }
+
+hipError_t launch_decode(const Shapes& s, const Work& w, const uint8_t* x, const int32_t* idx, const float* router_w,
+                         const uint8_t* gu, int gu_fmt, const uint8_t* dn, int dn_fmt, float* y,
+                         const ProbeRows* probe_gu, const ProbeRows* probe_dn, hipStream_t st,
+                         hipEvent_t after_gateup) {
+  const int P = (int)s.pairs();
+  const ProbeRows none = {nullptr, 0, 0};
+  {
+    const int nxb = s.L / 32;
+    const size_t lds = kTok * s.L + 4 * kTok * nxb + 4 * kTok * (s.L / 16) + 4 * 64 * kTok;
+    const dim3 grid((unsigned)P, s.F / 32);
+    const bool q40 = gu_fmt == LAT_MOE_GATEUP_Q4_0;
+    auto kern = probe_gu ? (q40 ? k_dec_gateup<true, LAT_MOE_GATEUP_Q4_0> : k_dec_gateup<true, LAT_MOE_GATEUP_Q3_K>)
+                         : (q40 ? k_dec_gateup<false, LAT_MOE_GATEUP_Q4_0> : k_dec_gateup<false, LAT_MOE_GATEUP_Q3_K>);
+    hipLaunchKernelGGL(kern, grid, dim3(kGuThreads), lds, st, x, idx, gu, (int)s.T, P, s.k, s.L, s.F, s.E, w.h_codes,
+                       w.h_ds, probe_gu ? *probe_gu : none);
+  }
+  if (after_gateup && hipEventRecord(after_gateup, st) != hipSuccess) return hipErrorUnknown;
+  {
+    const dim3 grid((unsigned)s.T, s.L / kDnRows);
+    const bool q40 = dn_fmt == kDownQ40;
+    auto kern = s.F % 256 == 0
+                    ? (probe_dn ? (q40 ? k_dec_down<true, kDownQ40, true> : k_dec_down<true, kDownIq4Nl, true>)
+                                : (q40 ? k_dec_down<false, kDownQ40, true> : k_dec_down<false, kDownIq4Nl, true>))
+                    : (probe_dn ? (q40 ? k_dec_down<true, kDownQ40, false> : k_dec_down<true, kDownIq4Nl, false>)
+                                : (q40 ? k_dec_down<false, kDownQ40, false> : k_dec_down<false, kDownIq4Nl, false>));
+    hipLaunchKernelGGL(kern, grid, dim3(kDnThreads), 0, st, dn, idx, router_w, P, s.k, s.L, s.F, s.E, w.h_codes,
+                       w.h_ds, y, probe_dn ? *probe_dn : none);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_export_h_pairs(const int32_t* idx, const Shapes& s, const Work& w, uint8_t* h_out, hipStream_t st) {
+  const int nfb = s.F / 32;
+  const int64_t n = s.pairs() * nfb;
+  hipLaunchKernelGGL(k_export_h_pairs, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, idx, s.E, n, nfb,
+                     w.h_codes, w.h_ds, h_out);
+  return hipGetLastError();
+}
+
+}  // namespace latmoe

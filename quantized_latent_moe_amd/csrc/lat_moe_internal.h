@@ -22,9 +22,9 @@ constexpr int kRouteChunk = 1024;
 constexpr int kTileN = 128;
 // Tile table entry: (expert, first sorted position, pairs in the tile, 0).
 constexpr int kTileWords = 4;
-// Batches of at most this many pairs also get their activation rows gathered
-// in sorted order by the route pass (the small-batch kernels read them there).
-constexpr int kGatherRows = 64;
+// Batches of at most this many routed pairs (with L <= 1024, F <= 2048) take
+// the two decode kernels, which read the routing as given (no sort).
+constexpr int kDecodeMaxPairs = 64;
 
 // Slots of the small device status array written by the route scan.
 constexpr int kMiscTiles = 0;    // number of (expert, token tile) work items
@@ -51,8 +51,6 @@ struct Work {
   float* slots;         // [T*k][L] weighted expert outputs in pair order
   int8_t* xc;           // [T][L] activation codes (q8_1 blocks split into codes ...)
   float* xd;            // [T][L/32] ... and fp32 block scales)
-  int8_t* xg;           // [kGatherRows][L] codes of the valid pairs' rows in sorted order (small batches)
-  float* xgd;           // [kGatherRows][L/32] their fp32 block scales
   int nchunk, max_tiles;
   int num_cus;          // compute units of the current device (persistent grids)
 };
@@ -191,12 +189,11 @@ int stage_forward(const void* x, const int32_t* idx, const float* w, const void*
 int device_check(int* num_cus);
 
 // Kernel launchers (each returns hipGetLastError() after the enqueue).
-// Sorts pairs by expert and splits the q8_1 activations x into codes and scales.
-// gather: also copy small batches' rows in sorted order for the GEMV-shaped
-// gate/up kernel (which then needs no split rows).  yzero: y [T][L] to fill
-// with zeros for the down kernel's atomic adds, or null.
-hipError_t launch_route(const int32_t* idx, const uint8_t* x, const Shapes& s, const Work& w, bool gather,
-                        float* yzero, hipStream_t st);
+// Sorts pairs by expert and splits the q8_1 activations x into codes and
+// scales.  yzero: y [T][L] to fill with zeros for the down kernel's atomic
+// adds, or null.
+hipError_t launch_route(const int32_t* idx, const uint8_t* x, const Shapes& s, const Work& w, float* yzero,
+                        hipStream_t st);
 hipError_t launch_gateup(const Shapes& s, const Work& w, const uint8_t* gu, const ProbeRows* probe, hipStream_t st);
 // Gate/up weights in Q4_0 (18-byte blocks, a scale per 32 values), batches beyond small_path.
 hipError_t launch_gateup_q40(const Shapes& s, const Work& w, const uint8_t* gu, const ProbeRows* probe,
@@ -205,14 +202,15 @@ hipError_t launch_gateup_q40(const Shapes& s, const Work& w, const uint8_t* gu, 
 // added into y_atomic [T][L] (zeroed beforehand) with fp32 atomic adds.
 hipError_t launch_down(const uint8_t* dn, int fmt, const float* router_w, const Shapes& s, const Work& w,
                        float* y_atomic, const ProbeRows* probe, hipStream_t st);
-// Batches of at most kSmallMaxPairs pairs (L <= 1024, F <= 2048) take the
-// GEMV-shaped gate/up and down kernels.
-constexpr int kSmallMaxPairs = kGatherRows;
-bool small_path(const Shapes& s);
-hipError_t launch_gateup_small(const Shapes& s, const Work& w, const uint8_t* gu, int fmt, const ProbeRows* probe,
-                               hipStream_t st);
-hipError_t launch_down_small(const uint8_t* dn, int fmt, const float* router_w, const Shapes& s, const Work& w,
-                             const ProbeRows* probe, hipStream_t st);
+// Decode-sized batches: gate/up with SwiGLU and the q8_1 requant (H in pair
+// order), then down with the combine in slot order straight into y.  When
+// after_gateup is not null it is recorded between the two launches.
+bool decode_path(const Shapes& s);
+hipError_t launch_decode(const Shapes& s, const Work& w, const uint8_t* x, const int32_t* idx, const float* router_w,
+                         const uint8_t* gu, int gu_fmt, const uint8_t* dn, int dn_fmt, float* y,
+                         const ProbeRows* probe_gu, const ProbeRows* probe_dn, hipStream_t st, hipEvent_t after_gateup);
+// H of the decode path (pair order) as q8_1 blocks, zero for invalid ids.
+hipError_t launch_export_h_pairs(const int32_t* idx, const Shapes& s, const Work& w, uint8_t* h_out, hipStream_t st);
 hipError_t launch_combine(const int32_t* idx, const Shapes& s, const Work& w, float* y, hipStream_t st);
 hipError_t launch_quantize_q8_1(const float* x, int64_t rows, int cols, uint8_t* out, hipStream_t st);
 hipError_t launch_export_h(const Shapes& s, const Work& w, uint8_t* h_out, hipStream_t st);

@@ -6,9 +6,7 @@
 // Result: perm (pair ids grouped by expert, ascending within an expert),
 // offsets[E+1], the table of (expert, first position, pairs) token tiles of
 // kTileN pairs, and the dropped / valid / tile counts.  No host
-// synchronisation.  For the small-batch kernels (at most kGatherRows pairs)
-// the valid pairs' activation rows are also gathered in sorted order, so that
-// those kernels reach their rows in two dependent loads (tile entry, rows).
+// synchronisation.
 //
 // Up to kSmallPairs pairs: one workgroup does everything (LDS histogram, block
 // scan, tile table, stable scatter in rounds of 1024 pairs).  Larger: three
@@ -47,18 +45,6 @@ constexpr int kZeroPerBlock = 16384;
 __device__ __forceinline__ void zero_chunk(float* __restrict__ y, int64_t n, int64_t i0) {
   for (int64_t i = i0 + 4 * (int64_t)threadIdx.x; i < i0 + kZeroPerBlock && i < n; i += 4 * (int64_t)blockDim.x)
     *reinterpret_cast<float4*>(y + i) = float4{0.f, 0.f, 0.f, 0.f};
-}
-
-// Rows of the first nvalid sorted pairs (pair ids perm[0..nvalid), token =
-// pair / k) -> xg / xgd in sorted order; nvalid <= kGatherRows.  Every thread
-// of the workgroup calls it.
-__device__ void gather_rows(const uint8_t* __restrict__ x, const int32_t* sperm, int nvalid, int k, int nxb,
-                            int8_t* __restrict__ xg, float* __restrict__ xgd) {
-  for (int i = threadIdx.x; i < nvalid * nxb; i += blockDim.x) {
-    const int pos = i / nxb, b = i - pos * nxb;
-    const int64_t t = sperm[pos] / k;
-    split_block(x, t * nxb + b, (int64_t)pos * nxb + b, xg, xgd);
-  }
 }
 
 // Exclusive prefix sum over the workgroup (blockDim.x a multiple of 64, at
@@ -134,20 +120,14 @@ __device__ __forceinline__ int wave_rank(int e, bool valid, int nbits, int* cnt)
   return __popcll(same & below);
 }
 
-// ---- small batches: everything in workgroup 0; workgroups 1.. split x.
-// With gather (at most kGatherRows pairs) workgroup 0 also copies the valid
-// pairs' rows to xg / xgd in sorted order (and no workgroup splits x): each
-// thread loads one or two q8_1 blocks of x when the kernel starts, so the
-// loads overlap the sort, and after the scatter writes them to the sorted
-// position of every valid slot of their token.
+// ---- small batches: everything in workgroup 0; workgroups 1 .. xblocks
+// split x, the ones after them zero y (atomic combine).
 __global__ __launch_bounds__(1024) void k_route_small(const int32_t* __restrict__ idx, int n, int E, int nbits,
                                                       int32_t* __restrict__ offsets, int32_t* __restrict__ tiles,
                                                       int32_t* __restrict__ misc, int32_t* __restrict__ perm,
                                                       const uint8_t* __restrict__ x, int64_t nxb,
-                                                      int8_t* __restrict__ xc, float* __restrict__ xd, int gather,
-                                                      int k, int rb, int8_t* __restrict__ xg,
-                                                      float* __restrict__ xgd, int xblocks, float* __restrict__ yzero,
-                                                      int64_t ny) {
+                                                      int8_t* __restrict__ xc, float* __restrict__ xd, int xblocks,
+                                                      float* __restrict__ yzero, int64_t ny) {
   if (blockIdx.x > 0) {
     if ((int)blockIdx.x > xblocks) {  // y for the atomic combine
       zero_chunk(yzero, ny, (int64_t)(blockIdx.x - 1 - xblocks) * kZeroPerBlock);
@@ -157,58 +137,22 @@ __global__ __launch_bounds__(1024) void k_route_small(const int32_t* __restrict_
     if (b < nxb) split_block(x, b, b, xc, xd);
     return;
   }
-  extern __shared__ int32_t sm[];  // cnt[E] | base[E] | wcnt[16][E] | spos[kGatherRows]
+  extern __shared__ int32_t sm[];  // cnt[E] | base[E] | wcnt[16][E]
   __shared__ int scratch[16];
   __shared__ int bad;
   int* cnt = sm;
   int* base = sm + E;
   int* wcnt = sm + 2 * E;
-  int* spos = sm + 18 * E;  // gather: sorted position of pair p, or -1
-  // gather: x blocks i = threadIdx.x + 1024 r (r < 2) of the T * rb blocks
-  // (T = n / k <= kGatherRows, rb <= 32 with L <= 1024, so T * rb <= 2048)
-  constexpr int kGatherPer = kGatherRows * 32 / 1024;
-  uint32_t xd16[kGatherPer];
-  uint4 xlo[kGatherPer], xhi[kGatherPer];
-  // the ids of the first round, loaded before the x blocks: a wave's loads
-  // complete in issue order, so the histogram does not wait for the blocks
-  // (unconditional buffer load and a select: no branch around the load)
-  const int e_first = (int)threadIdx.x < n ? (int)buf_u32(make_rsrc(idx, (uint32_t)n * 4u),
-                                                           (int)threadIdx.x * 4, 0) : -1;
-  {
-    // issued on every path, as buffer loads whose offset past the end (or any
-    // offset without gather) reads zeros: a branch around them would make the
-    // compiler wait for all of them before the histogram
-    const int nblk = gather ? (n / k) * rb : 0;
-    const rsrc_t rx = make_rsrc(x, (uint32_t)(nblk * kQ81Bytes));
-#pragma unroll
-    for (int r = 0; r < kGatherPer; ++r) {
-      const int i = threadIdx.x + 1024 * r;
-      const int off = i < nblk ? i * kQ81Bytes : kOutOfRange;
-      xd16[r] = buf_u32(rx, off, 0);
-      xlo[r] = buf_u128(rx, off, 4);
-      xhi[r] = buf_u128(rx, off, 20);
-    }
-    if (gather && (int)threadIdx.x < n) spos[threadIdx.x] = -1;
-  }
   for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
   for (int i = threadIdx.x; i < 16 * E; i += blockDim.x) wcnt[i] = 0;
   if (threadIdx.x == 0) bad = 0;
   __syncthreads();
-  if (n <= (int)blockDim.x) {  // one round (always with gather): no loop, so no wait for the x blocks
-    if ((int)threadIdx.x < n) {
-      if ((unsigned)e_first < (unsigned)E)
-        atomicAdd(&cnt[e_first], 1);
-      else
-        atomicAdd(&bad, 1);
-    }
-  } else {
-    for (int p = threadIdx.x; p < n; p += blockDim.x) {
-      const int e = idx[p];
-      if ((unsigned)e < (unsigned)E)
-        atomicAdd(&cnt[e], 1);
-      else
-        atomicAdd(&bad, 1);
-    }
+  for (int p = threadIdx.x; p < n; p += blockDim.x) {
+    const int e = idx[p];
+    if ((unsigned)e < (unsigned)E)
+      atomicAdd(&cnt[e], 1);
+    else
+      atomicAdd(&bad, 1);
   }
   __syncthreads();
   finish_offsets(cnt, base, E, bad, offsets, tiles, misc, scratch);
@@ -217,7 +161,7 @@ __global__ __launch_bounds__(1024) void k_route_small(const int32_t* __restrict_
   const int wave = threadIdx.x >> 6;
   for (int r0 = 0; r0 < n; r0 += blockDim.x) {
     const int p = r0 + threadIdx.x;
-    const int e = p < n ? (r0 == 0 ? e_first : idx[p]) : -1;
+    const int e = p < n ? idx[p] : -1;
     const bool valid = (unsigned)e < (unsigned)E;
     int c;
     const int rank = wave_rank(e, valid, nbits, &c);
@@ -226,9 +170,7 @@ __global__ __launch_bounds__(1024) void k_route_small(const int32_t* __restrict_
     if (valid) {
       int before = 0;
       for (int w = 0; w < wave; ++w) before += wcnt[w * E + e];  // 0 where a wave had no such id
-      const int pos = base[e] + before + rank;
-      perm[pos] = p;
-      if (gather) spos[p] = pos;  // n <= kGatherRows, so p < kGatherRows
+      perm[base[e] + before + rank] = p;
     }
     __syncthreads();
     if (valid && rank == 0) {
@@ -237,37 +179,6 @@ __global__ __launch_bounds__(1024) void k_route_small(const int32_t* __restrict_
     }
     __syncthreads();
   }
-  if (gather) {  // (the scatter loop ended with a barrier: spos is complete)
-    const int nblk = (n / k) * rb;
-#pragma unroll
-    for (int r = 0; r < kGatherPer; ++r) {
-      const int i = threadIdx.x + 1024 * r;
-      if (i < nblk) {
-        const int t = i / rb, b = i - t * rb;
-        for (int j = 0; j < k; ++j) {
-          const int pos = spos[t * k + j];
-          if (pos < 0) continue;  // dropped id
-          uint4* dst = reinterpret_cast<uint4*>(xg + (int64_t)pos * rb * 32 + 32 * b);
-          dst[0] = xlo[r];
-          dst[1] = xhi[r];
-          xgd[pos * rb + b] = half_bits_to_float(xd16[r] & 0xffffu);
-        }
-      }
-    }
-  }
-}
-
-// Small batches routed by the chunked passes (E > 512): the gather alone, one
-// workgroup, after the scatter.
-__global__ __launch_bounds__(1024) void k_gather_small(const int32_t* __restrict__ perm,
-                                                       const int32_t* __restrict__ misc, const uint8_t* __restrict__ x,
-                                                       int k, int nxb, int8_t* __restrict__ xg,
-                                                       float* __restrict__ xgd) {
-  __shared__ int32_t sperm[kGatherRows];
-  const int nvalid = misc[kMiscValid];
-  if ((int)threadIdx.x < nvalid) sperm[threadIdx.x] = perm[threadIdx.x];
-  __syncthreads();
-  gather_rows(x, sperm, nvalid, k, nxb, xg, xgd);
 }
 
 // ---- large batches, pass 1: per-chunk histograms; workgroups past the
@@ -394,8 +305,8 @@ __global__ __launch_bounds__(256) void k_route_scatter(const int32_t* __restrict
 
 }  // namespace
 
-hipError_t launch_route(const int32_t* idx, const uint8_t* x, const Shapes& s, const Work& w, bool gather,
-                        float* yzero, hipStream_t st) {
+hipError_t launch_route(const int32_t* idx, const uint8_t* x, const Shapes& s, const Work& w, float* yzero,
+                        hipStream_t st) {
   const int64_t n = s.pairs();
   int nbits = 0;
   while ((1 << nbits) < s.E) ++nbits;
@@ -403,14 +314,10 @@ hipError_t launch_route(const int32_t* idx, const uint8_t* x, const Shapes& s, c
   const unsigned xblocks = (unsigned)((nxb + kSplitPerBlock - 1) / kSplitPerBlock);
   const int64_t ny = yzero ? s.T * s.L : 0;
   const unsigned zblocks = (unsigned)((ny + kZeroPerBlock - 1) / kZeroPerBlock);
-  // The GEMV-shaped gate/up kernel reads the gathered rows and not the split
-  // ones (small batches: T * k <= kGatherRows and L <= 1024).
-  if (n <= kSmallPairs && s.E <= 512) {  // (2 + 16) * E + kGatherRows ints of LDS
-    const unsigned xb = gather ? 0 : xblocks;
-    hipLaunchKernelGGL(k_route_small, dim3(1 + xb + zblocks), dim3(1024),
-                       ((2 + 16) * s.E + kGatherRows) * sizeof(int32_t), st, idx, (int)n, s.E, nbits, w.offsets,
-                       w.tiles, w.misc, w.perm, x, nxb, w.xc, w.xd, gather ? 1 : 0, s.k, s.L / 32, w.xg, w.xgd,
-                       (int)xb, yzero, ny);
+  if (n <= kSmallPairs && s.E <= 512) {  // (2 + 16) * E ints of LDS
+    hipLaunchKernelGGL(k_route_small, dim3(1 + xblocks + zblocks), dim3(1024), (2 + 16) * s.E * sizeof(int32_t), st,
+                       idx, (int)n, s.E, nbits, w.offsets, w.tiles, w.misc, w.perm, x, nxb, w.xc, w.xd, (int)xblocks,
+                       yzero, ny);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(k_route_hist, dim3(w.nchunk + xblocks + zblocks), dim3(256), s.E * sizeof(int32_t), st, idx, n,
@@ -419,8 +326,6 @@ hipError_t launch_route(const int32_t* idx, const uint8_t* x, const Shapes& s, c
                      w.tiles, w.misc);
   hipLaunchKernelGGL(k_route_scatter, dim3(w.nchunk), dim3(256), 5 * s.E * sizeof(int32_t), st, idx, n, s.E, nbits,
                      w.chunk_hist, w.offsets, w.perm);
-  if (gather)
-    hipLaunchKernelGGL(k_gather_small, dim3(1), dim3(1024), 0, st, w.perm, w.misc, x, s.k, s.L / 32, w.xg, w.xgd);
   return hipGetLastError();
 }
 
