@@ -32,14 +32,15 @@
 // The 32 features are one q8_1 block of H, so SwiGLU and the requant finish
 // inside a half wave.
 //
-// Down, workgroup (token t, 8 output rows l0..): its 512 threads are (slot
-// j, row, K slice of 8 blocks); per pass of 8 slots each thread loads the
-// 144 contiguous bytes of its row's slice for expert idx[t][j] (8 threads
-// cover a whole 1152-byte row) while the token's H rows (pair order, no
-// dependence on the routing) go to LDS; block dots J32 by v_dot4 against the
-// table-expanded indices, acc += fl(d_dn * d_H) * J32, a sum over the 8
-// slices, and y[t][l] = sum over j of w[t][j] * O_j taken in slot order: the
-// combine happens here, deterministically.
+// Down, workgroup (token t, R output rows l0..): its 512 threads are (slot
+// j, row, slice of 4 blocks), a wave per slot; per pass of 8 slots each
+// thread loads the 72 contiguous bytes of its row's slice for expert
+// idx[t][j] while the token's H rows (pair order, no dependence on the
+// routing) go to LDS; block dots J32 by v_dot4 against the table-expanded
+// indices, acc += fl(d_dn * d_H) * J32, a sum over the row's slices, and
+// y[t][l] = sum over j of w[t][j] * O_j taken in slot order: the combine
+// happens here, deterministically.  Slices of 4 blocks (rather than 8) give
+// twice the waves, each with half the instructions to issue.
 #include <mutex>
 #include <type_traits>
 
@@ -51,10 +52,8 @@ namespace {
 constexpr int kTok = 2;                 // tokens per dot pass of the gate/up kernel (an expert holds 1-2 at decode)
 constexpr int kBatch = 8;               // tokens whose activations the gate/up kernel stages at once
 constexpr int kGuMaxThreads = 512;      // 64 weight rows x up to 8 parts (two per super-block)
-constexpr int kDnRows = 8;              // output rows per down workgroup
 constexpr int kDnSlots = 8;             // pairs of the token per pass of the down kernel
-constexpr int kDnSlices = 8;            // K slices of 8 blocks (F <= 2048)
-constexpr int kDnThreads = kDnRows * kDnSlots * kDnSlices;  // 512
+constexpr int kDnThreads = 64 * kDnSlots;  // a wave per slot: rows x 4-block slices = 64
 constexpr int kDnMaxK = kDecodeMaxPairs;  // experts per token (T >= 1)
 static_assert(kDnThreads == 512 && kDecodeMaxPairs <= 64, "one lane per pair in a wave");
 
@@ -380,22 +379,26 @@ __global__ __launch_bounds__(kGuMaxThreads) void k_dec_gateup(const uint8_t* __r
 }
 
 // ---------------------------------------------------------------------------
-// WHOLE: F % 256 == 0, so every slice is 8 whole blocks (144 bytes) inside
-// its row, loaded as nine 16-byte pieces; otherwise each block is loaded on
-// its own (d, then the 16 index bytes), so no load reaches past its row (a
-// load partly past the end of the buffer would come back zero).
+// Thread (slot, row, slice) of a down workgroup: a wave is one slot's 64
+// lanes, rows x slices = 64 with a slice of 4 blocks (72 bytes) of the row;
+// S = slices per row (a power of two, >= F / 128), R = 64 / S rows per
+// workgroup.  WHOLE: F % 128 == 0, so every slice is 4 whole blocks inside
+// its row, loaded as four 16-byte pieces and 8 bytes; otherwise each block is
+// loaded on its own (d, then the 16 index bytes), so no load reaches past its
+// row (a load partly past the end of the buffer would come back zero).
 template <bool PROBE, int FMT, bool WHOLE>
 __global__ __launch_bounds__(kDnThreads) void k_dec_down(const uint8_t* __restrict__ dn, const int32_t* __restrict__ idx,
                                                        const float* __restrict__ router_w, int P, int k, int L, int F,
-                                                       int E, const int8_t* __restrict__ h_codes,
+                                                       int E, int s_log2, const int8_t* __restrict__ h_codes,
                                                        const uint32_t* __restrict__ h_ds, float* __restrict__ y,
                                                        ProbeRows probe) {
   __shared__ __align__(16) int8_t hs[kDnSlots][2048];  // the pass's H codes (F <= 2048)
   __shared__ float hds[kDnSlots][64];                   // and their fp32 d_H
-  __shared__ float osum[kDnMaxK][kDnRows];              // O of each slot and row
-  const int t = blockIdx.x, l0 = blockIdx.y * kDnRows;
+  __shared__ float osum[kDnMaxK][64];                   // O of each slot and row
+  const int S = 1 << s_log2, R = 64 >> s_log2;
+  const int t = blockIdx.x, l0 = blockIdx.y * R;
   const int tid = threadIdx.x;
-  const int slice = tid & 7, row = (tid >> 3) & 7, slot = tid >> 6;  // a wave = one slot's 8 rows
+  const int slice = tid & (S - 1), row = (tid & 63) >> s_log2, slot = tid >> 6;  // a wave = one slot's R rows
   const int nfb = F / 32, row_bytes = nfb * kIq4Bytes;
   const int l = l0 + row;
   const rsrc_t rh = make_rsrc(h_codes, (uint32_t)(P * F));
@@ -420,22 +423,24 @@ __global__ __launch_bounds__(kDnThreads) void k_dec_down(const uint8_t* __restri
     const int ds_s = tid >> 6, ds_b = tid & 63;
     const uint32_t dv = buf_u32(rs, (j0 + ds_s < k && ds_b < nfb) ? ((t * k + j0 + ds_s) * nfb + ds_b) * 4 : kOutOfRange,
                                 0);
-    // this thread's slice: bytes 144 slice .. +143 of row l of expert e
+    // this thread's slice: bytes 72 slice .. +71 of row l of expert e
     const rsrc_t rw = make_rsrc(dn + (int64_t)(valid ? e : 0) * L * row_bytes, (uint32_t)(L * row_bytes));
-    const int woff = valid && 8 * slice < nfb ? l * row_bytes + 144 * slice : kOutOfRange;
-    uint32_t wb[36];
+    const int woff = valid && 4 * slice < nfb ? l * row_bytes + 72 * slice : kOutOfRange;
+    uint32_t wb[18];
     if constexpr (WHOLE) {
 #pragma unroll
-      for (int c = 0; c < 9; ++c) {
+      for (int c = 0; c < 4; ++c) {
         const uint4 v = buf_u128(rw, woff, 16 * c);
         wb[4 * c] = v.x, wb[4 * c + 1] = v.y, wb[4 * c + 2] = v.z, wb[4 * c + 3] = v.w;
       }
+      const auto t2 = __builtin_amdgcn_raw_buffer_load_b64(rw, woff, 64, 0);
+      wb[16] = t2[0], wb[17] = t2[1];
     } else {
       // block m: d into the 16-bit half at byte 18 m, indices at 18 m + 2 (the
-      // layout of the 144-byte piece, as the unpack below reads it)
+      // layout of the 72-byte piece, as the unpack below reads it)
 #pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const int bo = 8 * slice + m < nfb ? woff + 18 * m : kOutOfRange;
+      for (int m = 0; m < 4; ++m) {
+        const int bo = 4 * slice + m < nfb ? woff + 18 * m : kOutOfRange;
         const uint32_t d16 = buf_u16(rw, bo, 0);
         const uint4 v = buf_u128(rw, bo, 2);
         const int wi = (18 * m) >> 2;
@@ -464,8 +469,8 @@ __global__ __launch_bounds__(kDnThreads) void k_dec_down(const uint8_t* __restri
     float acc = 0.f;
     if (valid) {
 #pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const int b = 8 * slice + m;
+      for (int m = 0; m < 4; ++m) {
+        const int b = 4 * slice + m;
         if (b < nfb) {
           // block m at byte 18 m of the slice: d, then 16 index bytes
           const int base = 18 * m, wi = base >> 2;
@@ -496,15 +501,13 @@ __global__ __launch_bounds__(kDnThreads) void k_dec_down(const uint8_t* __restri
         }
       }
     }
-    // sum the row's 8 slices (lanes 8 row .. 8 row + 7 of the wave)
-    acc += __shfl_xor(acc, 1);
-    acc += __shfl_xor(acc, 2);
-    acc += __shfl_xor(acc, 4);
+    // sum the row's S slices (adjacent lanes of the wave)
+    for (int o = 1; o < S; o <<= 1) acc += __shfl_xor(acc, o);
     if (slice == 0 && j < k) osum[j][row] = valid ? acc : 0.f;
   }
   __syncthreads();
   // combine: y[t][l] = sum over the slots, in order, of w[t][j] * O_j[l]
-  if (tid < kDnRows) {
+  if (tid < R) {
     float v = 0.f;
     for (int j = 0; j < k; ++j) v = __builtin_fmaf(router_w[t * k + j], osum[j][tid], v);
     y[(int64_t)t * L + l0 + tid] = v;
@@ -599,15 +602,18 @@ hipError_t launch_decode(const Shapes& s, const Work& w, const uint8_t* x, const
   }
   if (after_gateup && hipEventRecord(after_gateup, st) != hipSuccess) return hipErrorUnknown;
   {
-    const dim3 grid((unsigned)s.T, s.L / kDnRows);
+    // slices of 4 blocks per row: a power of two covering F / 128, rows = 64 / slices
+    const int nsl = (s.F / 32 + 3) / 4;
+    const int s_log2 = nsl <= 1 ? 0 : nsl <= 2 ? 1 : nsl <= 4 ? 2 : nsl <= 8 ? 3 : 4;
+    const dim3 grid((unsigned)s.T, s.L >> (6 - s_log2));
     const bool q40 = dn_fmt == kDownQ40;
-    auto kern = s.F % 256 == 0
+    auto kern = s.F % 128 == 0
                     ? (probe_dn ? (q40 ? k_dec_down<true, kDownQ40, true> : k_dec_down<true, kDownIq4Nl, true>)
                                 : (q40 ? k_dec_down<false, kDownQ40, true> : k_dec_down<false, kDownIq4Nl, true>))
                     : (probe_dn ? (q40 ? k_dec_down<true, kDownQ40, false> : k_dec_down<true, kDownIq4Nl, false>)
                                 : (q40 ? k_dec_down<false, kDownQ40, false> : k_dec_down<false, kDownIq4Nl, false>));
-    hipLaunchKernelGGL(kern, grid, dim3(kDnThreads), 0, st, dn, idx, router_w, P, s.k, s.L, s.F, s.E, w.h_codes,
-                       w.h_ds, y, probe_dn ? *probe_dn : none);
+    hipLaunchKernelGGL(kern, grid, dim3(kDnThreads), 0, st, dn, idx, router_w, P, s.k, s.L, s.F, s.E, s_log2,
+                       w.h_codes, w.h_ds, y, probe_dn ? *probe_dn : none);
   }
   return hipGetLastError();
 }
