@@ -536,15 +536,23 @@ __global__ __launch_bounds__(kWsThreads) void k_down(const uint8_t* __restrict__
   // one copy of the loop per token group th (the priority pattern is an immediate)
   auto consumer_loop = [&](auto grp_tag) {
     __syncthreads();
+    DItem nxt = cur;
     for (int g = 0; g < n_steps; ++g) {
       const int b = g & 1;
       const bool wide = cur.cnt > 64;
+      // Loads whose results wait: the next item's tile entry at the start of
+      // the item's last step (the barrier that ends a step waits for all
+      // scalar loads), the pairs at the item's first step and their router
+      // weights one step later (the weight's address needs the pair).
+      if (csb == nsb - 1 && cj + 1 < my_items) nxt = ditem(item_of(cj + 1), nlt, tiles);
       if (csb == 0) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc0[i] = acc1[i] = 0.f;
         const int n0 = (wide ? 64 : 32) * th + col, n1 = n0 + 32;
         pair0 = n0 < cur.cnt ? perm[cur.pos0 + n0] : -1;
         pair1 = wide && n1 < cur.cnt ? perm[cur.pos0 + n1] : -1;
+      }
+      if (csb == (nsb > 1 ? 1 : 0)) {
         w0 = pair0 >= 0 ? router_w[pair0] : 0.f;
         w1 = pair1 >= 0 ? router_w[pair1] : 0.f;
       }
@@ -574,7 +582,7 @@ __global__ __launch_bounds__(kWsThreads) void k_down(const uint8_t* __restrict__
           }
         }
         csb = 0;
-        if (++cj < my_items) cur = ditem(item_of(cj), nlt, tiles);
+        if (++cj < my_items) cur = nxt;
       }
       __syncthreads();
     }

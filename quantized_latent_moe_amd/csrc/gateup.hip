@@ -397,12 +397,17 @@ __global__ __launch_bounds__(kThreads) void k_gateup(const int8_t* __restrict__ 
     auto consumer_loop = [&](auto grp_tag) {
       __syncthreads();
       __syncthreads();
+      Item nxt = cur;
       for (int g = 0; g < n_steps; ++g) {
+        // the next item's tile entry is read at the start of the item's last
+        // step, so the barrier that ends the step (which waits for all scalar
+        // loads) does not wait for it
+        if (csb == nsb - 1 && cj + 1 < my_items) nxt = item_info(item_of(cj + 1), nft, tiles);
         mfma_step(grp_tag, g & 1);
         if (++csb == nsb) {
           epilogue();
           csb = 0;
-          if (++cj < my_items) cur = item_info(item_of(cj), nft, tiles);
+          if (++cj < my_items) cur = nxt;
         }
         __syncthreads();
       }
