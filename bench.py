@@ -242,12 +242,17 @@ class DenseStage:
         self.dw, self.uw = t(I.d_q8_0), t(I.u_q8_0)
         self.dw4, self.uw4 = t(I.d_q4_0), t(I.u_q4_0)  # the same projections with Q4_0 weights
         self.xl = torch.empty((dwl.T, dwl.L // 32, 36), dtype=torch.uint8, device=dev)
+        self.xlf = torch.empty((dwl.T, dwl.L), dtype=torch.float32, device=dev)
         self.out = torch.empty((dwl.T, dwl.H), dtype=torch.float32, device=dev)
         torch.cuda.synchronize()
 
     def run_d(self):
+        # decode-sized batches ask for the fp32 rows too: the library then
+        # spreads the weight stream over many workgroups and rounds the rows
+        # to q8_1 in a second kernel (q8_1 output alone keeps one workgroup
+        # per 32 rows)
         w = self.wl
-        self.lm.dense_q8_0(self.xh, self.dw, w.T, w.L, w.H, None, self.xl)
+        self.lm.dense_q8_0(self.xh, self.dw, w.T, w.L, w.H, self.xlf if w.T <= 8 else None, self.xl)
 
     def run_u(self):
         w = self.wl
@@ -255,7 +260,7 @@ class DenseStage:
 
     def run_d4(self):
         w = self.wl
-        self.lm.dense_q4_0(self.xh, self.dw4, w.T, w.L, w.H, None, self.xl)
+        self.lm.dense_q4_0(self.xh, self.dw4, w.T, w.L, w.H, self.xlf if w.T <= 8 else None, self.xl)
 
     def run_u4(self):
         w = self.wl

@@ -34,11 +34,14 @@
 //
 // Batches of at most kSmallTok tokens take k_dense_small instead: GEMV
 // shaped, one workgroup of up to 16 waves per 32 output rows (one q8_1 block
-// of every token's output).  The lanes of a wave take consecutive blocks of
-// one row (coalesced weight reads, issued first into registers), the
-// activation rows are copied into LDS once in contiguous 16-byte chunks,
-// integer dots by v_dot4, the fold per block in fp32, a butterfly sum across
-// the lanes of a row, and the q8_1 rounding from LDS.
+// of every token's output) when only q8_1 output is asked for, else per 4
+// rows (a CU keeps a bounded number of loads in flight, so the weight stream
+// needs many CUs), followed for q8_1 output by the rounding kernel on the
+// fp32 rows.  The lanes of a wave take consecutive blocks of one row
+// (coalesced weight reads, issued first into registers), the activation rows
+// are copied into LDS once in contiguous 16-byte chunks, integer dots by
+// v_dot4, the fold per block in fp32, a butterfly sum across the lanes of a
+// row, and the q8_1 rounding from LDS.
 //
 // Work items are dealt XCD-major: workgroup w runs on XCD w % 8 and takes
 // item (w % 8) * ceil(items / 8) + w / 8 of an order that sweeps groups of
@@ -314,11 +317,16 @@ __global__ __launch_bounds__(kThreads) void k_dense_q8_0(const uint8_t* __restri
 // Decode-sized batches.
 // ------------------------------------------------------------------------
 constexpr int kSmallTok = 8;      // largest batch of the GEMV-shaped kernel
-constexpr int kSmallRows = 32;    // output rows per workgroup (one q8_1 block)
-// Waves of a workgroup for LPR lanes per row: enough that each wave has one or
-// two rows (many loads in flight per CU: these few workgroups are latency
-// bound), at most 16.
-constexpr int small_waves(int lpr) { return 64 / lpr * 16 <= kSmallRows ? 16 : kSmallRows / (64 / lpr); }
+constexpr int kSmallRows = 32;    // output rows per workgroup with q8_1 output (one q8_1 block)
+// With fp32 output only, a workgroup takes this many rows (at least one lane
+// group): a CU keeps only so many loads in flight, so the weight stream needs
+// many CUs, and D (1024 rows) would have 32 workgroups of 32 rows.
+constexpr int kSmallRowsF32 = 4;
+// Waves of a workgroup of ROWS rows for LPR lanes per row: enough that each
+// wave has one or two rows (many loads in flight per CU: these workgroups are
+// latency bound), at most 16.
+constexpr int small_waves(int lpr, int rows) { return 64 / lpr * 16 <= rows ? 16 : rows / (64 / lpr); }
+constexpr int small_rows_f32(int lpr) { return 64 / lpr > kSmallRowsF32 ? 64 / lpr : kSmallRowsF32; }
 
 // 16 bytes from LDS at a 4-byte-aligned address (one ds_read_b128: gfx950
 // serves unaligned LDS accesses).
@@ -339,23 +347,25 @@ __device__ __forceinline__ float group_sum(float v) {
 }
 
 // BPL: blocks per lane and row (the row's K/32 blocks are dealt to LPR lanes
-// round-robin); LPR: lanes per row.
-template <int BPL, int LPR, bool PROBE, int WFMT>
-__global__ __launch_bounds__(64 * small_waves(LPR)) void k_dense_small(const uint8_t* __restrict__ x,
-                                                               const uint8_t* __restrict__ w, int T, int N, int K,
-                                                               float* __restrict__ y_f32, uint8_t* __restrict__ y_q8,
-                                                               ProbeRows probe) {
-  constexpr int kSmallThreads = 64 * small_waves(LPR);
+// round-robin); LPR: lanes per row; ROWS: output rows per workgroup (32 for
+// q8_1 output).  A row's value does not depend on ROWS: the same lanes fold
+// the same blocks in the same order.
+template <int BPL, int LPR, bool PROBE, int WFMT, int ROWS>
+__global__ __launch_bounds__(64 * small_waves(LPR, ROWS)) void k_dense_small(const uint8_t* __restrict__ x,
+                                                                     const uint8_t* __restrict__ w, int T, int N,
+                                                                     int K, float* __restrict__ y_f32,
+                                                                     uint8_t* __restrict__ y_q8, ProbeRows probe) {
+  constexpr int kSmallThreads = 64 * small_waves(LPR, ROWS);
   constexpr int kRowsPerIter = 64 / LPR;
-  constexpr int kRowsPerWave = kSmallRows / small_waves(LPR);
+  constexpr int kRowsPerWave = ROWS / small_waves(LPR, ROWS);
   static_assert(kRowsPerWave % kRowsPerIter == 0 && kRowsPerWave >= kRowsPerIter,
                 "rows of a wave come in whole iterations");
-  __shared__ float ys[kSmallTok][kSmallRows];
+  __shared__ float ys[kSmallTok][ROWS];
   extern __shared__ __align__(16) uint8_t xraw[];  // the T activation rows as they are in memory (+16)
   const int nb = K / 32;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int row0 = blockIdx.x * kSmallRows;
+  const int row0 = blockIdx.x * ROWS;
   const int li = lane & (LPR - 1), sub = lane / LPR;  // lane within its row group, row group
   constexpr int kWB = WFMT == kDenseQ40 ? kQ40Bytes : kQ80Bytes;  // weight block bytes
   const rsrc_t rw = make_rsrc(w, (uint32_t)((int64_t)N * nb * kWB));
@@ -456,12 +466,12 @@ __global__ __launch_bounds__(64 * small_waves(LPR)) void k_dense_small(const uin
   __syncthreads();
 
   if (y_f32) {
-    for (int i = tid; i < T * kSmallRows; i += kSmallThreads) {
-      const int t = i / kSmallRows, rl = i - t * kSmallRows;
+    for (int i = tid; i < T * ROWS; i += kSmallThreads) {
+      const int t = i / ROWS, rl = i - t * ROWS;
       if (row0 + rl < N) y_f32[(int64_t)t * N + row0 + rl] = ys[t][rl];
     }
   }
-  if (y_q8 && tid < 64 * ((T + 1) / 2)) {
+  if (ROWS == kSmallRows && y_q8 && tid < 64 * ((T + 1) / 2)) {
     // q8_1 rule over the 32 rows of a token, 32 lanes per token (two tokens a wave)
 #pragma clang fp contract(off)
     const int t = tid >> 5, i = tid & 31;
@@ -485,18 +495,30 @@ __global__ __launch_bounds__(64 * small_waves(LPR)) void k_dense_small(const uin
   }
 }
 
+template <int BPL, int LPR, int WFMT, int ROWS>
+void launch_small_rows(const uint8_t* x, const uint8_t* w, int T, int N, int K, float* y_f32, uint8_t* y_q8,
+                       const ProbeRows* probe, hipStream_t st) {
+  const dim3 grid((N + ROWS - 1) / ROWS);
+  const size_t lds = (size_t)T * (K / 32) * kQ81Bytes + 16;
+  const ProbeRows none = {nullptr, 0, 0};
+  const dim3 block(64 * small_waves(LPR, ROWS));
+  if (probe)
+    hipLaunchKernelGGL((k_dense_small<BPL, LPR, true, WFMT, ROWS>), grid, block, lds, st, x, w, T, N, K, y_f32, y_q8,
+                       *probe);
+  else
+    hipLaunchKernelGGL((k_dense_small<BPL, LPR, false, WFMT, ROWS>), grid, block, lds, st, x, w, T, N, K, y_f32, y_q8,
+                       none);
+}
+
+// q8_1 output: workgroups of 32 rows, which round their rows themselves.  fp32
+// output only: workgroups of small_rows_f32(LPR) rows, many more of them.
 template <int BPL, int LPR, int WFMT>
 void launch_small_fmt(const uint8_t* x, const uint8_t* w, int T, int N, int K, float* y_f32, uint8_t* y_q8,
                       const ProbeRows* probe, hipStream_t st) {
-  const dim3 grid(N / kSmallRows);
-  const size_t lds = (size_t)T * (K / 32) * kQ81Bytes + 16;
-  const ProbeRows none = {nullptr, 0, 0};
-  if (probe)
-    hipLaunchKernelGGL((k_dense_small<BPL, LPR, true, WFMT>), grid, dim3(64 * small_waves(LPR)), lds, st, x, w, T, N,
-                       K, y_f32, y_q8, *probe);
+  if (y_q8)
+    launch_small_rows<BPL, LPR, WFMT, kSmallRows>(x, w, T, N, K, y_f32, y_q8, probe, st);
   else
-    hipLaunchKernelGGL((k_dense_small<BPL, LPR, false, WFMT>), grid, dim3(64 * small_waves(LPR)), lds, st, x, w, T,
-                       N, K, y_f32, y_q8, none);
+    launch_small_rows<BPL, LPR, WFMT, small_rows_f32(LPR)>(x, w, T, N, K, y_f32, nullptr, probe, st);
 }
 
 template <int BPL, int LPR>
@@ -534,13 +556,18 @@ hipError_t launch_dense(const uint8_t* x, const uint8_t* w, int wfmt, int64_t T,
   int bpl = 0, lpr = 0;
   if (small_config(T, K / 32, &bpl, &lpr)) {
     const int t = (int)T;
-    if (lpr == 8) launch_small<1, 8>(wfmt, x, w, t, N, K, y_f32, y_q8, probe, st);
-    else if (lpr == 16) launch_small<1, 16>(wfmt, x, w, t, N, K, y_f32, y_q8, probe, st);
-    else if (lpr == 32) launch_small<1, 32>(wfmt, x, w, t, N, K, y_f32, y_q8, probe, st);
-    else if (bpl == 1) launch_small<1, 64>(wfmt, x, w, t, N, K, y_f32, y_q8, probe, st);
-    else if (bpl == 2) launch_small<2, 64>(wfmt, x, w, t, N, K, y_f32, y_q8, probe, st);
-    else launch_small<4, 64>(wfmt, x, w, t, N, K, y_f32, y_q8, probe, st);
-    return hipGetLastError();
+    // Both outputs: the fp32 rows from the many-workgroup kernel, then their
+    // q8_1 rounding (the same bytes the 32-row workgroups would write).
+    uint8_t* q8_direct = y_f32 ? nullptr : y_q8;
+    if (lpr == 8) launch_small<1, 8>(wfmt, x, w, t, N, K, y_f32, q8_direct, probe, st);
+    else if (lpr == 16) launch_small<1, 16>(wfmt, x, w, t, N, K, y_f32, q8_direct, probe, st);
+    else if (lpr == 32) launch_small<1, 32>(wfmt, x, w, t, N, K, y_f32, q8_direct, probe, st);
+    else if (bpl == 1) launch_small<1, 64>(wfmt, x, w, t, N, K, y_f32, q8_direct, probe, st);
+    else if (bpl == 2) launch_small<2, 64>(wfmt, x, w, t, N, K, y_f32, q8_direct, probe, st);
+    else launch_small<4, 64>(wfmt, x, w, t, N, K, y_f32, q8_direct, probe, st);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !y_q8 || q8_direct) return e;
+    return launch_quantize_q8_1(y_f32, T, N, y_q8, st);
   }
   // Q4_0 weights above the GEMV sizes take the persistent kernel at any T
   // (the entry point has checked its shape rule); Q8_0 weights from T = 128.
