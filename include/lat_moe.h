@@ -209,7 +209,10 @@ int lat_moe_quantize_q8_1(const float* x, int64_t rows, int32_t cols, void* out_
  * N * K/32 * 34 < 2^31 and T * K/32 * 36 < 2^31 bytes.  At least one output
  * must be given; pointers 16-byte aligned (the weight rows themselves are only
  * 2-byte aligned and are read as such).  T = 0 enqueues nothing.  Outputs are
- * deterministic.  No workspace. */
+ * deterministic.  No workspace.  For T <= 8, a call with y_f32 given spreads
+ * the weight rows over many more workgroups (and, if y_q8_1 is given too,
+ * rounds y_f32 in a second kernel); with y_q8_1 alone one workgroup takes
+ * each 32 rows, which is slower for few rows.  The bytes are the same. */
 int lat_moe_dense_q8_0(const void* x_q8_1, const void* w_q8_0, int64_t T, int32_t N, int32_t K, float* y_f32,
                        void* y_q8_1, void* stream);
 
