@@ -235,12 +235,20 @@ __global__ __launch_bounds__(kThreads) void k_gateup(const int8_t* __restrict__ 
       }
       const int qshift = 2 * uj;       // low two bits of element 128un + 32uj + l: bit 2uj of qs[l]
       const int hs = 4 * un + uj - 2;  // its high bit (bit 4un + uj of hmask[l]) moves to bit 2
+      // Two words at a time through 64-bit shifts: the bits a shift moves
+      // across the word boundary (at most 6 at the top of the low word, 2 at
+      // the bottom of the high word) fall outside the masks.
       uint32_t o[8];
 #pragma unroll
-      for (int g = 0; g < 8; ++g) {
-        const uint32_t hb = (hs >= 0 ? (hm[g] >> hs) : (hm[g] << -hs)) & 0x04040404u;
-        const uint32_t c = ((qs[g] >> qshift) & 0x03030303u) | hb;
-        o[g] = __builtin_amdgcn_perm(thi[g >> 2], tlo[g >> 2], c);
+      for (int g = 0; g < 8; g += 2) {
+        const uint64_t h64 = ((uint64_t)hm[g + 1] << 32) | hm[g];
+        const uint64_t q64 = ((uint64_t)qs[g + 1] << 32) | qs[g];
+        const uint64_t hsh = hs >= 0 ? (h64 >> hs) : (h64 << -hs);
+        const uint64_t qsh = q64 >> qshift;
+        const uint32_t c0 = ((uint32_t)qsh & 0x03030303u) | ((uint32_t)hsh & 0x04040404u);
+        const uint32_t c1 = ((uint32_t)(qsh >> 32) & 0x03030303u) | ((uint32_t)(hsh >> 32) & 0x04040404u);
+        o[g] = __builtin_amdgcn_perm(thi[g >> 2], tlo[g >> 2], c0);
+        o[g + 1] = __builtin_amdgcn_perm(thi[g >> 2], tlo[g >> 2], c1);
       }
       uint4* udst = reinterpret_cast<uint4*>(As[b] + ur * kOpStride + 128 * un + 32 * uj);
       udst[0] = uint4{o[0], o[1], o[2], o[3]};
