@@ -259,7 +259,14 @@ __global__ __launch_bounds__(kThreads) void k_gateup(const int8_t* __restrict__ 
   // =========================== consumer state ===========================
   const int fsub = wave & 1, tsub = (wave >> 1) & 3;
   const int col = lane & 31, khalf = lane >> 5;
-  const v16i zero = {};
+  // MFMA accumulator input: the float bits of 1.5 * 2^23 in every element, so
+  // an MFMA returns those bits plus the int32 block dot, which read as a float
+  // is 1.5 * 2^23 + dot exactly (|dot| < 2^22): the conversion costs no VALU
+  // instruction.  Built by opaque moves: with a visible splat constant as the
+  // accumulator input, this compiler treats all 16 results as equal.
+  v16i magic;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) asm volatile("v_mov_b32 %0, 0x4b400000" : "=v"(magic[i]));
   float accg[16], accu[16];
   int cj = 0, csb = 0;  // item index and super-block of the MFMA step
   Item cur = item_info(item_of(0), nft, tiles);
@@ -294,18 +301,22 @@ __global__ __launch_bounds__(kThreads) void k_gateup(const int8_t* __restrict__ 
       // (oldest-first issue alone lets one run ahead and the other finish
       // alone at a fraction of the VALU rate).
       if ((GRP ^ kb) & 1) __builtin_amdgcn_s_setprio(1); else __builtin_amdgcn_s_setprio(0);
-      const v16i ig = __builtin_amdgcn_mfma_i32_32x32x32_i8(va, vb, zero, 0, 0, 0);  // -I32
-      const v16i iu = __builtin_amdgcn_mfma_i32_32x32x32_i8(vu, vb, zero, 0, 0, 0);
+      const v16i ig = __builtin_amdgcn_mfma_i32_32x32x32_i8(va, vb, magic, 0, 0, 0);  // M - I32
+      const v16i iu = __builtin_amdgcn_mfma_i32_32x32x32_i8(vu, vb, magic, 0, 0, 0);
       if (kb < 7) {  // next block's operands
         va = *reinterpret_cast<const v4i*>(ag + 32 * (kb + 1));
         vu = *reinterpret_cast<const v4i*>(au + 32 * (kb + 1));
         vb = *reinterpret_cast<const v4i*>(bp + 32 * (kb + 1));
       }
       const float d = dxv[kb];  // -d_x
+      const float cm = -d * kMagic;  // exact: d has at most 11 significant bits
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        sbg[i] = kb == 0 ? d * (float)ig[i] : __builtin_fmaf(d, (float)ig[i], sbg[i]);
-        sbu[i] = kb == 0 ? d * (float)iu[i] : __builtin_fmaf(d, (float)iu[i], sbu[i]);
+        // d * (M - I) - d * M, rounded once: d_x * I rounded
+        const float tg = __builtin_fmaf(d, as_float(ig[i]), cm);
+        const float tu = __builtin_fmaf(d, as_float(iu[i]), cm);
+        sbg[i] = kb == 0 ? tg : sbg[i] + tg;
+        sbu[i] = kb == 0 ? tu : sbu[i] + tu;
       }
       if (PROBE && probe_pair >= 0) {
 #pragma unroll
@@ -313,8 +324,8 @@ __global__ __launch_bounds__(kThreads) void k_gateup(const int8_t* __restrict__ 
           const int f = cur.f0 + 32 * fsub + 8 * (i >> 2) + 4 * khalf + (i & 3);
           const int rg = f - probe.row0, ru = F + f - probe.row0;
           const int64_t o = (int64_t)probe_pair * probe.rows;
-          if (f < F && rg >= 0 && rg < probe.rows) probe.out[(o + rg) * nxb + csb * 8 + kb] = -ig[i];
-          if (f < F && ru >= 0 && ru < probe.rows) probe.out[(o + ru) * nxb + csb * 8 + kb] = -iu[i];
+          if (f < F && rg >= 0 && rg < probe.rows) probe.out[(o + rg) * nxb + csb * 8 + kb] = kMagicBits - ig[i];
+          if (f < F && ru >= 0 && ru < probe.rows) probe.out[(o + ru) * nxb + csb * 8 + kb] = kMagicBits - iu[i];
         }
       }
     }
