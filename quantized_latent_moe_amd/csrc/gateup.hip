@@ -17,10 +17,11 @@
 //     f0 + 32*(c&1) .. +31 and tokens 32*(c>>1) .. +31 (both MFMAs share the
 //     activation fragment; gate and up of a (feature, token) meet in one lane
 //     for SwiGLU).  Per K step of 256 values: v_mfma_i32_32x32x32_i8 per
-//     32-value block (zero accumulator, the result is minus the block dot
-//     I32), acc_sb = fma(d_x, float(I32), acc_sb) (exact conversion,
-//     |I32| < 2^20), and once per step acc += d_w[row][sb] * acc_sb.  A wave
-//     whose 32 tokens are all padding skips its MFMAs.
+//     32-value block with the float bits of M = 1.5 * 2^23 as accumulator
+//     input, so the result read as a float is M - I32 exactly (the operand is
+//     -w, |I32| < 2^20); fma(-d_x, M - I32, d_x * M) is d_x * I32 rounded
+//     once, added into acc_sb; once per step acc += d_w[row][sb] * acc_sb.
+//     A wave whose 32 tokens are all padding skips its MFMAs.
 //   4 producer waves: producer p owns weight rows 32p .. 32p+31 of the item
 //     (gate rows, then up rows) and tokens 32p .. 32p+31.  Per K step it loads
 //     into registers, through buffer loads whose out-of-range offset returns
