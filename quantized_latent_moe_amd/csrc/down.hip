@@ -311,8 +311,12 @@ __global__ __launch_bounds__(kWsThreads) void k_down(const uint8_t* __restrict__
   __shared__ __align__(16) uint8_t raw[kWsLT * kWsStep];
   __shared__ __align__(16) int8_t As[2][kWsLT * 256];
   __shared__ __align__(16) int8_t Bs[2][kWsNT * 256];
-  __shared__ __align__(16) _Float16 dds[2][8][kWsLT];  // d_dn per block, rows in dd_pos order
-  __shared__ __align__(16) float dhs[2][kWsNT][8];      // d_H per token and block
+  // d_dn in fp32, d_H in fp16: a consumer lane folds 16 rows' d_dn per block
+  // (fp32 there keeps that a full-rate v_fma_f32; a mixed fp16 operand makes
+  // it a v_fma_mix_f32, which issues at about 0.6 of the rate) and one or two
+  // tokens' d_H, which it converts itself.
+  __shared__ __align__(16) float dds[2][8][kWsLT];          // d_dn per block, rows in dd_pos order
+  __shared__ __align__(16) _Float16 dhs[2][kWsNT][8];       // d_H per token and block
 
   const int nlt = L / kWsLT;
   // XCD x (workgroups w with w % 8 == x) takes token tiles [t0, t1), all their
@@ -406,7 +410,8 @@ __global__ __launch_bounds__(kWsThreads) void k_down(const uint8_t* __restrict__
         *reinterpret_cast<uint4*>(Bs[b] + swz(n, lane & 15)) = rx[a];
       }
 #pragma unroll
-      for (int c = 0; c < 4; ++c) dhs[b][32 * p + 8 * c + (lane >> 3)][lane & 7] = half_bits_to_float(rd[c] & 0xffffu);
+      for (int c = 0; c < 4; ++c)
+        dhs[b][32 * p + 8 * c + (lane >> 3)][lane & 7] = __builtin_bit_cast(_Float16, (uint16_t)(rd[c] & 0xffffu));
     };
     auto unpack = [&](int b) {
       // expand: row 32p + (lane & 31), blocks 4*(lane >> 5) .. +3 from the 72
@@ -438,7 +443,7 @@ __global__ __launch_bounds__(kWsThreads) void k_down(const uint8_t* __restrict__
         const int kg = 4 * hb + kk;
         *reinterpret_cast<uint4*>(As[b] + swz(r, 2 * kg)) = lo;
         *reinterpret_cast<uint4*>(As[b] + swz(r, 2 * kg + 1)) = hi;
-        dds[b][kg][dd_pos(r)] = __builtin_bit_cast(_Float16, (uint16_t)dbits);
+        dds[b][kg][dd_pos(r)] = half_bits_to_float(dbits);
       }
     };
 
@@ -480,15 +485,18 @@ __global__ __launch_bounds__(kWsThreads) void k_down(const uint8_t* __restrict__
     const int8_t* ap = As[b] + (32 * rs + col) * 256;
     const int8_t* bp0 = Bs[b] + n0 * 256;
     const int8_t* bp1 = Bs[b] + (TWO ? n1 : n0) * 256;
-    const float4 h00 = *reinterpret_cast<const float4*>(&dhs[b][n0][0]);
-    const float4 h01 = *reinterpret_cast<const float4*>(&dhs[b][n0][4]);
-    float4 h10 = h00, h11 = h01;
-    if (TWO) {
-      h10 = *reinterpret_cast<const float4*>(&dhs[b][n1][0]);
-      h11 = *reinterpret_cast<const float4*>(&dhs[b][n1][4]);
+    const uint4 hq0 = *reinterpret_cast<const uint4*>(&dhs[b][n0][0]);
+    const uint4 hq1 = TWO ? *reinterpret_cast<const uint4*>(&dhs[b][n1][0]) : hq0;
+    const uint32_t hw0[4] = {hq0.x, hq0.y, hq0.z, hq0.w}, hw1[4] = {hq1.x, hq1.y, hq1.z, hq1.w};
+    // converted once per step; the empty asm keeps the compiler from folding
+    // the conversion into every fma of the block as a v_fma_mix_f32
+    float dh0[8], dh1[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      dh0[q] = half_bits_to_float((q & 1) ? hw0[q >> 1] >> 16 : hw0[q >> 1] & 0xffffu);
+      dh1[q] = TWO ? half_bits_to_float((q & 1) ? hw1[q >> 1] >> 16 : hw1[q >> 1] & 0xffffu) : dh0[q];
+      asm volatile("" : "+v"(dh0[q]), "+v"(dh1[q]));
     }
-    const float dh0[8] = {h00.x, h00.y, h00.z, h00.w, h01.x, h01.y, h01.z, h01.w};
-    const float dh1[8] = {h10.x, h10.y, h10.z, h10.w, h11.x, h11.y, h11.z, h11.w};
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb) {
       // The two consumer waves of a SIMD (th = 0, 1) take turns at the higher
@@ -506,15 +514,15 @@ __global__ __launch_bounds__(kWsThreads) void k_down(const uint8_t* __restrict__
         j1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(va, vb1, magic, 0, 0, 0);
       }
       // d_dn of this lane's 16 rows for block kb (fp16, contiguous)
-      const uint4 dq0 = *reinterpret_cast<const uint4*>(&dds[b][kb][32 * rs + 16 * khalf]);
-      const uint4 dq1 = *reinterpret_cast<const uint4*>(&dds[b][kb][32 * rs + 16 * khalf + 8]);
-      const uint32_t dq[8] = {dq0.x, dq0.y, dq0.z, dq0.w, dq1.x, dq1.y, dq1.z, dq1.w};
+      const float4* dqp = reinterpret_cast<const float4*>(&dds[b][kb][32 * rs + 16 * khalf]);
+      const float4 dq0 = dqp[0], dq1 = dqp[1], dq2 = dqp[2], dq3 = dqp[3];
+      const float ddv[16] = {dq0.x, dq0.y, dq0.z, dq0.w, dq1.x, dq1.y, dq1.z, dq1.w,
+                             dq2.x, dq2.y, dq2.z, dq2.w, dq3.x, dq3.y, dq3.z, dq3.w};
       const float c0 = -kMagic * dh0[kb], c1 = -kMagic * dh1[kb];  // exact
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float dd = half_bits_to_float((i & 1) ? (dq[i >> 1] >> 16) : (dq[i >> 1] & 0xffffu));
-        acc0[i] = __builtin_fmaf(dd, __builtin_fmaf(dh0[kb], as_float(j0[i]), c0), acc0[i]);
-        if (TWO) acc1[i] = __builtin_fmaf(dd, __builtin_fmaf(dh1[kb], as_float(j1[i]), c1), acc1[i]);
+        acc0[i] = __builtin_fmaf(ddv[i], __builtin_fmaf(dh0[kb], as_float(j0[i]), c0), acc0[i]);
+        if (TWO) acc1[i] = __builtin_fmaf(ddv[i], __builtin_fmaf(dh1[kb], as_float(j1[i]), c1), acc1[i]);
       }
       if (PROBE) {
 #pragma unroll
