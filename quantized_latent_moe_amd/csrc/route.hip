@@ -22,7 +22,7 @@ namespace latmoe {
 namespace {
 
 constexpr int kSmallPairs = 4096;
-constexpr int kScanStage = 16384;  // chunk-histogram entries the scan stages in LDS
+constexpr int kScanStage = 32768;  // chunk-histogram entries the scan stages in LDS (128 KB)
 constexpr int kSplitPerBlock = 1024;  // q8_1 blocks split per extra workgroup
 
 // q8_1 block sb -> 32 codes at xc + 32 db and the fp32 scale xd[db].
@@ -231,17 +231,32 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ chunk
   __shared__ int32_t stage[kScanStage];  // the chunk histograms, when they fit
   const int64_t nh = (int64_t)nchunk * E;
   if (nh <= kScanStage) {
-    // coalesced copy to LDS, per-expert running sums there, prefixes back out
+    // coalesced copy to LDS; per expert, G threads (adjacent lanes) each take
+    // a contiguous run of chunks: their sums, an exclusive scan of those over
+    // the G lanes, then the running prefixes written back; prefixes back out
     for (int i = threadIdx.x; i < nh; i += blockDim.x) stage[i] = chunk_hist[i];
     __syncthreads();
-    for (int e = threadIdx.x; e < E; e += blockDim.x) {
-      int run = 0;
-      for (int c = 0; c < nchunk; ++c) {
+    int G = 1;
+    while (G < 64 && G * 2 * E <= (int)blockDim.x) G *= 2;
+    const int e = threadIdx.x / G, g = threadIdx.x % G;
+    const int per = (nchunk + G - 1) / G, c0 = g * per, c1 = min(nchunk, c0 + per);
+    int part = 0;
+    if (e < E)
+      for (int c = c0; c < c1; ++c) part += stage[c * E + e];
+    // inclusive scan over the group's lanes (G a power of two, groups aligned)
+    int inc = part;
+    for (int d = 1; d < G; d <<= 1) {
+      const int y = __shfl_up(inc, d, G);
+      if (g >= d) inc += y;
+    }
+    if (e < E) {
+      int run = inc - part;
+      for (int c = c0; c < c1; ++c) {
         const int v = stage[c * E + e];
         stage[c * E + e] = run;
         run += v;
       }
-      cnt[e] = run;
+      if (g == G - 1) cnt[e] = inc;
     }
     __syncthreads();
     for (int i = threadIdx.x; i < nh; i += blockDim.x) chunk_hist[i] = stage[i];

@@ -242,6 +242,25 @@ def test_invalid_and_duplicate_ids():
     check_y(out["y"], stagewise_y(out, I), label="edge stage-wise")
 
 
+# The large-batch counting sort at shapes that take each branch of its chunk
+# scan: several lanes per expert (E = 128), one lane per expert (E = 600),
+# and chunk histograms too large for the scan's LDS stage (36 chunks x 1024
+# experts); with invalid ids mixed in.  Routing only: perm, offsets, dropped.
+@pytest.mark.parametrize("T,E,k", [(4000, 128, 8), (3000, 600, 8), (9000, 1024, 4)], ids=lambda v: str(v))
+def test_route_scan_branches(T, E, k):
+    wl = Workload(f"route_{T}_{E}", T=T, L=256, F=128, E=E, k=k, zipf_s=1.1, seed=21)
+    say(f"route case T={T} E={E} k={k}")
+    I, xq = _case(wl)
+    rng = np.random.default_rng(5)
+    idx = I.router_idx.copy()
+    bad = rng.random(idx.shape) < 0.01
+    idx[bad] = rng.choice(np.array([-1, E, 1 << 20], dtype=np.int32), size=int(bad.sum()))
+    I.router_idx[...] = idx
+    out = Gpu(I, xq).forward_debug()
+    _check_routing(out, I)
+    assert out["dropped"] == int(bad.sum())
+
+
 def test_small_batch_invalid_and_duplicate_ids():
     """The small-batch kernels (at most 64 pairs) with dropped and repeated ids:
     only the valid pairs' rows are gathered, in sorted order."""
