@@ -228,7 +228,7 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ chunk
   __shared__ int32_t first[1024];
   __shared__ int scratch[16];
   __shared__ int bad;
-  __shared__ int32_t stage[kScanStage];  // the chunk histograms, when they fit
+  extern __shared__ int32_t stage[];  // the chunk histograms, when they fit (sized by the launch)
   const int64_t nh = (int64_t)nchunk * E;
   if (nh <= kScanStage) {
     // coalesced copy to LDS; per expert, G threads (adjacent lanes) each take
@@ -337,8 +337,9 @@ hipError_t launch_route(const int32_t* idx, const uint8_t* x, const Shapes& s, c
   }
   hipLaunchKernelGGL(k_route_hist, dim3(w.nchunk + xblocks + zblocks), dim3(256), s.E * sizeof(int32_t), st, idx, n,
                      s.E, w.nchunk, w.chunk_hist, w.chunk_bad, x, nxb, w.xc, w.xd, (int)xblocks, yzero, ny);
-  hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(1024), 0, st, w.chunk_hist, w.chunk_bad, w.nchunk, s.E, w.offsets,
-                     w.tiles, w.misc);
+  const int64_t nh = (int64_t)w.nchunk * s.E;
+  hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(1024), nh <= kScanStage ? nh * sizeof(int32_t) : 0, st, w.chunk_hist,
+                     w.chunk_bad, w.nchunk, s.E, w.offsets, w.tiles, w.misc);
   hipLaunchKernelGGL(k_route_scatter, dim3(w.nchunk), dim3(256), 5 * s.E * sizeof(int32_t), st, idx, n, s.E, nbits,
                      w.chunk_hist, w.offsets, w.perm);
   return hipGetLastError();
