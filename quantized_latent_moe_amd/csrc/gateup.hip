@@ -129,10 +129,27 @@ __global__ __launch_bounds__(kThreads) void k_gateup(const int8_t* __restrict__ 
   const int w55 = (lane & 7) == 7 ? -kQ3kBytes : 0;
   int lj = 0, lsb = 0, qf0 = -1;
   bool need_setup = true;
+  // The next item's token ids: producer p fetches those of its own tokens
+  // 32p .. 32p+31 (lanes 0..31), so only the wave that writes an entry reads
+  // it and no barrier has to separate the two (with one K step per item the
+  // next setup can follow in the same step).  The pair loads are issued in
+  // setup; their LDS store (flush_ids) comes at the end of the step, or at
+  // the next setup if that comes first.
+  int pend_pair = -1, pend_buf = 0;
+  bool pend = false;
   auto fetch_ids = [&](int j) {
     if (j < my_items) {
       const Item it = item_info(item_of(j), nft, tiles);
-      if (ptid < kNT) ids[j & 1][ptid] = ptid < it.cnt ? perm[it.pos0 + ptid] / k : -1;
+      const int n = 32 * p + lane;
+      if (lane < 32) pend_pair = n < it.cnt ? perm[it.pos0 + n] : -1;
+      pend_buf = j & 1;
+      pend = true;
+    }
+  };
+  auto flush_ids = [&]() {
+    if (pend) {
+      if (lane < 32) ids[pend_buf][32 * p + lane] = pend_pair >= 0 ? pend_pair / k : -1;
+      pend = false;
     }
   };
   auto setup = [&](int j) {
@@ -164,11 +181,12 @@ __global__ __launch_bounds__(kThreads) void k_gateup(const int8_t* __restrict__ 
   uint32_t rq[4][7];
   uint4 rx[8];
   uint32_t rd[4];
-  // L: sets up a new item when the loader enters one (reading the ids that
-  // fetch_ids wrote at least one barrier earlier), then only moves bits into
-  // registers and advances the loader.
+  // L: sets up a new item when the loader enters one (reading the ids this
+  // wave stored for it), then only moves bits into registers and advances
+  // the loader.
   auto load_next = [&]() {
     if (need_setup) {
+      flush_ids();  // the ids this setup reads, if their store is still pending
       setup(lj);
       need_setup = false;
     }
@@ -399,16 +417,19 @@ __global__ __launch_bounds__(kThreads) void k_gateup(const int8_t* __restrict__ 
       *reinterpret_cast<uint2*>(As[0] + ptid * kOpStride + kTabOff) = uint2{tlo, thi};
     }
     fetch_ids(0);
+    flush_ids();
     __syncthreads();
     load_next();
     stage(0);
     unpack(0);
-    __syncthreads();  // also orders fetch_ids(1) (in setup(0)) before setup(1)
+    flush_ids();
+    __syncthreads();
     if (n_steps > 1) load_next();
     for (int g = 0; g < n_steps; ++g) {
       if (g + 1 < n_steps) stage((g & 1) ^ 1);
       if (g + 2 < n_steps) load_next();
       if (g + 1 < n_steps) unpack((g & 1) ^ 1);
+      flush_ids();
       __syncthreads();
     }
   } else {
