@@ -8,8 +8,8 @@
 // kTileN pairs, and the dropped / valid / tile counts.  No host
 // synchronisation.
 //
-// Up to kSmallPairs pairs: one workgroup does everything (LDS histogram, block
-// scan, tile table, stable scatter in rounds of 1024 pairs).  Larger: three
+// Up to kSmallPairs pairs: one workgroup does everything (per-wave running
+// counts by expert, block scan, tile table, stable scatter).  Larger: three
 // passes over chunks of kRouteChunk pairs (per-chunk histograms; one
 // workgroup scanning chunks and experts; per-chunk stable scatter).  In both
 // the first launch carries extra workgroups that split the q8_1 activations
@@ -122,6 +122,47 @@ __device__ __forceinline__ int wave_rank(int e, bool valid, int nbits, int* cnt)
 
 // ---- small batches: everything in workgroup 0; workgroups 1 .. xblocks
 // split x, the ones after them zero y (atomic combine).
+//
+// Wave w takes pairs [256 w, 256 w + 256) in 4 rounds of 64: the stable rank
+// of a pair among the earlier pairs of its expert inside its wave's range is
+// the wave's running count of that expert (wcnt[w][e], in LDS, touched only
+// by wave w) plus its rank by ballot in the round.  After one barrier, one
+// thread per expert turns the 16 running counts into the first position of
+// each wave's run (expert offset + counts of the earlier waves), and each
+// pair lands at that position plus its rank.  6 barriers in all.
+constexpr int kSmallWaves = 16, kSmallRounds = kSmallPairs / (64 * kSmallWaves);  // 4 rounds of 64 per wave
+static_assert(kSmallRounds * 64 * kSmallWaves == kSmallPairs, "small route split");
+
+// Offsets, tile table and counts from per-expert totals c (thread e < E <=
+// blockDim.x): finish_offsets with one block scan over (count | tiles << 16),
+// which cannot carry at n <= kSmallPairs.  Returns expert e's first position.
+__device__ int finish_offsets_small(int c, int E, int bad, int32_t* __restrict__ offsets, int32_t* __restrict__ tiles,
+                                    int32_t* __restrict__ misc, int* scratch) {
+  static_assert(kSmallPairs < (1 << 16) && 1024 + kSmallPairs / kTileN < (1 << 15), "packed scan without carries");
+  const int e = threadIdx.x;
+  const int nt = (c + kTileN - 1) / kTileN;
+  int total;
+  const int packed = block_exclusive_scan(c | (nt << 16), scratch, &total);
+  const int off = packed & 0xffff, toff = packed >> 16;
+  if (e < E) {
+    offsets[e] = off;
+    for (int i = 0; i < nt; ++i) {
+      int32_t* te = tiles + kTileWords * (toff + i);
+      te[0] = e;
+      te[1] = off + i * kTileN;
+      te[2] = min(kTileN, c - i * kTileN);
+      te[3] = 0;
+    }
+  }
+  if (threadIdx.x == 0) {
+    offsets[E] = total & 0xffff;
+    misc[kMiscTiles] = total >> 16;
+    misc[kMiscDropped] = bad;
+    misc[kMiscValid] = total & 0xffff;
+  }
+  return off;
+}
+
 __global__ __launch_bounds__(1024) void k_route_small(const int32_t* __restrict__ idx, int n, int E, int nbits,
                                                       int32_t* __restrict__ offsets, int32_t* __restrict__ tiles,
                                                       int32_t* __restrict__ misc, int32_t* __restrict__ perm,
@@ -137,47 +178,54 @@ __global__ __launch_bounds__(1024) void k_route_small(const int32_t* __restrict_
     if (b < nxb) split_block(x, b, b, xc, xd);
     return;
   }
-  extern __shared__ int32_t sm[];  // cnt[E] | base[E] | wcnt[16][E]
+  extern __shared__ int32_t wcnt[];  // [kSmallWaves][E]: running counts, then each wave's first positions
   __shared__ int scratch[16];
   __shared__ int bad;
-  int* cnt = sm;
-  int* base = sm + E;
-  int* wcnt = sm + 2 * E;
-  for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
-  for (int i = threadIdx.x; i < 16 * E; i += blockDim.x) wcnt[i] = 0;
-  if (threadIdx.x == 0) bad = 0;
-  __syncthreads();
-  for (int p = threadIdx.x; p < n; p += blockDim.x) {
-    const int e = idx[p];
-    if ((unsigned)e < (unsigned)E)
-      atomicAdd(&cnt[e], 1);
-    else
-      atomicAdd(&bad, 1);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave's ids first (their loads overlap the clearing of the counts)
+  int ev[kSmallRounds];
+#pragma unroll
+  for (int r = 0; r < kSmallRounds; ++r) {
+    const int p = 64 * (kSmallRounds * wave + r) + lane;
+    ev[r] = p < n ? idx[p] : -1;
   }
+  for (int i = tid; i < kSmallWaves * E; i += blockDim.x) wcnt[i] = 0;
+  if (tid == 0) bad = 0;
   __syncthreads();
-  finish_offsets(cnt, base, E, bad, offsets, tiles, misc, scratch);
-  __syncthreads();
-  // stable scatter, 1024 pairs per round: rank in wave + counts of earlier waves
-  const int wave = threadIdx.x >> 6;
-  for (int r0 = 0; r0 < n; r0 += blockDim.x) {
-    const int p = r0 + threadIdx.x;
-    const int e = p < n ? idx[p] : -1;
-    const bool valid = (unsigned)e < (unsigned)E;
+  int* my = wcnt + wave * E;
+  int rk[kSmallRounds];
+  int nbad = 0;
+#pragma unroll
+  for (int r = 0; r < kSmallRounds; ++r) {
+    const int p = 64 * (kSmallRounds * wave + r) + lane;
+    const bool valid = (unsigned)ev[r] < (unsigned)E;
+    nbad += __popcll(__ballot(p < n && !valid));
     int c;
-    const int rank = wave_rank(e, valid, nbits, &c);
-    if (valid && rank == 0) wcnt[wave * E + e] = c;
-    __syncthreads();
-    if (valid) {
-      int before = 0;
-      for (int w = 0; w < wave; ++w) before += wcnt[w * E + e];  // 0 where a wave had no such id
-      perm[base[e] + before + rank] = p;
+    const int rank = wave_rank(ev[r], valid, nbits, &c);
+    // this wave alone reads and updates its counts: the read of every lane
+    // with id e is one instruction, the leader's update comes after it
+    const int base = valid ? my[ev[r]] : 0;
+    rk[r] = base + rank;
+    if (valid && rank == 0) my[ev[r]] = base + c;
+  }
+  if (lane == 0 && nbad) atomicAdd(&bad, nbad);
+  __syncthreads();
+  // per expert: exclusive sums over the waves, the expert's total, its offset
+  int c = 0;
+  if (tid < E)
+    for (int w = 0; w < kSmallWaves; ++w) {
+      const int v = wcnt[w * E + tid];
+      wcnt[w * E + tid] = c;
+      c += v;
     }
-    __syncthreads();
-    if (valid && rank == 0) {
-      atomicAdd(&base[e], c);
-      wcnt[wave * E + e] = 0;
-    }
-    __syncthreads();
+  const int first = finish_offsets_small(tid < E ? c : 0, E, bad, offsets, tiles, misc, scratch);
+  if (tid < E)
+    for (int w = 0; w < kSmallWaves; ++w) wcnt[w * E + tid] += first;
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < kSmallRounds; ++r) {
+    const int p = 64 * (kSmallRounds * wave + r) + lane;
+    if ((unsigned)ev[r] < (unsigned)E) perm[my[ev[r]] + rk[r]] = p;
   }
 }
 
@@ -329,8 +377,9 @@ hipError_t launch_route(const int32_t* idx, const uint8_t* x, const Shapes& s, c
   const unsigned xblocks = (unsigned)((nxb + kSplitPerBlock - 1) / kSplitPerBlock);
   const int64_t ny = yzero ? s.T * s.L : 0;
   const unsigned zblocks = (unsigned)((ny + kZeroPerBlock - 1) / kZeroPerBlock);
-  if (n <= kSmallPairs && s.E <= 512) {  // (2 + 16) * E ints of LDS
-    hipLaunchKernelGGL(k_route_small, dim3(1 + xblocks + zblocks), dim3(1024), (2 + 16) * s.E * sizeof(int32_t), st,
+  if (n <= kSmallPairs && s.E <= 512) {  // kSmallWaves * E ints of LDS
+    hipLaunchKernelGGL(k_route_small, dim3(1 + xblocks + zblocks), dim3(64 * kSmallWaves),
+                       kSmallWaves * s.E * sizeof(int32_t), st,
                        idx, (int)n, s.E, nbits, w.offsets, w.tiles, w.misc, w.perm, x, nxb, w.xc, w.xd, (int)xblocks,
                        yzero, ny);
     return hipGetLastError();
