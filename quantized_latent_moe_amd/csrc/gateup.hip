@@ -25,8 +25,8 @@
 //   4 producer waves: producer p owns weight rows 32p .. 32p+31 of the item
 //     (gate rows, then up rows) and tokens 32p .. 32p+31.  Per K step it loads
 //     into registers, through buffer loads whose out-of-range offset returns
-//     zeros for padding, its rows' Q3_K blocks as 16-bit words (rows are only
-//     2-byte aligned; 8 lanes read 16 contiguous bytes of a row), its tokens'
+//     zeros for padding, its rows' Q3_K blocks as dwords (blocks are only
+//     2-byte aligned: unaligned dword loads, 28 lanes a row), its tokens'
 //     int8 codes (16-byte loads) and fp32 block scales; writes them to LDS;
 //     and unpacks its rows from LDS: per (row, half, j) 32 codes become
 //     (4 - c) * sigma with one v_perm_b32 per 4 values against the 8-entry
@@ -121,12 +121,15 @@ __global__ __launch_bounds__(kThreads) void k_gateup(const int8_t* __restrict__ 
   const rsrc_t rx_src = make_rsrc(xc, (uint32_t)(T * L));
   const rsrc_t rd_src = make_rsrc(xd, (uint32_t)(T * nxb * 4));
   rsrc_t rw_src;
-  // raw: rows 32p + 8g + (lane >> 3), words (lane & 7) + 8m (m < 7; word 55
-  // re-reads word 0 and lands in the staging pad).  codes: tokens
-  // 32p + 4a + (lane >> 4), 16-byte chunk lane & 15.  scales: tokens
+  // raw: dword w = lane & 31 of rows 32p + 2i + (lane >> 5), i < 16 (w < 27:
+  // block bytes 4w .. 4w+3; w = 27: bytes 106 .. 109, so d lands in the high
+  // half of staged dword 27 and no load reaches past the block; w > 27 load
+  // nothing).  The blocks are only 2-byte aligned, so these are unaligned
+  // dword loads: two rows a load instead of 16 bytes of eight, which keeps
+  // the CU's address unit from queueing the four producers' loads.  codes:
+  // tokens 32p + 4a + (lane >> 4), 16-byte chunk lane & 15.  scales: tokens
   // 32p + 8c + (lane >> 3), block lane & 7.
-  int qoff[4], xoff[8], doff[4];
-  const int w55 = (lane & 7) == 7 ? -kQ3kBytes : 0;
+  int qoff = kOutOfRange, xoff[8], doff[4];
   int lj = 0, lsb = 0, qf0 = -1;
   bool need_setup = true;
   // The next item's token ids: producer p fetches those of its own tokens
@@ -158,13 +161,11 @@ __global__ __launch_bounds__(kThreads) void k_gateup(const int8_t* __restrict__ 
     rw_src = make_rsrc(gu + (int64_t)e * 2 * F * row_bytes, (uint32_t)(2 * F * row_bytes));
     if (it.f0 != qf0) {  // once per workgroup when the grid is a multiple of nft
       qf0 = it.f0;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int r = 32 * p + 8 * g + (lane >> 3);  // item row
-        const int rl = r < kFT ? r : r - kFT;
-        const int row = (r < kFT ? 0 : F) + it.f0 + rl;
-        qoff[g] = it.f0 + rl < F ? row * row_bytes + 2 * (lane & 7) : kOutOfRange;
-      }
+      // this producer's 32 rows: gate (p < 2) or up rows f0 + 32 (p & 1) ..,
+      // all inside F or all past it (F % 32 == 0)
+      const int rl0 = 32 * (p & 1), w = lane & 31;
+      const int row = (p < 2 ? 0 : F) + it.f0 + rl0 + (lane >> 5);
+      qoff = (it.f0 + rl0 < F && w < 28) ? row * row_bytes + (w < 27 ? 4 * w : 106) : kOutOfRange;
     }
 #pragma unroll
     for (int a = 0; a < 8; ++a) {
@@ -178,7 +179,7 @@ __global__ __launch_bounds__(kThreads) void k_gateup(const int8_t* __restrict__ 
     }
     fetch_ids(j + 1);
   };
-  uint32_t rq[4][7];
+  uint32_t rq[16];
   uint4 rx[8];
   uint32_t rd[4];
   // L: sets up a new item when the loader enters one (reading the ids this
@@ -194,11 +195,7 @@ __global__ __launch_bounds__(kThreads) void k_gateup(const int8_t* __restrict__ 
     const int sx = __builtin_amdgcn_readfirstlane(lsb * 256);
     const int sd = __builtin_amdgcn_readfirstlane(lsb * 32);
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-#pragma unroll
-      for (int m = 0; m < 6; ++m) rq[g][m] = buf_u16(rw_src, qoff[g] + 16 * m, sq);
-      rq[g][6] = buf_u16(rw_src, qoff[g] + 96 + w55, sq);
-    }
+    for (int i = 0; i < 16; ++i) rq[i] = buf_u32(rw_src, qoff, sq + 2 * i * row_bytes);
 #pragma unroll
     for (int a = 0; a < 8; ++a) rx[a] = buf_u128(rx_src, xoff[a], sx);
 #pragma unroll
@@ -212,11 +209,11 @@ __global__ __launch_bounds__(kThreads) void k_gateup(const int8_t* __restrict__ 
   // registers are free again after it, so the next step's loads are issued
   // before the unpack and their latency overlaps it.
   auto stage = [&](int b) {
-    uint16_t* raw16 = reinterpret_cast<uint16_t*>(raw) + (32 * p + (lane >> 3)) * (kRawStride / 2) + (lane & 7);
+    uint32_t* raw32 = reinterpret_cast<uint32_t*>(raw) + (32 * p + (lane >> 5)) * (kRawStride / 4) + (lane & 31);
+    if ((lane & 31) < 28) {
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
-#pragma unroll
-      for (int m = 0; m < 7; ++m) raw16[8 * g * (kRawStride / 2) + 8 * m] = (uint16_t)rq[g][m];
+      for (int i = 0; i < 16; ++i) raw32[2 * i * (kRawStride / 4)] = rq[i];
+    }
 #pragma unroll
     for (int a = 0; a < 8; ++a)
       *reinterpret_cast<uint4*>(Bs[b] + (32 * p + 4 * a + (lane >> 4)) * kOpStride + 16 * (lane & 15)) = rx[a];
@@ -231,10 +228,10 @@ __global__ __launch_bounds__(kThreads) void k_gateup(const int8_t* __restrict__ 
     const uint8_t* ublk = raw + ur * kRawStride;
     const uint4 h0 = *reinterpret_cast<const uint4*>(ublk);
     const uint4 h1 = *reinterpret_cast<const uint4*>(ublk + 16);
-    const uint4 scw = *reinterpret_cast<const uint4*>(ublk + 96);  // scales[12] | d | pad
+    const uint4 scw = *reinterpret_cast<const uint4*>(ublk + 96);  // scales[12] | scales[10..11] | d
     const uint32_t hm[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
     const uint32_t scb[3] = {scw.x, scw.y, scw.z};
-    if (lane < 32) dws[b][ur] = half_bits_to_float(scw.w & 0xffffu);
+    if (lane < 32) dws[b][ur] = half_bits_to_float(scw.w >> 16);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int un = u >> 1, uj = 2 * (u & 1) + (lane >> 5);
