@@ -289,15 +289,12 @@ struct DItem {
   int e, pos0, cnt, l0;
 };
 
-__device__ __forceinline__ DItem ditem(int i, int nlt, const int32_t* tiles) {
-  DItem it;
-  const int tile = i / nlt;
-  it.l0 = (i - tile * nlt) * kWsLT;
-  it.e = tiles[kTileWords * tile];
-  it.pos0 = tiles[kTileWords * tile + 1];
-  it.cnt = tiles[kTileWords * tile + 2];  // at most kTileN == kWsNT
-  return it;
-}
+// Where item j of a workgroup sits in its XCD's list (tile major): q = wl + j
+// * G8 as the tile q / nlt past the range's first tile and the row tile
+// q % nlt, stepped from item to item without a division.
+struct DItemPos {
+  int qd, qm;
+};
 
 template <bool PROBE, int FMT, bool ATOMIC>
 __global__ __launch_bounds__(kWsThreads) void k_down(const uint8_t* __restrict__ dn, const float* __restrict__ router_w,
@@ -329,9 +326,25 @@ __global__ __launch_bounds__(kWsThreads) void k_down(const uint8_t* __restrict__
   const int x_items = (t1 - t0) * nlt;
   if (wl >= x_items) return;
   const int my_items = (x_items - 1 - wl) / G8 + 1;
-  auto item_of = [&](int j) {
-    const int q = wl + j * G8;
-    return (t0 + q / nlt) * nlt + q % nlt;  // global item index: tile * nlt + row tile
+  const int g8d = G8 / nlt, g8m = G8 - g8d * nlt;
+  const DItemPos first_pos = {wl / nlt, wl % nlt};
+  auto next_pos = [&](DItemPos a) {
+    a.qd += g8d;
+    a.qm += g8m;
+    if (a.qm >= nlt) {
+      a.qm -= nlt;
+      ++a.qd;
+    }
+    return a;
+  };
+  auto item_at = [&](DItemPos a) {
+    DItem it;
+    const int tile = t0 + a.qd;
+    it.l0 = a.qm * kWsLT;
+    it.e = tiles[kTileWords * tile];
+    it.pos0 = tiles[kTileWords * tile + 1];
+    it.cnt = tiles[kTileWords * tile + 2];  // at most kTileN == kWsNT
+    return it;
   };
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: role branches stay scalar
@@ -351,8 +364,10 @@ __global__ __launch_bounds__(kWsThreads) void k_down(const uint8_t* __restrict__
     int qoff[5], hoff[8], soff[4];
     int lj = 0, lsb = 0, ql0 = -1;
     bool need_setup = true;
-    auto setup = [&](int j) {
-      const DItem it = ditem(item_of(j), nlt, tiles);
+    DItemPos lpos = first_pos;  // item lj's position
+    auto setup = [&]() {
+      const DItem it = item_at(lpos);
+      lpos = next_pos(lpos);
       const int e = __builtin_amdgcn_readfirstlane(it.e);
       rw_src = make_rsrc(dn + (int64_t)e * L * row_bytes, (uint32_t)(L * row_bytes));
       if (it.l0 != ql0) {  // once per workgroup when the grid is a multiple of nlt
@@ -379,7 +394,7 @@ __global__ __launch_bounds__(kWsThreads) void k_down(const uint8_t* __restrict__
     uint32_t rd[4];
     auto load_next = [&]() {
       if (need_setup) {
-        setup(lj);
+        setup();
         need_setup = false;
       }
       const int sq = __builtin_amdgcn_readfirstlane(lsb * kWsStep);  // scalar offsets stay in SGPRs
@@ -474,7 +489,8 @@ __global__ __launch_bounds__(kWsThreads) void k_down(const uint8_t* __restrict__
   for (int i = 0; i < 16; ++i) magic[i] = kMagicBits;
   float acc0[16], acc1[16];
   int cj = 0, csb = 0;
-  DItem cur = ditem(item_of(0), nlt, tiles);
+  DItemPos cpos = first_pos;  // item cj's position
+  DItem cur = item_at(cpos);
   int pair0 = -1, pair1 = -1;
   float w0 = 0.f, w1 = 0.f;
   // one K step over both halves (TWO) or the first only
@@ -552,7 +568,10 @@ __global__ __launch_bounds__(kWsThreads) void k_down(const uint8_t* __restrict__
       // the item's last step (the barrier that ends a step waits for all
       // scalar loads), the pairs at the item's first step and their router
       // weights one step later (the weight's address needs the pair).
-      if (csb == nsb - 1 && cj + 1 < my_items) nxt = ditem(item_of(cj + 1), nlt, tiles);
+      if (csb == nsb - 1 && cj + 1 < my_items) {
+        cpos = next_pos(cpos);
+        nxt = item_at(cpos);
+      }
       if (csb == 0) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc0[i] = acc1[i] = 0.f;

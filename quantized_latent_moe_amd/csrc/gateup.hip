@@ -67,15 +67,12 @@ struct Item {
   int e, pos0, cnt, f0;
 };
 
-__device__ __forceinline__ Item item_info(int i, int nft, const int32_t* tiles) {
-  Item it;
-  const int tile = i / nft;
-  it.f0 = (i - tile * nft) * kFT;
-  it.e = tiles[kTileWords * tile];
-  it.pos0 = tiles[kTileWords * tile + 1];
-  it.cnt = tiles[kTileWords * tile + 2];  // at most kTileN == kNT
-  return it;
-}
+// Where item j of a workgroup sits in its XCD's list (tile major): q = wl + j
+// * G8 as the tile q / nft past the range's first tile and the feature tile
+// q % nft, stepped from item to item without a division.
+struct ItemPos {
+  int qd, qm;
+};
 
 template <bool PROBE>
 __global__ __launch_bounds__(kThreads) void k_gateup(const int8_t* __restrict__ xc, const float* __restrict__ xd,
@@ -103,9 +100,25 @@ __global__ __launch_bounds__(kThreads) void k_gateup(const int8_t* __restrict__ 
   const int x_items = (t1 - t0) * nft;
   if (wl >= x_items) return;
   const int my_items = (x_items - 1 - wl) / G8 + 1;
-  auto item_of = [&](int j) {
-    const int q = wl + j * G8;
-    return (t0 + q / nft) * nft + q % nft;  // global item index: tile * nft + feature tile
+  const int g8d = G8 / nft, g8m = G8 - g8d * nft;
+  const ItemPos first_pos = {wl / nft, wl % nft};
+  auto next_pos = [&](ItemPos a) {
+    a.qd += g8d;
+    a.qm += g8m;
+    if (a.qm >= nft) {
+      a.qm -= nft;
+      ++a.qd;
+    }
+    return a;
+  };
+  auto item_at = [&](ItemPos a) {
+    Item it;
+    const int tile = t0 + a.qd;
+    it.f0 = a.qm * kFT;
+    it.e = tiles[kTileWords * tile];
+    it.pos0 = tiles[kTileWords * tile + 1];
+    it.cnt = tiles[kTileWords * tile + 2];  // at most kTileN == kNT
+    return it;
   };
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -140,9 +153,9 @@ __global__ __launch_bounds__(kThreads) void k_gateup(const int8_t* __restrict__ 
   // the next setup if that comes first.
   int pend_pair = -1, pend_buf = 0;
   bool pend = false;
-  auto fetch_ids = [&](int j) {
+  auto fetch_ids = [&](int j, ItemPos at) {
     if (j < my_items) {
-      const Item it = item_info(item_of(j), nft, tiles);
+      const Item it = item_at(at);
       const int n = 32 * p + lane;
       if (lane < 32) pend_pair = n < it.cnt ? perm[it.pos0 + n] : -1;
       pend_buf = j & 1;
@@ -155,8 +168,9 @@ __global__ __launch_bounds__(kThreads) void k_gateup(const int8_t* __restrict__ 
       pend = false;
     }
   };
+  ItemPos lpos = first_pos;  // item lj's position
   auto setup = [&](int j) {
-    const Item it = item_info(item_of(j), nft, tiles);
+    const Item it = item_at(lpos);
     const int e = __builtin_amdgcn_readfirstlane(it.e);  // uniform: the descriptor lives in SGPRs
     rw_src = make_rsrc(gu + (int64_t)e * 2 * F * row_bytes, (uint32_t)(2 * F * row_bytes));
     if (it.f0 != qf0) {  // once per workgroup when the grid is a multiple of nft
@@ -177,7 +191,8 @@ __global__ __launch_bounds__(kThreads) void k_gateup(const int8_t* __restrict__ 
       const int t = ids[j & 1][32 * p + 8 * c + (lane >> 3)];
       doff[c] = t >= 0 ? (t * nxb + (lane & 7)) * 4 : kOutOfRange;
     }
-    fetch_ids(j + 1);
+    lpos = next_pos(lpos);
+    fetch_ids(j + 1, lpos);
   };
   uint32_t rq[16];
   uint4 rx[8];
@@ -285,7 +300,8 @@ __global__ __launch_bounds__(kThreads) void k_gateup(const int8_t* __restrict__ 
   for (int i = 0; i < 16; ++i) asm volatile("v_mov_b32 %0, 0x4b400000" : "=v"(magic[i]));
   float accg[16], accu[16];
   int cj = 0, csb = 0;  // item index and super-block of the MFMA step
-  Item cur = item_info(item_of(0), nft, tiles);
+  ItemPos cpos = first_pos;  // item cj's position
+  Item cur = item_at(cpos);
 
   auto mfma_step = [&](auto grp_tag, int b) {
     constexpr int GRP = decltype(grp_tag)::value;
@@ -413,7 +429,7 @@ __global__ __launch_bounds__(kThreads) void k_gateup(const int8_t* __restrict__ 
       q3_tables(ptid - 32, tlo, thi);
       *reinterpret_cast<uint2*>(As[0] + ptid * kOpStride + kTabOff) = uint2{tlo, thi};
     }
-    fetch_ids(0);
+    fetch_ids(0, first_pos);
     flush_ids();
     __syncthreads();
     load_next();
@@ -440,7 +456,10 @@ __global__ __launch_bounds__(kThreads) void k_gateup(const int8_t* __restrict__ 
         // the next item's tile entry is read at the start of the item's last
         // step, so the barrier that ends the step (which waits for all scalar
         // loads) does not wait for it
-        if (csb == nsb - 1 && cj + 1 < my_items) nxt = item_info(item_of(cj + 1), nft, tiles);
+        if (csb == nsb - 1 && cj + 1 < my_items) {
+          cpos = next_pos(cpos);
+          nxt = item_at(cpos);
+        }
         mfma_step(grp_tag, g & 1);
         if (++csb == nsb) {
           epilogue();
