@@ -52,15 +52,12 @@ struct Item {
   int e, pos0, cnt, f0;
 };
 
-__device__ __forceinline__ Item item_info(int i, int nft, const int32_t* tiles) {
-  Item it;
-  const int tile = i / nft;
-  it.f0 = (i - tile * nft) * kFT;
-  it.e = tiles[kTileWords * tile];
-  it.pos0 = tiles[kTileWords * tile + 1];
-  it.cnt = tiles[kTileWords * tile + 2];
-  return it;
-}
+// Where item j of a workgroup sits in its XCD's list (tile major): q = wl + j
+// * G8 as the tile q / nft past the range's first tile and the feature tile
+// q % nft, stepped from item to item without a division.
+struct ItemPos {
+  int qd, qm;
+};
 
 template <bool PROBE>
 __global__ __launch_bounds__(kThreads) void k_gateup_q40(const int8_t* __restrict__ xc, const float* __restrict__ xd,
@@ -83,9 +80,25 @@ __global__ __launch_bounds__(kThreads) void k_gateup_q40(const int8_t* __restric
   const int x_items = (t1 - t0) * nft;
   if (wl >= x_items) return;
   const int my_items = (x_items - 1 - wl) / G8 + 1;
-  auto item_of = [&](int j) {
-    const int q = wl + j * G8;
-    return (t0 + q / nft) * nft + q % nft;  // global item index: tile * nft + feature tile
+  const int g8d = G8 / nft, g8m = G8 - g8d * nft;
+  const ItemPos first_pos = {wl / nft, wl % nft};
+  auto next_pos = [&](ItemPos a) {
+    a.qd += g8d;
+    a.qm += g8m;
+    if (a.qm >= nft) {
+      a.qm -= nft;
+      ++a.qd;
+    }
+    return a;
+  };
+  auto item_at = [&](ItemPos a) {
+    Item it;
+    const int tile = t0 + a.qd;
+    it.f0 = a.qm * kFT;
+    it.e = tiles[kTileWords * tile];
+    it.pos0 = tiles[kTileWords * tile + 1];
+    it.cnt = tiles[kTileWords * tile + 2];
+    return it;
   };
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: role branches stay scalar
@@ -96,7 +109,6 @@ __global__ __launch_bounds__(kThreads) void k_gateup_q40(const int8_t* __restric
   if (wave >= kConsumers) {
     // =============================== producer ===============================
     const int p = wave - kConsumers;
-    const int ptid = tid - 64 * kConsumers;  // 0 .. 255
     const rsrc_t rx_src = make_rsrc(xc, (uint32_t)(T * L));
     const rsrc_t rd_src = make_rsrc(xd, (uint32_t)(T * nb * 4));
     rsrc_t rw_src;
@@ -106,14 +118,19 @@ __global__ __launch_bounds__(kThreads) void k_gateup_q40(const int8_t* __restric
     int woff[4], xoff[8], doff[4];
     int lj = 0, lsb = 0;
     bool need_setup = true;
-    auto fetch_ids = [&](int j) {
+    // Producer p fetches the token ids of its own tokens 32p .. 32p+31, so
+    // only the wave that stores an entry reads it (with one K step per item
+    // the next setup can follow without a barrier between).
+    auto fetch_ids = [&](int j, ItemPos at) {
       if (j < my_items) {
-        const Item it = item_info(item_of(j), nft, tiles);
-        if (ptid < kNT) ids[j & 1][ptid] = ptid < it.cnt ? perm[it.pos0 + ptid] / k : -1;
+        const Item it = item_at(at);
+        const int n = 32 * p + lane;
+        if (lane < 32) ids[j & 1][n] = n < it.cnt ? perm[it.pos0 + n] / k : -1;
       }
     };
+    ItemPos lpos = first_pos;  // item lj's position
     auto setup = [&](int j) {
-      const Item it = item_info(item_of(j), nft, tiles);
+      const Item it = item_at(lpos);
       const int e = __builtin_amdgcn_readfirstlane(it.e);  // uniform: the descriptor lives in SGPRs
       rw_src = make_rsrc(gu + (int64_t)e * 2 * F * row_bytes, (uint32_t)(2 * F * row_bytes));
 #pragma unroll
@@ -133,7 +150,8 @@ __global__ __launch_bounds__(kThreads) void k_gateup_q40(const int8_t* __restric
         const int t = ids[j & 1][32 * p + 8 * c + (lane >> 3)];
         doff[c] = t >= 0 ? (t * nb + (lane & 7)) * 4 : kOutOfRange;
       }
-      fetch_ids(j + 1);
+      lpos = next_pos(lpos);
+      fetch_ids(j + 1, lpos);
     };
     uint4 rq[4], rx[8];
     uint32_t rwd[4], rd[4];
@@ -184,11 +202,11 @@ __global__ __launch_bounds__(kThreads) void k_gateup_q40(const int8_t* __restric
         dxs[b][n][kb] = as_float((int)rd[c]);
       }
     };
-    fetch_ids(0);
+    fetch_ids(0, first_pos);
     __syncthreads();
     load_next();
     stage(0);
-    __syncthreads();  // also orders fetch_ids(1) (in setup(0)) before setup(1)
+    __syncthreads();
     if (n_steps > 1) load_next();
     for (int g = 0; g < n_steps; ++g) {
       if (g + 1 < n_steps) stage((g & 1) ^ 1);
@@ -207,7 +225,8 @@ __global__ __launch_bounds__(kThreads) void k_gateup_q40(const int8_t* __restric
   for (int i = 0; i < 16; ++i) magic[i] = kMagicBits;
   float accg[16], accu[16];
   int cj = 0, csb = 0;
-  Item cur = item_info(item_of(0), nft, tiles);
+  ItemPos cpos = first_pos;  // item cj's position
+  Item cur = item_at(cpos);
 
   auto mfma_step = [&](auto grp_tag, int b) {
     constexpr int GRP = decltype(grp_tag)::value;
@@ -312,7 +331,10 @@ __global__ __launch_bounds__(kThreads) void k_gateup_q40(const int8_t* __restric
       if (++csb == nsb) {
         epilogue();
         csb = 0;
-        if (++cj < my_items) cur = item_info(item_of(cj), nft, tiles);
+        if (++cj < my_items) {
+          cpos = next_pos(cpos);
+          cur = item_at(cpos);
+        }
       }
       __syncthreads();
     }
