@@ -637,8 +637,10 @@ def q4_0_report(steps, warmup, gateup_q4_0, workloads=("prefill_5k", "decode")):
         ms, _ = st.time_steps(n, warmup)
         stages = st.stage_times(n)
         alg = algorithmic(wl, st.inputs.router_idx, gateup_q4_0=gateup_q4_0)
+        # the decode workload runs the two-launch path: only gate/up and down are stages there
+        shown = ("gateup", "down") if name == "decode" else names
         r = {"workload": name, "ms_per_step": round(ms, 5), "tokens_per_s": round(wl.T / (ms * 1e-3), 1),
-             "stage_ms": {k: round(v, 5) for k, v in zip(names, stages)}}
+             "stage_ms": {k: round(v, 5) for k, v in zip(names, stages) if k in shown}}
         if name == "prefill_5k":
             fold = alg["fold_down"] / (stages[2] * 1e-3) / 1e12
             r["down_roofline"] = {"bound": "alu", "kernel": "k_down (Q4_0)", "achieved": round(fold, 2),
@@ -739,14 +741,19 @@ def main():
     stages = st.stage_times(args.steps)
     router_us, _ = st.router_and_graph(args.steps)
     names = ["route", "gateup", "down", "combine"]
-    print("[bench] stage ms: " + ", ".join(f"{n}={v:.4f}" for n, v in zip(names, stages)), file=sys.stderr,
+    # decode-sized batches (at most 64 routed pairs, L <= 1024, F <= 2048) make
+    # two launches, the GEMV-shaped gate/up and down kernels: no route or
+    # combine kernel runs between their events
+    small = wl.T * wl.k <= 64 and wl.L <= 1024 and wl.F <= 2048
+    shown = ["gateup", "down"] if small else names
+    print("[bench] stage ms: " + ", ".join(f"{n}={stages[names.index(n)]:.4f}" for n in shown), file=sys.stderr,
           flush=True)
     ops = {"gateup": alg["ops_gateup"], "down": alg["ops_down"]}
     folds = {"gateup": alg["fold_gateup"], "down": alg["fold_down"]}
     dom = max(("gateup", "down"), key=lambda n: stages[names.index(n)])
     dom_ms = stages[names.index(dom)]
     achieved = ops[dom] / (dom_ms * 1e-3) / 1e12
-    kernel = {"gateup": "k_gateup", "down": "k_down"}[dom]
+    kernel = ({"gateup": "k_dec_gateup", "down": "k_dec_down"} if small else {"gateup": "k_gateup", "down": "k_down"})[dom]
     fold_tops = folds[dom] / (dom_ms * 1e-3) / 1e12
     # The dominant kernel against the int8 MFMA peak (the metric's roof).  Its
     # binding limit is the per-block fp32 scale fold on the VALU (2 unpacked
@@ -775,7 +782,7 @@ def main():
                    "zipf_s": wl.zipf_s, "n_masked": wl.n_masked, "seed": wl.seed, "pairs": alg["pairs"],
                    "active_experts": alg["active"]},
         "roofline": roofline,
-        "stage_ms": {n: round(v, 5) for n, v in zip(names, stages)},
+        "stage_ms": {n: round(stages[names.index(n)], 5) for n in shown},
         "router_us": round(router_us, 2),
         "stage_int8_frac": round(total_ops / (ms * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4),
         "stage_hbm_gbs": round(alg["bytes"] / (ms * 1e-3) / 1e9, 1),

@@ -120,12 +120,24 @@ __global__ __launch_bounds__(kThreads) void k_gateup_q40(const int8_t* __restric
     bool need_setup = true;
     // Producer p fetches the token ids of its own tokens 32p .. 32p+31, so
     // only the wave that stores an entry reads it (with one K step per item
-    // the next setup can follow without a barrier between).
+    // the next setup can follow without a barrier between).  The pair loads
+    // are issued in setup; their LDS store (flush_ids) comes at the end of
+    // the step, or at the next setup if that comes first.
+    int pend_pair = -1, pend_buf = 0;
+    bool pend = false;
     auto fetch_ids = [&](int j, ItemPos at) {
       if (j < my_items) {
         const Item it = item_at(at);
         const int n = 32 * p + lane;
-        if (lane < 32) ids[j & 1][n] = n < it.cnt ? perm[it.pos0 + n] / k : -1;
+        if (lane < 32) pend_pair = n < it.cnt ? perm[it.pos0 + n] : -1;
+        pend_buf = j & 1;
+        pend = true;
+      }
+    };
+    auto flush_ids = [&]() {
+      if (pend) {
+        if (lane < 32) ids[pend_buf][32 * p + lane] = pend_pair >= 0 ? pend_pair / k : -1;
+        pend = false;
       }
     };
     ItemPos lpos = first_pos;  // item lj's position
@@ -157,6 +169,7 @@ __global__ __launch_bounds__(kThreads) void k_gateup_q40(const int8_t* __restric
     uint32_t rwd[4], rd[4];
     auto load_next = [&]() {
       if (need_setup) {
+        flush_ids();  // the ids this setup reads, if their store is still pending
         setup(lj);
         need_setup = false;
       }
@@ -203,14 +216,17 @@ __global__ __launch_bounds__(kThreads) void k_gateup_q40(const int8_t* __restric
       }
     };
     fetch_ids(0, first_pos);
+    flush_ids();
     __syncthreads();
     load_next();
     stage(0);
+    flush_ids();
     __syncthreads();
     if (n_steps > 1) load_next();
     for (int g = 0; g < n_steps; ++g) {
       if (g + 1 < n_steps) stage((g & 1) ^ 1);
       if (g + 2 < n_steps) load_next();
+      flush_ids();
       __syncthreads();
     }
     return;
