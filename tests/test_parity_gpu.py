@@ -245,8 +245,12 @@ def test_invalid_and_duplicate_ids():
 # The large-batch counting sort at shapes that take each branch of its chunk
 # scan: several lanes per expert (E = 128), one lane per expert (E = 600),
 # and chunk histograms too large for the scan's LDS stage (36 chunks x 1024
-# experts); with invalid ids mixed in.  Routing only: perm, offsets, dropped.
-@pytest.mark.parametrize("T,E,k", [(4000, 128, 8), (3000, 600, 8), (9000, 1024, 4)], ids=lambda v: str(v))
+# experts); and the one-workgroup sort (at most 4096 pairs and 512 experts)
+# at its limits: 4088 pairs over 512 experts (the last wave's range part
+# full), 4000 over 300, 80 over 7.  With invalid ids mixed in.  Routing only:
+# perm, offsets, dropped.
+@pytest.mark.parametrize("T,E,k", [(4000, 128, 8), (3000, 600, 8), (9000, 1024, 4),
+                                   (511, 512, 8), (1000, 300, 4), (20, 7, 4)], ids=lambda v: str(v))
 def test_route_scan_branches(T, E, k):
     wl = Workload(f"route_{T}_{E}", T=T, L=256, F=128, E=E, k=k, zipf_s=1.1, seed=21)
     say(f"route case T={T} E={E} k={k}")
