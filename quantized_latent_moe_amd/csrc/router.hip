@@ -11,7 +11,11 @@
 //   picks: the k largest logits, equal logits in ascending expert order;
 //   w_j = exp(l_j - l_max) / sum_i exp(l_i - l_max) over the picks (fp32).
 //
-// One wave per token.  Lane l holds logits l, l + 64, ... in registers (as
+// Up to 256 experts and 16 picks, from 256 tokens: a 16-lane row per token,
+// four tokens a wave (k_router_topk16, below).  Otherwise one wave per token
+// (at a few tokens the rounds' latency, not the wave count, sets the time,
+// and a wave per token has the shorter chain).  Lane l
+// holds logits l, l + 64, ... in registers (as
 // many slots as E needs, by instantiation).  Each
 // of the k rounds takes every lane's best remaining logit (ascending index,
 // strict compare, so ties keep the lower expert), reduces (value, index)
@@ -115,11 +119,86 @@ __global__ __launch_bounds__(64 * kRouterWaves) void k_router_topk(const float* 
   }
 }
 
+// The same rule for E <= 256 and k <= 16 with a 16-lane row (a DPP row) per
+// token, four tokens a wave: lane l of a row holds logits l, l + 16, ...; the
+// row's best (value, index) comes from four DPP steps that leave it in every
+// lane of the row (quad swaps, half-row and row mirrors), so a round needs no
+// readlane, and a wave's rounds serve four tokens.  Lane j of a row keeps pick
+// j; the k exponentials are summed by the same four steps (every lane of the
+// row ends with the same sum, bit for bit).
+template <int P>
+__global__ __launch_bounds__(64 * kRouterWaves) void k_router_topk16(const float* __restrict__ logits, int64_t T,
+                                                                      int E, int k, int32_t* __restrict__ idx,
+                                                                      float* __restrict__ w) {
+  const int lane = threadIdx.x & 63, rl = lane & 15;
+  const int64_t t0 = ((int64_t)blockIdx.x * kRouterWaves + (threadIdx.x >> 6)) * 4;
+  if (t0 >= T) return;  // wave-uniform
+  const int64_t t = t0 + (lane >> 4);
+  const bool live = t < T;
+  const rsrc_t rlg = make_rsrc(logits + (live ? t : 0) * E, live ? (uint32_t)E * 4 : 0u);
+  float v[P];
+  uint32_t taken = 0;  // bit i: entry i of this lane already picked (or past E)
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    const int e = rl + 16 * i;
+    v[i] = as_float((int)buf_u32(rlg, e < E ? 4 * e : kOutOfRange, 0));
+    if (e >= E) {
+      v[i] = -INFINITY;
+      taken |= 1u << i;
+    }
+  }
+  int my_idx = 0;
+  float my_val = -INFINITY, top = -INFINITY;
+  for (int j = 0; j < k; ++j) {
+    // this lane's best remaining entry (ascending index, strict compare)
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      const bool free_i = !((taken >> i) & 1u);
+      if (free_i && (v[i] > bv || bi == 0x7fffffff)) {
+        bv = v[i];
+        bi = rl + 16 * i;
+      }
+    }
+    dpp_step<0xB1, 0xF>(bv, bi);   // quad_perm [1,0,3,2]
+    dpp_step<0x4E, 0xF>(bv, bi);   // quad_perm [2,3,0,1]
+    dpp_step<0x141, 0xF>(bv, bi);  // row_half_mirror
+    dpp_step<0x140, 0xF>(bv, bi);  // row_mirror: every lane of the row holds the row's best
+    if ((bi & 15) == rl) taken |= 1u << (bi >> 4);
+    if (j == 0) top = bv;
+    if (rl == j) {
+      my_idx = bi;
+      my_val = bv;
+    }
+  }
+  // weights: softmax of the picked logits (pick 0 is the largest)
+  float ex = rl < k ? expf(my_val - top) : 0.f;
+  float sum = ex;
+  sum += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, sum), __builtin_bit_cast(int, sum), 0xB1, 0xF, 0xF, false));
+  sum += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, sum), __builtin_bit_cast(int, sum), 0x4E, 0xF, 0xF, false));
+  sum += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, sum), __builtin_bit_cast(int, sum), 0x141, 0xF, 0xF, false));
+  sum += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, sum), __builtin_bit_cast(int, sum), 0x140, 0xF, 0xF, false));
+  if (live && rl < k) {
+    idx[t * k + rl] = my_idx;
+    w[t * k + rl] = ex / sum;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_router_topk(const float* logits, int64_t T, int E, int k, int32_t* idx, float* w, hipStream_t st) {
-  const dim3 grid((unsigned)((T + kRouterWaves - 1) / kRouterWaves));
   const dim3 block(64 * kRouterWaves);
+  if (E <= 256 && k <= 16 && T >= 256) {  // four tokens a wave (fewer tokens: more waves, each with a shorter chain)
+    const dim3 grid16((unsigned)((T + 4 * kRouterWaves - 1) / (4 * kRouterWaves)));
+    if (E <= 16) hipLaunchKernelGGL(k_router_topk16<1>, grid16, block, 0, st, logits, T, E, k, idx, w);
+    else if (E <= 32) hipLaunchKernelGGL(k_router_topk16<2>, grid16, block, 0, st, logits, T, E, k, idx, w);
+    else if (E <= 64) hipLaunchKernelGGL(k_router_topk16<4>, grid16, block, 0, st, logits, T, E, k, idx, w);
+    else if (E <= 128) hipLaunchKernelGGL(k_router_topk16<8>, grid16, block, 0, st, logits, T, E, k, idx, w);
+    else hipLaunchKernelGGL(k_router_topk16<16>, grid16, block, 0, st, logits, T, E, k, idx, w);
+    return hipGetLastError();
+  }
+  const dim3 grid((unsigned)((T + kRouterWaves - 1) / kRouterWaves));
   if (E <= 64) hipLaunchKernelGGL(k_router_topk<1>, grid, block, 0, st, logits, T, E, k, idx, w);
   else if (E <= 128) hipLaunchKernelGGL(k_router_topk<2>, grid, block, 0, st, logits, T, E, k, idx, w);
   else if (E <= 256) hipLaunchKernelGGL(k_router_topk<4>, grid, block, 0, st, logits, T, E, k, idx, w);

@@ -51,8 +51,12 @@ def _check(logits, k, label):
     assert (err <= bound).all()
 
 
+# From 256 tokens, E <= 256 and k <= 16 take the four-tokens-a-wave kernel:
+# (1000, 128, 8), (300, 256, 1), (401, 16, 16) (a part-full last wave), (513, 40, 5)
+# and (600, 200, 16) there; the rest the wave-per-token one.
 @pytest.mark.parametrize("T,E,k,seed", [(1000, 128, 8, 0), (37, 8, 2, 1), (64, 1024, 64, 2), (100, 600, 10, 3),
-                                         (5, 1, 1, 4), (33, 65, 64, 5), (7, 64, 64, 6), (300, 256, 1, 7)],
+                                         (5, 1, 1, 4), (33, 65, 64, 5), (7, 64, 64, 6), (300, 256, 1, 7),
+                                         (401, 16, 16, 8), (513, 40, 5, 9), (600, 200, 16, 10)],
                          ids=lambda v: str(v))
 def test_router_matches_oracle(T, E, k, seed):
     rng = np.random.default_rng(seed)
@@ -60,9 +64,11 @@ def test_router_matches_oracle(T, E, k, seed):
     _check(logits, k, f"T={T} E={E} k={k}")
 
 
-def test_router_ties_and_masked_experts():
+# T = 200 takes the wave-per-token kernel, T = 600 the four-tokens-a-wave one
+@pytest.mark.parametrize("T", [200, 600])
+def test_router_ties_and_masked_experts(T):
     rng = np.random.default_rng(9)
-    T, E, k = 200, 96, 8
+    E, k = 96, 8
     logits = (rng.integers(0, 4, (T, E)) * 0.5).astype(np.float32)     # many exact ties
     logits[:20, 1::2] = -np.inf                                           # masked experts
     logits[20:25, :] = -np.inf
