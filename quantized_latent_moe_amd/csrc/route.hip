@@ -77,8 +77,10 @@ __device__ int block_exclusive_scan(int v, int* scratch, int* total) {
 
 // Offsets, tile table and counts from per-expert totals cnt[e] (e < E <=
 // blockDim.x = 1024, in LDS); leaves each expert's first position in
-// first[e].  Every thread of the workgroup calls it.
-__device__ void finish_offsets(const int* cnt, int* first, int E, int bad, int32_t* __restrict__ offsets,
+// first[e] and its first tile in tstart[e].  Every thread of the workgroup
+// calls it.  The tile table is written by all threads, a tile each in turn
+// (a busy expert has hundreds of tiles: one thread would issue them all).
+__device__ void finish_offsets(const int* cnt, int* first, int* tstart, int E, int bad, int32_t* __restrict__ offsets,
                                int32_t* __restrict__ tiles, int32_t* __restrict__ misc, int* scratch) {
   const int e = threadIdx.x;
   const int c = e < E ? cnt[e] : 0;
@@ -88,14 +90,24 @@ __device__ void finish_offsets(const int* cnt, int* first, int E, int bad, int32
   const int toff = block_exclusive_scan(nt, scratch, &ttotal);
   if (e < E) {
     first[e] = off;
+    tstart[e] = toff;
     offsets[e] = off;
-    for (int i = 0; i < nt; ++i) {
-      int32_t* te = tiles + kTileWords * (toff + i);
-      te[0] = e;
-      te[1] = off + i * kTileN;
-      te[2] = min(kTileN, c - i * kTileN);
-      te[3] = 0;
+  }
+  __syncthreads();
+  for (int q = threadIdx.x; q < ttotal; q += blockDim.x) {
+    // the tile's expert: the last e with tstart[e] <= q (experts without
+    // tiles share their start with the next one, so the last has tiles)
+    int lo = 0, hi = E - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (tstart[mid] <= q) lo = mid; else hi = mid - 1;
     }
+    const int i = q - tstart[lo];
+    int32_t* te = tiles + kTileWords * q;
+    te[0] = lo;
+    te[1] = first[lo] + i * kTileN;
+    te[2] = min(kTileN, cnt[lo] - i * kTileN);
+    te[3] = 0;
   }
   if (threadIdx.x == 0) {
     offsets[E] = total;
@@ -274,6 +286,7 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ chunk
                                                      int32_t* __restrict__ misc) {
   __shared__ int32_t cnt[1024];
   __shared__ int32_t first[1024];
+  __shared__ int32_t tstart[1024];
   __shared__ int scratch[16];
   __shared__ int bad;
   extern __shared__ int32_t stage[];  // the chunk histograms, when they fit (sized by the launch)
@@ -282,15 +295,31 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ chunk
     // coalesced copy to LDS; per expert, G threads (adjacent lanes) each take
     // a contiguous run of chunks: their sums, an exclusive scan of those over
     // the G lanes, then the running prefixes written back; prefixes back out
-    for (int i = threadIdx.x; i < nh; i += blockDim.x) stage[i] = chunk_hist[i];
+    // eight loads in flight per thread before their stores (a load waited for
+    // one at a time would cost a memory round trip per 1024 entries)
+    for (int64_t i0 = 0; i0 < nh; i0 += 8 * (int64_t)blockDim.x) {
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t i = i0 + u * (int64_t)blockDim.x + threadIdx.x;
+        v[u] = i < nh ? chunk_hist[i] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t i = i0 + u * (int64_t)blockDim.x + threadIdx.x;
+        if (i < nh) stage[i] = v[u];
+      }
+    }
     __syncthreads();
     int G = 1;
     while (G < 64 && G * 2 * E <= (int)blockDim.x) G *= 2;
     const int e = threadIdx.x / G, g = threadIdx.x % G;
     const int per = (nchunk + G - 1) / G, c0 = g * per, c1 = min(nchunk, c0 + per);
     int part = 0;
-    if (e < E)
+    if (e < E) {
+#pragma unroll 8
       for (int c = c0; c < c1; ++c) part += stage[c * E + e];
+    }
     // inclusive scan over the group's lanes (G a power of two, groups aligned)
     int inc = part;
     for (int d = 1; d < G; d <<= 1) {
@@ -299,6 +328,7 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ chunk
     }
     if (e < E) {
       int run = inc - part;
+#pragma unroll 8
       for (int c = c0; c < c1; ++c) {
         const int v = stage[c * E + e];
         stage[c * E + e] = run;
@@ -307,7 +337,19 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ chunk
       if (g == G - 1) cnt[e] = inc;
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < nh; i += blockDim.x) chunk_hist[i] = stage[i];
+    for (int64_t i0 = 0; i0 < nh; i0 += 8 * (int64_t)blockDim.x) {
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t i = i0 + u * (int64_t)blockDim.x + threadIdx.x;
+        v[u] = i < nh ? stage[i] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t i = i0 + u * (int64_t)blockDim.x + threadIdx.x;
+        if (i < nh) chunk_hist[i] = v[u];
+      }
+    }
   } else {
     for (int e = threadIdx.x; e < E; e += blockDim.x) {
       int run = 0;
@@ -325,7 +367,7 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ chunk
   __syncthreads();
   if (b) atomicAdd(&bad, b);
   __syncthreads();
-  finish_offsets(cnt, first, E, bad, offsets, tiles, misc, scratch);
+  finish_offsets(cnt, first, tstart, E, bad, offsets, tiles, misc, scratch);
 }
 
 // Pass 3: per chunk, stable scatter of pair ids.
