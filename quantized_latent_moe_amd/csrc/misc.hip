@@ -8,6 +8,10 @@ constexpr int kCombineUnroll = 8;  // slots per token whose loads are all issued
 
 // y[t][l] = sum_{j=0..k-1, id valid} slot[t*k + j][l], slots taken in order.
 // Each slot already holds router_w[t][j] * O (down epilogue).
+// NT: non-temporal slot loads, for slot buffers larger than the 256 MB
+// memory-side cache (measured: 147 -> 117 us at 21000 tokens, 688 MB of slots;
+// with 173 MB of slots, 5268 tokens, plain loads are 1.3 us faster).
+template <bool NT>
 __global__ __launch_bounds__(256) void k_combine(const int32_t* __restrict__ idx, const float* __restrict__ slots,
                                                  int64_t T, int L, int E, int k, float* __restrict__ y) {
   const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;  // one float4 of y
@@ -17,21 +21,31 @@ __global__ __launch_bounds__(256) void k_combine(const int32_t* __restrict__ idx
   const int l = (int)(q - t * l4) * 4;
   float4 acc = {0.f, 0.f, 0.f, 0.f};
   if (k <= kCombineUnroll) {
-    // issue every slot load before summing (in slot order, as below)
-    float4 v[kCombineUnroll];
+    // All ids first, then every slot load with no branch between them (a load
+    // guarded by its id would wait for that id before the next one issues):
+    // a slot that is not summed loads slot row 0 instead and is dropped by
+    // the select.
+    typedef float v4f __attribute__((ext_vector_type(4)));
+    int e[kCombineUnroll];
 #pragma unroll
     for (int j = 0; j < kCombineUnroll; ++j) {
-      const int e = j < k ? idx[t * k + j] : -1;
-      v[j] = (unsigned)e < (unsigned)E ? *reinterpret_cast<const float4*>(slots + (t * k + j) * L + l)
-                                       : float4{0.f, 0.f, 0.f, 0.f};
+      const int v = idx[t * k + (j < k ? j : 0)];  // a load on every path: no branch
+      e[j] = j < k ? v : -1;
+    }
+    v4f v[kCombineUnroll];
+#pragma unroll
+    for (int j = 0; j < kCombineUnroll; ++j) {
+      const bool ok = (unsigned)e[j] < (unsigned)E;
+      const v4f* src = reinterpret_cast<const v4f*>(slots + (ok ? (t * k + j) * L : 0) + l);
+      v[j] = NT ? __builtin_nontemporal_load(src) : *src;
     }
 #pragma unroll
-    for (int j = 0; j < kCombineUnroll; ++j) {
-      if (j < k) {
-        acc.x += v[j].x;
-        acc.y += v[j].y;
-        acc.z += v[j].z;
-        acc.w += v[j].w;
+    for (int j = 0; j < kCombineUnroll; ++j) {  // in slot order
+      if ((unsigned)e[j] < (unsigned)E) {
+        acc.x += v[j][0];
+        acc.y += v[j][1];
+        acc.z += v[j][2];
+        acc.w += v[j][3];
       }
     }
   } else {
@@ -119,7 +133,11 @@ inline unsigned blocks_for(int64_t n) { return (unsigned)((n + 255) / 256); }
 
 hipError_t launch_combine(const int32_t* idx, const Shapes& s, const Work& w, float* y, hipStream_t st) {
   const int64_t n = s.T * (s.L / 4);
-  hipLaunchKernelGGL(k_combine, dim3(blocks_for(n)), dim3(256), 0, st, idx, w.slots, s.T, s.L, s.E, s.k, y);
+  const bool nt = s.T * s.k * (int64_t)s.L * 4 > (int64_t(256) << 20);
+  if (nt)
+    hipLaunchKernelGGL(k_combine<true>, dim3(blocks_for(n)), dim3(256), 0, st, idx, w.slots, s.T, s.L, s.E, s.k, y);
+  else
+    hipLaunchKernelGGL(k_combine<false>, dim3(blocks_for(n)), dim3(256), 0, st, idx, w.slots, s.T, s.L, s.E, s.k, y);
   return hipGetLastError();
 }
 
