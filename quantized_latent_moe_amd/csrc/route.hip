@@ -24,18 +24,27 @@ namespace {
 constexpr int kSmallPairs = 4096;
 constexpr int kScanStage = 32768;  // chunk-histogram entries the scan stages in LDS (128 KB)
 constexpr int kSplitPerBlock = 1024;  // q8_1 blocks split per extra workgroup
+constexpr int kRouteThreads = 256;    // threads of the histogram and scatter workgroups
 
 // q8_1 block sb -> 32 codes at xc + 32 db and the fp32 scale xd[db].
-__device__ __forceinline__ void split_block(const uint8_t* __restrict__ x, int64_t sb, int64_t db,
-                                            int8_t* __restrict__ xc, float* __restrict__ xd) {
+// Split in two halves, so a thread can have several blocks' loads in flight
+// before it stores any of them.
+struct Q81Words {
+  uint32_t w[kQ81Bytes / 4];
+};
+__device__ __forceinline__ Q81Words load_q81(const uint8_t* __restrict__ x, int64_t sb) {
   const uint32_t* src = reinterpret_cast<const uint32_t*>(x + sb * kQ81Bytes);
-  uint4 lo, hi;
-  lo.x = src[1]; lo.y = src[2]; lo.z = src[3]; lo.w = src[4];
-  hi.x = src[5]; hi.y = src[6]; hi.z = src[7]; hi.w = src[8];
+  Q81Words r;
+#pragma unroll
+  for (int i = 0; i < kQ81Bytes / 4; ++i) r.w[i] = src[i];
+  return r;
+}
+__device__ __forceinline__ void store_split(const Q81Words& r, int64_t db, int8_t* __restrict__ xc,
+                                            float* __restrict__ xd) {
   uint4* dst = reinterpret_cast<uint4*>(xc + db * 32);
-  dst[0] = lo;
-  dst[1] = hi;
-  xd[db] = half_bits_to_float(src[0] & 0xffffu);
+  dst[0] = uint4{r.w[1], r.w[2], r.w[3], r.w[4]};
+  dst[1] = uint4{r.w[5], r.w[6], r.w[7], r.w[8]};
+  xd[db] = half_bits_to_float(r.w[0] & 0xffffu);
 }
 
 // Zeroes floats [i0, i0 + kZeroPerBlock) of y (clipped to n): the extra
@@ -187,7 +196,7 @@ __global__ __launch_bounds__(1024) void k_route_small(const int32_t* __restrict_
       return;
     }
     const int64_t b = (int64_t)(blockIdx.x - 1) * kSplitPerBlock + threadIdx.x;
-    if (b < nxb) split_block(x, b, b, xc, xd);
+    if (b < nxb) store_split(load_q81(x, b), b, xc, xd);
     return;
   }
   extern __shared__ int32_t wcnt[];  // [kSmallWaves][E]: running counts, then each wave's first positions
@@ -243,7 +252,7 @@ __global__ __launch_bounds__(1024) void k_route_small(const int32_t* __restrict_
 
 // ---- large batches, pass 1: per-chunk histograms; workgroups past the
 // chunks split x.
-__global__ __launch_bounds__(256) void k_route_hist(const int32_t* __restrict__ idx, int64_t n_pairs, int E,
+__global__ __launch_bounds__(kRouteThreads) void k_route_hist(const int32_t* __restrict__ idx, int64_t n_pairs, int E,
                                                     int nchunk, int32_t* __restrict__ chunk_hist,
                                                     int32_t* __restrict__ chunk_bad, const uint8_t* __restrict__ x,
                                                     int64_t nxb, int8_t* __restrict__ xc,
@@ -253,25 +262,48 @@ __global__ __launch_bounds__(256) void k_route_hist(const int32_t* __restrict__ 
     zero_chunk(yzero, ny, (int64_t)(blockIdx.x - nchunk - xblocks) * kZeroPerBlock);
     return;
   }
+  // Each thread's loads are all issued before any of their results is used
+  // (a loop of load-then-use waits out one memory round trip per iteration);
+  // a thread past the end loads the workgroup's first item instead and drops
+  // it.
+  constexpr int kPer = kSplitPerBlock / kRouteThreads;
+  static_assert(kPer * kRouteThreads == kSplitPerBlock && kPer * kRouteThreads == kRouteChunk, "four per thread");
   if ((int)blockIdx.x >= nchunk) {
     const int64_t b0 = (int64_t)(blockIdx.x - nchunk) * kSplitPerBlock;
-    for (int i = threadIdx.x; i < kSplitPerBlock; i += blockDim.x)
-      if (b0 + i < nxb) split_block(x, b0 + i, b0 + i, xc, xd);
+    Q81Words r[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int64_t b = b0 + threadIdx.x + kRouteThreads * i;
+      r[i] = load_q81(x, b < nxb ? b : b0);
+    }
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int64_t b = b0 + threadIdx.x + kRouteThreads * i;
+      if (b < nxb) store_split(r[i], b, xc, xd);
+    }
     return;
   }
   extern __shared__ int32_t hist[];  // [E]
   __shared__ int32_t bad;
+  const int64_t base = (int64_t)blockIdx.x * kRouteChunk;
+  int ev[kPer];  // loaded before the counts are cleared, so the two overlap
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int64_t p = base + threadIdx.x + kRouteThreads * i;
+    ev[i] = idx[p < n_pairs ? p : base];
+  }
   for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
   if (threadIdx.x == 0) bad = 0;
   __syncthreads();
-  const int64_t base = (int64_t)blockIdx.x * kRouteChunk;
-  const int64_t end = base + kRouteChunk < n_pairs ? base + kRouteChunk : n_pairs;
-  for (int64_t p = base + threadIdx.x; p < end; p += blockDim.x) {
-    const int e = idx[p];
-    if ((unsigned)e < (unsigned)E)
-      atomicAdd(&hist[e], 1);
-    else
-      atomicAdd(&bad, 1);
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int64_t p = base + threadIdx.x + kRouteThreads * i;
+    if (p < n_pairs) {
+      if ((unsigned)ev[i] < (unsigned)E)
+        atomicAdd(&hist[ev[i]], 1);
+      else
+        atomicAdd(&bad, 1);
+    }
   }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += blockDim.x) chunk_hist[(int64_t)blockIdx.x * E + e] = hist[e];
@@ -371,23 +403,32 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ chunk
 }
 
 // Pass 3: per chunk, stable scatter of pair ids.
-__global__ __launch_bounds__(256) void k_route_scatter(const int32_t* __restrict__ idx, int64_t n_pairs, int E,
+__global__ __launch_bounds__(kRouteThreads) void k_route_scatter(const int32_t* __restrict__ idx, int64_t n_pairs, int E,
                                                        int nbits, const int32_t* __restrict__ chunk_prefix,
                                                        const int32_t* __restrict__ offsets,
                                                        int32_t* __restrict__ perm) {
   extern __shared__ int32_t sm[];  // base[E] | wave_count[4][E]
   int32_t* base = sm;
   int32_t* wcnt = sm + E;
+  const int64_t cbase = (int64_t)blockIdx.x * kRouteChunk;
+  constexpr int kRounds = kRouteChunk / kRouteThreads;
+  int ev[kRounds];  // all of this thread's ids first (past the end: -1, from a load of the chunk's first id)
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r) {
+    const int64_t p = cbase + r * kRouteThreads + threadIdx.x;
+    const int v = idx[p < n_pairs ? p : cbase];
+    ev[r] = p < n_pairs ? v : -1;
+  }
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
     base[e] = offsets[e] + chunk_prefix[(int64_t)blockIdx.x * E + e];
     for (int w = 0; w < 4; ++w) wcnt[w * E + e] = 0;
   }
   __syncthreads();
   const int wave = threadIdx.x >> 6;
-  const int64_t cbase = (int64_t)blockIdx.x * kRouteChunk;
-  for (int r = 0; r < kRouteChunk / 256; ++r) {
-    const int64_t p = cbase + r * 256 + threadIdx.x;
-    const int e = p < n_pairs ? idx[p] : -1;
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r) {
+    const int64_t p = cbase + r * kRouteThreads + threadIdx.x;
+    const int e = ev[r];
     const bool valid = (unsigned)e < (unsigned)E;
     int c;
     const int rank = wave_rank(e, valid, nbits, &c);
@@ -426,12 +467,12 @@ hipError_t launch_route(const int32_t* idx, const uint8_t* x, const Shapes& s, c
                        yzero, ny);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(k_route_hist, dim3(w.nchunk + xblocks + zblocks), dim3(256), s.E * sizeof(int32_t), st, idx, n,
+  hipLaunchKernelGGL(k_route_hist, dim3(w.nchunk + xblocks + zblocks), dim3(kRouteThreads), s.E * sizeof(int32_t), st, idx, n,
                      s.E, w.nchunk, w.chunk_hist, w.chunk_bad, x, nxb, w.xc, w.xd, (int)xblocks, yzero, ny);
   const int64_t nh = (int64_t)w.nchunk * s.E;
   hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(1024), nh <= kScanStage ? nh * sizeof(int32_t) : 0, st, w.chunk_hist,
                      w.chunk_bad, w.nchunk, s.E, w.offsets, w.tiles, w.misc);
-  hipLaunchKernelGGL(k_route_scatter, dim3(w.nchunk), dim3(256), 5 * s.E * sizeof(int32_t), st, idx, n, s.E, nbits,
+  hipLaunchKernelGGL(k_route_scatter, dim3(w.nchunk), dim3(kRouteThreads), 5 * s.E * sizeof(int32_t), st, idx, n, s.E, nbits,
                      w.chunk_hist, w.offsets, w.perm);
   return hipGetLastError();
 }
