@@ -398,7 +398,10 @@ __global__ __launch_bounds__(kDnThreads) void k_dec_down(const uint8_t* __restri
   const int S = 1 << s_log2, R = 64 >> s_log2;
   const int t = blockIdx.x, l0 = blockIdx.y * R;
   const int tid = threadIdx.x;
-  const int slice = tid & (S - 1), row = (tid & 63) >> s_log2, slot = tid >> 6;  // a wave = one slot's R rows
+  // a wave = one slot's R rows; slot is read as wave-uniform, so the expert's
+  // buffer descriptor stays scalar (a per-lane one makes every weight load a
+  // readfirstlane loop)
+  const int slice = tid & (S - 1), row = (tid & 63) >> s_log2, slot = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nfb = F / 32, row_bytes = nfb * kIq4Bytes;
   const int l = l0 + row;
   const rsrc_t rh = make_rsrc(h_codes, (uint32_t)(P * F));

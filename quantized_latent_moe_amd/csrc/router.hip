@@ -69,8 +69,9 @@ __global__ __launch_bounds__(64 * kRouterWaves) void k_router_topk(const float* 
                                                                     float* __restrict__ w) {
   constexpr int kPerLane = P;
   const int lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * kRouterWaves + (threadIdx.x >> 6);
-  if (t >= T) return;  // wave-uniform
+  // the wave's token, read as wave-uniform so that its buffer descriptor is scalar
+  const int64_t t = (int64_t)blockIdx.x * kRouterWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (t >= T) return;
   const rsrc_t rl = make_rsrc(logits + t * E, (uint32_t)E * 4);
   float v[kPerLane];
 #pragma unroll
@@ -131,17 +132,21 @@ __global__ __launch_bounds__(64 * kRouterWaves) void k_router_topk16(const float
                                                                       int E, int k, int32_t* __restrict__ idx,
                                                                       float* __restrict__ w) {
   const int lane = threadIdx.x & 63, rl = lane & 15;
-  const int64_t t0 = ((int64_t)blockIdx.x * kRouterWaves + (threadIdx.x >> 6)) * 4;
-  if (t0 >= T) return;  // wave-uniform
+  const int64_t t0 = ((int64_t)blockIdx.x * kRouterWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) * 4;
+  if (t0 >= T) return;
   const int64_t t = t0 + (lane >> 4);
   const bool live = t < T;
-  const rsrc_t rlg = make_rsrc(logits + (live ? t : 0) * E, live ? (uint32_t)E * 4 : 0u);
+  // one descriptor for the wave's (up to) four logit rows, so that it is
+  // scalar; a row past T lies beyond num_records and loads zeros
+  const int nlive = T - t0 < 4 ? (int)(T - t0) : 4;
+  const rsrc_t rlg = make_rsrc(logits + t0 * E, (uint32_t)(nlive * E) * 4u);
+  const int row0 = (lane >> 4) * E;
   float v[P];
   uint32_t taken = 0;  // bit i: entry i of this lane already picked (or past E)
 #pragma unroll
   for (int i = 0; i < P; ++i) {
     const int e = rl + 16 * i;
-    v[i] = as_float((int)buf_u32(rlg, e < E ? 4 * e : kOutOfRange, 0));
+    v[i] = as_float((int)buf_u32(rlg, e < E ? 4 * (row0 + e) : kOutOfRange, 0));
     if (e >= E) {
       v[i] = -INFINITY;
       taken |= 1u << i;
