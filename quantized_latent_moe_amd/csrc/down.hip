@@ -493,11 +493,13 @@ __global__ __launch_bounds__(kWsThreads) void k_down(const uint8_t* __restrict__
   DItem cur = item_at(cpos);
   int pair0 = -1, pair1 = -1;
   float w0 = 0.f, w1 = 0.f;
-  // one K step over both halves (TWO) or the first only
-  auto mma = [&](auto two_tag, auto grp_tag, int b) {
+  // one K step over both halves (TWO) or the first only; WIDE: this wave's
+  // tokens start at 64 th (a wide item), else at 32 th
+  auto mma = [&](auto two_tag, auto wide_tag, auto grp_tag, int b) {
     constexpr bool TWO = decltype(two_tag)::value;
+    constexpr bool WIDE = decltype(wide_tag)::value;
     constexpr int GRP = decltype(grp_tag)::value;
-    const int n0 = (TWO ? 64 : 32) * th + col, n1 = n0 + 32;
+    const int n0 = (WIDE ? 64 : 32) * th + col, n1 = n0 + 32;
     const int8_t* ap = As[b] + (32 * rs + col) * 256;
     const int8_t* bp0 = Bs[b] + n0 * 256;
     const int8_t* bp1 = Bs[b] + (TWO ? n1 : n0) * 256;
@@ -584,9 +586,12 @@ __global__ __launch_bounds__(kWsThreads) void k_down(const uint8_t* __restrict__
         w1 = pair1 >= 0 ? router_w[pair1] : 0.f;
       }
       if (wide) {
-        if (64 * th < cur.cnt) mma(std::true_type{}, grp_tag, b);
+        // the second half only when it holds a token (an item of 65..96
+        // tokens leaves the upper wave's second half all padding)
+        if (64 * th + 32 < cur.cnt) mma(std::true_type{}, std::true_type{}, grp_tag, b);
+        else if (64 * th < cur.cnt) mma(std::false_type{}, std::true_type{}, grp_tag, b);
       } else if (32 * th < cur.cnt) {
-        mma(std::false_type{}, grp_tag, b);
+        mma(std::false_type{}, std::false_type{}, grp_tag, b);
       }
       if (++csb == nsb) {
         // ---- weighted output rows into the pairs' slots (or added into y)
