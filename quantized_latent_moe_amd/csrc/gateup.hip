@@ -144,6 +144,10 @@ __global__ __launch_bounds__(kThreads) void k_gateup(const int8_t* __restrict__ 
   // 32p + 8c + (lane >> 3), block lane & 7.
   int qoff = kOutOfRange, xoff[8], doff[4];
   int lj = 0, lsb = 0, qf0 = -1;
+  // whether this producer's 32 tokens of the item being loaded hold a pair
+  // (else its activation loads and LDS stores are skipped: no consumer reads
+  // those rows), for the item set up and for the data in registers
+  bool x_live_item = true, x_live_regs = true;
   bool need_setup = true;
   // The next item's token ids: producer p fetches those of its own tokens
   // 32p .. 32p+31 (lanes 0..31), so only the wave that writes an entry reads
@@ -191,6 +195,7 @@ __global__ __launch_bounds__(kThreads) void k_gateup(const int8_t* __restrict__ 
       const int t = ids[j & 1][32 * p + 8 * c + (lane >> 3)];
       doff[c] = t >= 0 ? (t * nxb + (lane & 7)) * 4 : kOutOfRange;
     }
+    x_live_item = 32 * p < it.cnt;
     lpos = next_pos(lpos);
     fetch_ids(j + 1, lpos);
   };
@@ -211,10 +216,13 @@ __global__ __launch_bounds__(kThreads) void k_gateup(const int8_t* __restrict__ 
     const int sd = __builtin_amdgcn_readfirstlane(lsb * 32);
 #pragma unroll
     for (int i = 0; i < 16; ++i) rq[i] = buf_u32(rw_src, qoff, sq + 2 * i * row_bytes);
+    x_live_regs = x_live_item;
+    if (x_live_regs) {
 #pragma unroll
-    for (int a = 0; a < 8; ++a) rx[a] = buf_u128(rx_src, xoff[a], sx);
+      for (int a = 0; a < 8; ++a) rx[a] = buf_u128(rx_src, xoff[a], sx);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) rd[c] = buf_u32(rd_src, doff[c], sd);
+      for (int c = 0; c < 4; ++c) rd[c] = buf_u32(rd_src, doff[c], sd);
+    }
     if (++lsb == nsb) {
       lsb = 0;
       need_setup = ++lj < my_items;
@@ -229,12 +237,14 @@ __global__ __launch_bounds__(kThreads) void k_gateup(const int8_t* __restrict__ 
 #pragma unroll
       for (int i = 0; i < 16; ++i) raw32[2 * i * (kRawStride / 4)] = rq[i];
     }
+    if (x_live_regs) {
 #pragma unroll
-    for (int a = 0; a < 8; ++a)
-      *reinterpret_cast<uint4*>(Bs[b] + (32 * p + 4 * a + (lane >> 4)) * kOpStride + 16 * (lane & 15)) = rx[a];
+      for (int a = 0; a < 8; ++a)
+        *reinterpret_cast<uint4*>(Bs[b] + (32 * p + 4 * a + (lane >> 4)) * kOpStride + 16 * (lane & 15)) = rx[a];
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
-      dxs[b][(32 * p + 8 * c + (lane >> 3)) * 8 + (lane & 7)] = -as_float((int)rd[c]);  // minus: operand A is -w
+      for (int c = 0; c < 4; ++c)
+        dxs[b][(32 * p + 8 * c + (lane >> 3)) * 8 + (lane & 7)] = -as_float((int)rd[c]);  // minus: operand A is -w
+    }
   };
   // U: the producer's own staged rows unpacked into operand A of buffer b.
   auto unpack = [&](int b) {
