@@ -364,6 +364,10 @@ __global__ __launch_bounds__(kWsThreads) void k_down(const uint8_t* __restrict__
     int qoff[5], hoff[8], soff[4];
     int lj = 0, lsb = 0, ql0 = -1;
     bool need_setup = true;
+    // whether this producer's 32 tokens of the item being loaded hold a pair
+    // (else their H loads and LDS stores are skipped: no consumer reads those
+    // rows), for the item set up and for the data in registers
+    bool h_live_item = true, h_live_regs = true;
     DItemPos lpos = first_pos;  // item lj's position
     auto setup = [&]() {
       const DItem it = item_at(lpos);
@@ -389,6 +393,7 @@ __global__ __launch_bounds__(kWsThreads) void k_down(const uint8_t* __restrict__
         const int n = 32 * p + 8 * c + (lane >> 3);
         soff[c] = n < it.cnt ? ((it.pos0 + n) * nfb + (lane & 7)) * 4 : kOutOfRange;
       }
+      h_live_item = 32 * p < it.cnt;
     };
     uint4 rq[5], rx[8];
     uint32_t rd[4];
@@ -402,10 +407,13 @@ __global__ __launch_bounds__(kWsThreads) void k_down(const uint8_t* __restrict__
       const int sd = __builtin_amdgcn_readfirstlane(lsb * 32);
 #pragma unroll
       for (int m = 0; m < 5; ++m) rq[m] = buf_u128(rw_src, qoff[m], sq);
+      h_live_regs = h_live_item;
+      if (h_live_regs) {
 #pragma unroll
-      for (int a = 0; a < 8; ++a) rx[a] = buf_u128(rh_src, hoff[a], sx);
+        for (int a = 0; a < 8; ++a) rx[a] = buf_u128(rh_src, hoff[a], sx);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) rd[c] = buf_u32(rs_src, soff[c], sd);
+        for (int c = 0; c < 4; ++c) rd[c] = buf_u32(rs_src, soff[c], sd);
+      }
       if (++lsb == nsb) {
         lsb = 0;
         need_setup = ++lj < my_items;
@@ -419,14 +427,16 @@ __global__ __launch_bounds__(kWsThreads) void k_down(const uint8_t* __restrict__
 #pragma unroll
       for (int m = 0; m < 5; ++m)
         if (m < 4 || lane < 32) raw16[lane + 64 * m] = rq[m];
+      if (h_live_regs) {
 #pragma unroll
-      for (int a = 0; a < 8; ++a) {
-        const int n = 32 * p + 4 * a + (lane >> 4);
-        *reinterpret_cast<uint4*>(Bs[b] + swz(n, lane & 15)) = rx[a];
+        for (int a = 0; a < 8; ++a) {
+          const int n = 32 * p + 4 * a + (lane >> 4);
+          *reinterpret_cast<uint4*>(Bs[b] + swz(n, lane & 15)) = rx[a];
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          dhs[b][32 * p + 8 * c + (lane >> 3)][lane & 7] = __builtin_bit_cast(_Float16, (uint16_t)(rd[c] & 0xffffu));
       }
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        dhs[b][32 * p + 8 * c + (lane >> 3)][lane & 7] = __builtin_bit_cast(_Float16, (uint16_t)(rd[c] & 0xffffu));
     };
     auto unpack = [&](int b) {
       // expand: row 32p + (lane & 31), blocks 4*(lane >> 5) .. +3 from the 72
